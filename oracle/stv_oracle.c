@@ -1,0 +1,346 @@
+/*
+ * stv_oracle.c -- plain CPU oracle for verify-round attention over a 3-bit
+ * KV cache.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the CPU
+ * baseline leg of the benchmark may load this library.  The GPU path never
+ * calls it and shares no code, header, table or helper with it.
+ *
+ * What it computes (the elpis pages: "Why fast" for int8 Q.K^T over 3-bit K
+ * codes widened to int8 and for split-K with a merge; elpis-lossless
+ * "Lossless" and "Trust base" for fp32-accumulated P.V and row
+ * independence; "How" for the 8-row token tree):
+ *
+ *   for every query row (t, h), with kv head g = h / (Hq / Hkv):
+ *     (q_i8, sq)  = per-row int8 quantization of q[t][h]            (c1)
+ *     S_b[j]      = sum_{d in block b} q_i8[d] * (kcode[j][d] - 4)   int64
+ *     x[j]        = scale * sq * sum_b sk[j][b] * S_b[j]             fp64
+ *     visible(j)  = j < L, or the tree/causal rule for the new rows
+ *     out         = sum_j softmax(x)_j * vs[j][b(d)] * (vcode[j][d] - 4)
+ *     lse         = log sum_j exp(x[j])                              fp64
+ *
+ * It is the definition written out: no tiling, no splitting, no online
+ * rescaling.  Integer parts are int64, softmax and P.V are fp64, keys are
+ * visited in ascending order.  The only fp32 steps are the two quantizers,
+ * because they define integers and fp16 scales that the GPU must reproduce
+ * bit for bit; they use one correctly rounded IEEE division, one multiply
+ * and round-half-even, with no contraction (built with -ffp-contract=off).
+ *
+ * Readings where the pages are silent (each also listed in the design
+ * notes):
+ *  (c1) Q quantizer: amax = max|q|; amax == 0 gives sq = 0 and all-zero
+ *       codes; else inv = 127/amax, q_i8 = clamp(rint(q*inv), -127, 127),
+ *       sq = amax/127.
+ *  (c2) codes are offset binary with zero point 4: value = s * (c - 4).
+ *  (c3) bit layout of one 32-element block in three 32-bit words, the
+ *       "byte-plane" layout: element e = 4*qq + i (qq = e/4, i = e%4)
+ *         qq = 0,1 : word 0, bits [8i + 3qq, +3)
+ *         qq = 2,3 : word 1, bits [8i + 3(qq-2), +3)
+ *         qq = 4,5 : word 2, bits [8i + 3(qq-4), +3)
+ *         qq = 6   : code bits 0-1 at word 0 bits [8i+6, 8i+8),
+ *                    code bit 2 at word 2 bit 8i+6
+ *         qq = 7   : code bits 0-1 at word 1 bits [8i+6, 8i+8),
+ *                    code bit 2 at word 2 bit 8i+7
+ *  (c4) K/V quantizer per 32-element block: s16 = fp16_rne(amax/3) (the
+ *       largest finite fp16 if that overflows), code = clamp(rint(x/s), -4,
+ *       3) + 4, and code 4 everywhere when s16 is zero.
+ *  (c6) the K scale is one fp16 per 32 consecutive elements of one (token,
+ *       kv head) row; the softmax scale is a caller argument.
+ *  (c7) tree keys sit at L + node index; key L + a is visible to row i iff
+ *       bit a of mask[i] is set; a NULL mask means the causal chunk rule
+ *       (key L + u visible to row t iff u <= t).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_EXPORT __attribute__((visibility("default")))
+
+/* ---------------------------------------------------------------- format */
+
+/* Bit position of bit k (0..2) of the code of element e (0..31). */
+static void code_bit_pos(int e, int k, int *word, int *bit)
+{
+    int qq = e / 4, i = e % 4;
+    if (qq < 6) {
+        *word = qq / 2;
+        *bit = 8 * i + 3 * (qq % 2) + k;
+    } else if (k < 2) {
+        *word = qq - 6;              /* qq 6 -> word 0, qq 7 -> word 1 */
+        *bit = 8 * i + 6 + k;
+    } else {
+        *word = 2;
+        *bit = 8 * i + 6 + (qq - 6);
+    }
+}
+
+ORC_EXPORT int orc_code_get(const uint32_t *w, int e)
+{
+    int c = 0;
+    for (int k = 0; k < 3; ++k) {
+        int word, bit;
+        code_bit_pos(e, k, &word, &bit);
+        c |= (int)((w[word] >> bit) & 1u) << k;
+    }
+    return c;
+}
+
+ORC_EXPORT void orc_code_set(uint32_t *w, int e, int code)
+{
+    for (int k = 0; k < 3; ++k) {
+        int word, bit;
+        code_bit_pos(e, k, &word, &bit);
+        w[word] &= ~(1u << bit);
+        w[word] |= (uint32_t)((code >> k) & 1) << bit;
+    }
+}
+
+/* ------------------------------------------------------------------ fp16 */
+
+/* IEEE binary16 round-to-nearest-even of a float. */
+ORC_EXPORT uint16_t orc_f32_to_f16(float x)
+{
+    uint32_t u;
+    memcpy(&u, &x, 4);
+    uint16_t sign = (uint16_t)((u >> 16) & 0x8000u);
+    if (isnan(x))
+        return (uint16_t)(sign | 0x7E00u);
+    double a = fabs((double)x);
+    if (a >= 65520.0)                   /* halfway to 2^16 rounds up: inf */
+        return (uint16_t)(sign | 0x7C00u);
+    if (a < 0x1p-14) {                  /* subnormal range, quantum 2^-24 */
+        double n = rint(a / 0x1p-24);   /* exact quotient, ties to even */
+        return (uint16_t)(sign | (uint16_t)n);  /* n == 1024 is 2^-14 */
+    }
+    int E;
+    frexp(a, &E);                       /* a = f * 2^E, f in [0.5, 1) */
+    int e = E - 1;                      /* a in [2^e, 2^(e+1)) */
+    double n = rint(ldexp(a, 10 - e));  /* 11-bit significand, exact input */
+    if (n == 2048.0) {
+        n = 1024.0;
+        e += 1;
+    }
+    if (e + 15 >= 31)
+        return (uint16_t)(sign | 0x7C00u);
+    return (uint16_t)(sign | (uint16_t)((e + 15) << 10) | (uint16_t)(n - 1024.0));
+}
+
+ORC_EXPORT double orc_f16_to_f64(uint16_t h)
+{
+    int sign = (h >> 15) & 1, ex = (h >> 10) & 0x1F, man = h & 0x3FF;
+    double v;
+    if (ex == 0)
+        v = ldexp((double)man, -24);
+    else if (ex == 31)
+        v = man ? NAN : INFINITY;
+    else
+        v = ldexp((double)(man + 1024), ex - 25);
+    return sign ? -v : v;
+}
+
+/* -------------------------------------------------------------- quantizers */
+
+ORC_EXPORT void orc_quantize_q_row(const float *q, int D, int8_t *qi8, float *sq)
+{
+    float amax = 0.0f;
+    for (int d = 0; d < D; ++d) {
+        float a = fabsf(q[d]);
+        if (a > amax)
+            amax = a;
+    }
+    if (amax == 0.0f) {
+        for (int d = 0; d < D; ++d)
+            qi8[d] = 0;
+        *sq = 0.0f;
+        return;
+    }
+    float inv = 127.0f / amax;
+    for (int d = 0; d < D; ++d) {
+        float t = rintf(q[d] * inv);
+        if (t > 127.0f) t = 127.0f;
+        if (t < -127.0f) t = -127.0f;
+        qi8[d] = (int8_t)t;
+    }
+    *sq = amax / 127.0f;
+}
+
+/* Quantize one 32-element block; returns the fp16 scale bits. */
+ORC_EXPORT uint16_t orc_quantize_kv_block(const float *x, uint32_t *w)
+{
+    float amax = 0.0f;
+    for (int e = 0; e < 32; ++e) {
+        float a = fabsf(x[e]);
+        if (a > amax)
+            amax = a;
+    }
+    uint16_t s16 = orc_f32_to_f16(amax / 3.0f);
+    if ((s16 & 0x7FFFu) == 0x7C00u)
+        s16 = 0x7BFFu;                  /* saturate to the largest finite */
+    float s = (float)orc_f16_to_f64(s16);
+    w[0] = w[1] = w[2] = 0;
+    for (int e = 0; e < 32; ++e) {
+        int c = 4;
+        if (s != 0.0f) {
+            float t = rintf(x[e] / s);
+            if (t > 3.0f) t = 3.0f;
+            if (t < -4.0f) t = -4.0f;
+            c = (int)t + 4;
+        }
+        orc_code_set(w, e, c);
+    }
+    return s16;
+}
+
+/* x: [n_tok][Hkv][D] fp32; codes: [Hkv][cap][D/32][3]; scales: [Hkv][cap][D/32].
+ * Writes positions pos0 .. pos0+n_tok-1. */
+ORC_EXPORT void orc_kv_quant_pack(const float *x, int n_tok, int pos0, uint32_t *codes,
+                                  uint16_t *scales, int Hkv, int D, int cap)
+{
+    int nb = D / 32;
+    for (int t = 0; t < n_tok; ++t)
+        for (int g = 0; g < Hkv; ++g)
+            for (int b = 0; b < nb; ++b) {
+                size_t pos = (size_t)g * cap + (size_t)(pos0 + t);
+                scales[pos * nb + b] = orc_quantize_kv_block(
+                    x + ((size_t)t * Hkv + g) * D + 32 * b, codes + (pos * nb + b) * 3);
+            }
+}
+
+/* ------------------------------------------------------------- attention */
+
+/* Returns 0 on success, -1 on bad arguments.
+ * q: [T][Hq][D]; caches as above; mask: [T] (NULL = causal chunk rule).
+ * Only keys j in [k_begin, k_end) take part (a split-K partial); pass
+ * 0, L+T for the whole call.  rows: flattened t*Hq + h (NULL = all rows in
+ * order).  Outputs are per listed row: out [n][D], lse [n], and optionally
+ * logits [n][L+T][D/32] (every key, visible or not), qi8 [n][D], sq [n]. */
+ORC_EXPORT int orc_attention(const float *q, int T, int Hq,
+                             const uint32_t *kc, const uint16_t *ks,
+                             const uint32_t *vc, const uint16_t *vs,
+                             int Hkv, int D, int cap, int L,
+                             const uint64_t *mask, double scale,
+                             int k_begin, int k_end,
+                             const int32_t *rows, int n_rows,
+                             double *out, double *lse, int64_t *logits,
+                             int8_t *qi8_out, float *sq_out)
+{
+    if (T < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || D <= 0 || D % 32 || L < 0 ||
+        L + T > cap || (mask && T > 64))
+        return -1;
+    int nb = D / 32, G = Hq / Hkv, N = L + T;
+    if (!rows)
+        n_rows = T * Hq;
+    int bad = 0;
+
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int r = 0; r < n_rows; ++r) {
+        int flat = rows ? rows[r] : r;
+        if (flat < 0 || flat >= T * Hq) {
+            bad = 1;
+            continue;
+        }
+        int t = flat / Hq, h = flat % Hq, g = h / G;
+        int8_t *qi = (int8_t *)malloc((size_t)D);
+        double *x = (double *)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
+        char *vis = (char *)malloc((size_t)(N > 0 ? N : 1));
+        float sq;
+        orc_quantize_q_row(q + ((size_t)t * Hq + h) * D, D, qi, &sq);
+        if (qi8_out)
+            memcpy(qi8_out + (size_t)r * D, qi, (size_t)D);
+        if (sq_out)
+            sq_out[r] = sq;
+
+        double m = -INFINITY;
+        for (int j = 0; j < N; ++j) {
+            const uint32_t *kw = kc + (((size_t)g * cap + j) * nb) * 3;
+            const uint16_t *ksj = ks + ((size_t)g * cap + j) * nb;
+            double acc = 0.0;
+            for (int b = 0; b < nb; ++b) {
+                int64_t s = 0;
+                for (int e = 0; e < 32; ++e)
+                    s += (int64_t)qi[32 * b + e] * (int64_t)(orc_code_get(kw + 3 * b, e) - 4);
+                if (logits)
+                    logits[((size_t)r * N + j) * nb + b] = s;
+                acc += orc_f16_to_f64(ksj[b]) * (double)s;
+            }
+            x[j] = scale * (double)sq * acc;
+            int v = (j >= k_begin && j < k_end);
+            if (v && j >= L) {
+                int a = j - L;
+                v = mask ? (int)((mask[t] >> a) & 1u) : (a <= t);
+            }
+            vis[j] = (char)v;
+            if (v && x[j] > m)
+                m = x[j];
+        }
+
+        double *o = out + (size_t)r * D;
+        for (int d = 0; d < D; ++d)
+            o[d] = 0.0;
+        if (m == -INFINITY) {
+            lse[r] = -INFINITY;
+        } else {
+            double l = 0.0;
+            for (int j = 0; j < N; ++j) {
+                if (!vis[j])
+                    continue;
+                double p = exp(x[j] - m);
+                l += p;
+                const uint32_t *vw = vc + (((size_t)g * cap + j) * nb) * 3;
+                const uint16_t *vsj = vs + ((size_t)g * cap + j) * nb;
+                for (int b = 0; b < nb; ++b) {
+                    double sv = orc_f16_to_f64(vsj[b]);
+                    for (int e = 0; e < 32; ++e)
+                        o[32 * b + e] += p * (sv * (double)(orc_code_get(vw + 3 * b, e) - 4));
+                }
+            }
+            for (int d = 0; d < D; ++d)
+                o[d] /= l;
+            lse[r] = m + log(l);
+        }
+        free(qi);
+        free(x);
+        free(vis);
+    }
+    return bad ? -1 : 0;
+}
+
+/* ----------------------------------------------------------------- merge */
+
+/* part_o: [S][rows][D] (each normalised), part_lse: [S][rows] (natural log,
+ * -inf for a split that saw no key).  out = sum_s e^(lse_s - LSE) O_s with
+ * LSE = log sum_s e^lse_s; out_lse may be NULL. */
+ORC_EXPORT void orc_merge(const double *part_o, const double *part_lse, int S, int rows,
+                          int D, double *out, double *out_lse)
+{
+    for (int r = 0; r < rows; ++r) {
+        double M = -INFINITY;
+        for (int s = 0; s < S; ++s)
+            if (part_lse[(size_t)s * rows + r] > M)
+                M = part_lse[(size_t)s * rows + r];
+        double *o = out + (size_t)r * D;
+        for (int d = 0; d < D; ++d)
+            o[d] = 0.0;
+        if (M == -INFINITY) {
+            if (out_lse)
+                out_lse[r] = -INFINITY;
+            continue;
+        }
+        double W = 0.0;
+        for (int s = 0; s < S; ++s) {
+            double ls = part_lse[(size_t)s * rows + r];
+            if (ls == -INFINITY)
+                continue;
+            double w = exp(ls - M);
+            W += w;
+            const double *os = part_o + ((size_t)s * rows + r) * D;
+            for (int d = 0; d < D; ++d)
+                o[d] += w * os[d];
+        }
+        for (int d = 0; d < D; ++d)
+            o[d] /= W;
+        if (out_lse)
+            out_lse[r] = M + log(W);
+    }
+}

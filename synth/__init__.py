@@ -1,0 +1,165 @@
+"""Seeded synthetic inputs for the verify-attention path.
+
+This module only draws random numbers.  It holds none of the method's
+arithmetic: no quantizer, no packing, no attention.  Both the CPU oracle
+and the GPU path read what it returns.
+
+Why raw random words stand in for packed codes: a 3-bit code block stores
+32 codes in exactly 96 bits, so 96 uniformly random bits are 32 independent
+codes uniform on [0, 7], whatever bit layout each side later reads them
+with.  The workload statement (codes uniform in [0, 7]) is therefore met
+without any packing code here.
+
+Workload recipe (shapes from the verify round on the elpis pages, "Setup"
+/ "Recipe" and the 8-row tree of "How"; distributions from the workload
+statement):
+  * K and V codes: uniform random 32-bit words, 3 words per 32 elements;
+  * K and V scales: U(0.01, 0.1) rounded to fp16, one per 32 elements of
+    one (token, KV head) row;
+  * Q: standard normal fp32;
+  * tree: node 0 is the root; node i > 0 takes a uniformly random parent
+    among earlier nodes whose depth is below the depth cap.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+__all__ = [
+    "Geometry", "CONFIGS", "EXTRA_CONFIGS", "KVCache",
+    "make_kv", "make_q", "make_tree_parents", "ancestor_masks",
+    "chain_parents", "all_tree_shapes",
+]
+
+
+@dataclass(frozen=True)
+class Geometry:
+    name: str
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    ctx_len: int          # L: keys already in the cache before the new rows
+    n_rows: int           # T: new query tokens (tree nodes or prefill chunk)
+    kind: str             # "tree", "chain" or "prefill"
+    max_depth: int        # depth cap for random trees (1 = root only)
+    seed: int
+
+    @property
+    def n_keys(self) -> int:
+        return self.ctx_len + self.n_rows
+
+
+# The five workload configurations, in order: tiny parity case, single-token
+# decode, 64-node tree at 32K, 64-node tree at 262K, 4,096-token prefill.
+CONFIGS = [
+    Geometry("tiny", 4, 1, 64, 512, 8, "chain", 8, 0),
+    Geometry("decode_8k", 24, 4, 256, 8192, 1, "tree", 1, 1),
+    Geometry("tree64_32k", 24, 4, 256, 32768, 64, "tree", 8, 2),
+    Geometry("tree64_262k", 24, 4, 256, 262144, 64, "tree", 8, 3),
+    Geometry("prefill_4k_32k", 24, 4, 256, 32768, 4096, "prefill", 0, 4),
+]
+
+# Shapes where streaming the cache, not the matrix pipe, bounds the call:
+# the pages' own 8-row tree at 262K, and one query token at 262K.
+EXTRA_CONFIGS = [
+    Geometry("tree8_262k", 24, 4, 256, 262144, 8, "tree", 8, 5),
+    Geometry("decode_262k", 24, 4, 256, 262144, 1, "tree", 1, 6),
+]
+
+
+@dataclass
+class KVCache:
+    """Host arrays of one layer's quantized K/V cache.
+
+    k_codes, v_codes: uint32 [Hkv][capacity][D/32][3]
+    k_scales, v_scales: uint16 (fp16 bit patterns) [Hkv][capacity][D/32]
+    Positions >= n_filled are zero.
+    """
+    k_codes: np.ndarray
+    k_scales: np.ndarray
+    v_codes: np.ndarray
+    v_scales: np.ndarray
+    n_kv_heads: int
+    head_dim: int
+    capacity: int
+    n_filled: int
+
+
+def _scales(rng: np.random.Generator, shape) -> np.ndarray:
+    s = rng.uniform(0.01, 0.1, size=shape)
+    return s.astype(np.float16).view(np.uint16)
+
+
+def make_kv(rng: np.random.Generator, n_kv_heads: int, head_dim: int,
+            n_filled: int, capacity: int | None = None) -> KVCache:
+    if capacity is None:
+        capacity = n_filled
+    assert head_dim % 32 == 0 and 0 <= n_filled <= capacity
+    nb = head_dim // 32
+    out = {}
+    for name in ("k", "v"):
+        codes = np.zeros((n_kv_heads, capacity, nb, 3), dtype=np.uint32)
+        scales = np.zeros((n_kv_heads, capacity, nb), dtype=np.uint16)
+        codes[:, :n_filled] = rng.integers(0, 2**32, size=(n_kv_heads, n_filled, nb, 3),
+                                           dtype=np.uint32)
+        scales[:, :n_filled] = _scales(rng, (n_kv_heads, n_filled, nb))
+        out[name + "_codes"] = codes
+        out[name + "_scales"] = scales
+    return KVCache(out["k_codes"], out["k_scales"], out["v_codes"], out["v_scales"],
+                   n_kv_heads, head_dim, capacity, n_filled)
+
+
+def make_q(rng: np.random.Generator, n_rows: int, n_q_heads: int, head_dim: int) -> np.ndarray:
+    return rng.standard_normal((n_rows, n_q_heads, head_dim), dtype=np.float32)
+
+
+def make_tree_parents(rng: np.random.Generator, n_nodes: int, max_depth: int) -> np.ndarray:
+    """Parent array of a random tree: parent[0] = -1, parent[i] < i.
+
+    Node 0 (the root) has depth 1; a node may only hang below a node whose
+    depth is under max_depth, so no node is deeper than max_depth.
+    """
+    parent = np.full(n_nodes, -1, dtype=np.int64)
+    depth = np.zeros(n_nodes, dtype=np.int64)
+    if n_nodes == 0:
+        return parent
+    depth[0] = 1
+    for i in range(1, n_nodes):
+        cand = np.nonzero(depth[:i] < max_depth)[0]
+        p = int(rng.choice(cand))
+        parent[i] = p
+        depth[i] = depth[p] + 1
+    return parent
+
+
+def chain_parents(n_nodes: int) -> np.ndarray:
+    p = np.arange(-1, n_nodes - 1, dtype=np.int64)
+    return p
+
+
+def ancestor_masks(parent: np.ndarray) -> np.ndarray:
+    """The input format of the verify call: bit a of mask[i] is set iff node a
+    is node i or one of its ancestors (parent[i] < i for every node)."""
+    n = len(parent)
+    assert n <= 64
+    m = np.zeros(n, dtype=np.uint64)
+    for i in range(n):
+        own = np.uint64(1) << np.uint64(i)
+        m[i] = own if parent[i] < 0 else (m[parent[i]] | own)
+    return m
+
+
+def all_tree_shapes(n_nodes: int):
+    """Every parent array with parent[0] = -1 and parent[i] in [0, i):
+    (n_nodes - 1)! shapes (5,040 for the pages' 8-row tree)."""
+    def rec(prefix):
+        i = len(prefix)
+        if i == n_nodes:
+            yield np.array(prefix, dtype=np.int64)
+            return
+        for p in range(i):
+            yield from rec(prefix + [p])
+    if n_nodes == 0:
+        return
+    yield from rec([-1])
