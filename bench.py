@@ -1,0 +1,267 @@
+#!/usr/bin/env python3
+"""Benchmark of the verify-round attention path on one MI355X.
+
+One step is one pass of the whole hot path for one layer of a verify round:
+  1. append the T new rows' K and V to the 3-bit cache (kv_quant_pack x2),
+  2. the split attention kernel (int8 Q.K^T, fp32 online softmax, P.V),
+  3. the log-sum-exp merge of the split partials.
+The headline workload is the 64-node draft tree over a 262,144-token context
+(24 query / 4 KV heads, head_dim 256).  Four distinct caches are rotated so
+every step streams its cache from HBM rather than from the 256 MB Infinity
+Cache.  Inputs are seeded synthetic data already resident on the GPU.
+
+Prints one JSON line (see the keys below).  Extra workloads (the prefill
+chunk, the pages' 8-row tree and one query token at 262K, the 8K decode and
+the 32K tree) are reported under "extra".
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+METRIC = "µs/verify-round attn + HBM GB/s (% peak) at 262K ctx; prefill int8 MFMA %"
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+INT8_PEAK_TOPS = 5000.0          # dense int8 MFMA
+FP16_PEAK_TFLOPS = 2500.0        # dense fp16 MFMA
+N_BUFFERS = 4                    # 4 x 235 MB > 256 MB Infinity Cache
+
+
+def work_of(geom: synth.Geometry, masks):
+    """Algorithmic bytes and operations of one step (see the design notes)."""
+    T, hq, hkv, d, L = geom.n_rows, geom.n_q_heads, geom.n_kv_heads, geom.head_dim, geom.ctx_len
+    nb = d // 32
+    n_keys = L + T
+    kv_bytes = n_keys * hkv * 2 * nb * (12 + 2)          # codes + fp16 scales, K and V
+    q_bytes = T * hq * d * 4
+    out_bytes = T * hq * d * 4
+    append_bytes = 2 * T * hkv * d * 4 + 2 * T * hkv * nb * 14
+    if masks is None:
+        visible = sum(L + t + 1 for t in range(T)) * hq
+    else:
+        visible = sum(L + bin(int(m)).count("1") for m in masks) * hq
+    macs = visible * d                                     # per product (Q.K^T, and P.V)
+    return {
+        "kv_bytes": kv_bytes, "q_bytes": q_bytes, "out_bytes": out_bytes,
+        "append_bytes": append_bytes,
+        "attn_bytes": kv_bytes + q_bytes + out_bytes,
+        "step_bytes": kv_bytes + q_bytes + out_bytes + append_bytes,
+        "qk_ops": 2 * macs, "pv_ops": 2 * macs,
+    }
+
+
+class Workload:
+    def __init__(self, geom: synth.Geometry, torch, stv, n_buffers=N_BUFFERS):
+        self.g = geom
+        self.torch = torch
+        self.stv = stv
+        rng = np.random.default_rng(geom.seed)
+        host = synth.make_kv(rng, geom.n_kv_heads, geom.head_dim, geom.n_keys)
+        self.host = host
+        self.q_host = synth.make_q(rng, geom.n_rows, geom.n_q_heads, geom.head_dim)
+        self.causal = geom.kind == "prefill"
+        self.mask = None
+        if not self.causal:
+            parents = (synth.chain_parents(geom.n_rows) if geom.kind == "chain"
+                       else synth.make_tree_parents(rng, geom.n_rows, geom.max_depth))
+            self.mask = synth.ancestor_masks(parents)
+        knew = synth.make_new_rows(rng, geom.n_rows, geom.n_kv_heads, geom.head_dim)
+        vnew = synth.make_new_rows(rng, geom.n_rows, geom.n_kv_heads, geom.head_dim)
+        dev = "cuda"
+        base = stv.KVCache.from_host(host, device=dev)
+        self.caches = [base] + [stv.KVCache(base.k_codes.clone(), base.k_scales.clone(),
+                                            base.v_codes.clone(), base.v_scales.clone())
+                                for _ in range(n_buffers - 1)]
+        self.q = torch.from_numpy(self.q_host).to(dev)
+        self.knew = torch.from_numpy(knew).to(dev)
+        self.vnew = torch.from_numpy(vnew).to(dev)
+        self.scale = 1.0 / math.sqrt(geom.head_dim)
+        self.S, self.ws_bytes = stv.attention_plan(geom.n_rows, geom.n_q_heads, geom.n_kv_heads,
+                                                   geom.head_dim, geom.ctx_len, self.causal, 0)
+        T, hq, d = geom.n_rows, geom.n_q_heads, geom.head_dim
+        self.part_o = self.part_lse = None
+        if self.S > 1:
+            self.part_o = torch.empty((self.S, T, hq, d), dtype=torch.float32, device=dev)
+            self.part_lse = torch.empty((self.S, T, hq), dtype=torch.float32, device=dev)
+        self.out = torch.empty((T, hq, d), dtype=torch.float32, device=dev)
+        self.out_lse = torch.empty((T, hq), dtype=torch.float32, device=dev)
+        self.work = work_of(geom, self.mask)
+
+    def step(self, i, ev=None):
+        stv, g = self.stv, self.g
+        kv = self.caches[i % len(self.caches)]
+        stv.kv_quant_pack(self.knew, g.ctx_len, kv.k_codes, kv.k_scales)
+        stv.kv_quant_pack(self.vnew, g.ctx_len, kv.v_codes, kv.v_scales)
+        if ev is not None:
+            ev[0].record()
+        if self.S == 1:
+            # one split: the attention kernel writes the output itself
+            if self.causal:
+                stv.prefill_attention(self.q, kv, g.ctx_len, self.scale, self.out, self.out_lse)
+            else:
+                stv.verify_attention(self.q, kv, g.ctx_len, self.mask, self.scale, self.out,
+                                     self.out_lse)
+            if ev is not None:
+                ev[1].record()
+                ev[2].record()
+            return
+        stv.attention_partials(self.q, kv, g.ctx_len, self.mask, self.scale, 0,
+                               self.part_o, self.part_lse)
+        if ev is not None:
+            ev[1].record()
+        stv.split_merge(self.part_o.reshape(self.S, -1, g.head_dim),
+                        self.part_lse.reshape(self.S, -1), self.out.reshape(-1, g.head_dim),
+                        self.out_lse.reshape(-1))
+        if ev is not None:
+            ev[2].record()
+
+    def run(self, steps, warmup):
+        torch = self.torch
+        for i in range(warmup):
+            self.step(i)
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            self.step(warmup + i, evs[i])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        attn_ms = [e[0].elapsed_time(e[1]) for e in evs]
+        merge_ms = [e[1].elapsed_time(e[2]) for e in evs]
+        return {"wall_s": wall, "attn_ms": attn_ms, "merge_ms": merge_ms}
+
+
+def summarize(wl: Workload, r, steps):
+    w = wl.work
+    ms_step = r["wall_s"] * 1e3 / steps
+    attn = float(np.mean(r["attn_ms"]))
+    merge = float(np.mean(r["merge_ms"]))
+    call_us = (attn + merge) * 1e3
+    mfma_s = w["qk_ops"] / (INT8_PEAK_TOPS * 1e12) + w["pv_ops"] / (FP16_PEAK_TFLOPS * 1e12)
+    return {
+        "ms_per_step": ms_step,
+        "attn_kernel_us": attn * 1e3,
+        "merge_kernel_us": merge * 1e3,
+        "us_per_call": call_us,
+        "splits": wl.S,
+        "hbm_gbs": w["attn_bytes"] / (call_us * 1e-6) / 1e9,
+        "hbm_frac": w["attn_bytes"] / (call_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+        "kernel_hbm_gbs": w["attn_bytes"] / (attn * 1e-3) / 1e9,
+        "int8_mfma_frac": w["qk_ops"] / (attn * 1e-3) / (INT8_PEAK_TOPS * 1e12),
+        "matrix_pipe_frac": mfma_s / (attn * 1e-3),
+        "ideal_mfma_us": mfma_s * 1e6,
+        "ideal_hbm_us": w["attn_bytes"] / (HBM_PEAK_GBS * 1e9) * 1e6,
+    }
+
+
+def cpu_baseline(wl: Workload, n_rows: int):
+    import oracle
+    g = wl.g
+    total = g.n_rows * g.n_q_heads
+    n_rows = min(n_rows, total)
+    rows = np.linspace(0, total - 1, n_rows).round().astype(np.int32)
+    threads = oracle.set_threads(len(os.sched_getaffinity(0)))
+    t0 = time.perf_counter()
+    oracle.attention(wl.q_host, wl.host, g.ctx_len, wl.mask, wl.scale, rows=rows)
+    el = time.perf_counter() - t0
+    full_s = el * total / n_rows
+    return {"value": wl.work["attn_bytes"] / full_s / 1e9, "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{n_rows} of {total} query rows of {g.name} (full context), {el:.1f} s; "
+                      f"scaled to the whole call: {full_s * 1e6:.0f} us"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="tree64_262k")
+    ap.add_argument("--extra", default="prefill_4k_32k,tree8_262k,decode_262k,decode_8k,tree64_32k",
+                    help="comma-separated extra workloads ('' for none)")
+    ap.add_argument("--extra-steps", type=int, default=10)
+    ap.add_argument("--cpu-rows", type=int, default=128, help="oracle sample size (0: skip)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import speculative_tree_verify_amd as stv
+    stv.load_library()
+    geoms = {g.name: g for g in synth.CONFIGS + synth.EXTRA_CONFIGS}
+    wl = Workload(geoms[args.workload], torch, stv)
+    r = wl.run(args.steps, args.warmup)
+    s = summarize(wl, r, args.steps)
+    g = wl.g
+    w = wl.work
+    total_ops = w["qk_ops"] + w["pv_ops"]
+    blended_peak = total_ops / (w["qk_ops"] / INT8_PEAK_TOPS + w["pv_ops"] / FP16_PEAK_TFLOPS)
+    achieved = total_ops / (s["attn_kernel_us"] * 1e-6) / 1e12
+    line = {
+        "metric": METRIC,
+        "value": round(w["step_bytes"] / (s["ms_per_step"] * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(s["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8xi8->i32, f16xf16->f32, f32",
+        "data": "synthetic (seeded; 3-bit codes uniform, fp16 scales U(0.01,0.1), Q N(0,1))",
+        "config": {"workload": g.name, "ctx_len": g.ctx_len, "tree_nodes": g.n_rows,
+                   "q_heads": g.n_q_heads, "kv_heads": g.n_kv_heads, "head_dim": g.head_dim,
+                   "kv_bits": 3, "splits": wl.S, "kv_buffers_rotated": N_BUFFERS},
+        "us_per_verify_call": round(s["us_per_call"], 2),
+        "hbm_gbs_per_call": round(s["hbm_gbs"], 1),
+        "hbm_frac_per_call": round(s["hbm_frac"], 4),
+        "roofline": {
+            "kernel": "attn_split_kernel",
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": round(blended_peak, 1),
+            "unit": "TFLOP/s",
+            "frac": round(achieved / blended_peak, 4),
+            "traffic": None,
+            "kernel_us": round(s["attn_kernel_us"], 2),
+            "ideal_mfma_us": round(s["ideal_mfma_us"], 2),
+            "ideal_hbm_us": round(s["ideal_hbm_us"], 2),
+        },
+    }
+    extra = {}
+    for name in [n for n in args.extra.split(",") if n]:
+        del wl
+        torch.cuda.empty_cache()
+        wl = Workload(geoms[name], torch, stv)
+        rr = wl.run(args.extra_steps, 2)
+        se = summarize(wl, rr, args.extra_steps)
+        extra[name] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in se.items()}
+    if extra:
+        line["extra"] = extra
+    if args.cpu_rows > 0:
+        del wl
+        torch.cuda.empty_cache()
+        wl = Workload(geoms[args.workload], torch, stv, n_buffers=1)
+        line["cpu_baseline"] = cpu_baseline(wl, args.cpu_rows)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,206 @@
+/*
+ * stv.h -- C ABI of the speculative tree-verify attention library for
+ * MI355X (gfx950).
+ *
+ * The operation: in a speculative verify round, a block of draft-tree query
+ * rows attends over a long KV cache quantized to 3 bits with one fp16 scale
+ * per 32 elements (elpis, "Setup": 3-bit KV, 262,144-token context; "How": an
+ * 8-row token tree whose rows see their ancestors).  Q.K^T is computed
+ * exactly in int8/int32 with the 3-bit K codes widened to int8 (elpis, "Why
+ * fast": decode verify and prefill int8 Q.K^T on integer matrix units),
+ * softmax runs in fp32 and P.V accumulates in fp32 (elpis, "What fast
+ * means": fp16-accumulated P.V was not shipped; elpis-lossless, "Lossless":
+ * fp32 sums), and the context is split across work-groups whose partial
+ * results are joined by a log-sum-exp merge (elpis-lossless, "Trust base":
+ * the split-K barrier; elpis, "Why fast": the prefill merge).
+ *
+ * Conventions for every entry point:
+ *  - Pointers are device pointers unless marked [host].
+ *  - The caller owns all memory.  The library never allocates or frees.
+ *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
+ *    null stream).  No entry point synchronizes the host.
+ *  - Every argument is validated on the host before any HIP call, so every
+ *    error path returns without touching the GPU.  The return value is
+ *    STV_OK or a negative STV_E* code; stv_last_error() (thread-local) then
+ *    describes the failure.
+ *  - Results are deterministic: a call with the same arguments produces
+ *    bitwise identical outputs (fixed split partition, fixed merge order).
+ *  - NaN or Inf in the inputs is not checked and propagates.
+ *
+ * Cache layout (one layer; K and V each):
+ *  codes  uint32 [Hkv][capacity][D/32][3]  three words per 32 elements
+ *  scales uint16 [Hkv][capacity][D/32]     fp16 bit patterns
+ * Element e of a 32-element block holds code c in [0, 7] standing for
+ * scale * (c - 4).  Bit layout ("byte-plane"), with e = 4*qq + i:
+ *   qq 0,1: word 0 bits [8i + 3qq, +3)      qq 2,3: word 1 bits [8i + 3(qq-2), +3)
+ *   qq 4,5: word 2 bits [8i + 3(qq-4), +3)
+ *   qq 6:   code bits 0-1 at word 0 bits [8i+6, 8i+8), bit 2 at word 2 bit 8i+6
+ *   qq 7:   code bits 0-1 at word 1 bits [8i+6, 8i+8), bit 2 at word 2 bit 8i+7
+ * so that one shift and one mask yield four codes in the four bytes of a
+ * word.  Supported head_dim: 64, 128, 256.
+ */
+#ifndef STV_H
+#define STV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define STV_OK 0
+#define STV_EINVAL (-1)     /* bad shape, pointer or argument */
+#define STV_EMASK (-2)      /* ancestor mask is not a forest of root-to-node paths */
+#define STV_ECAPACITY (-3)  /* ctx_len + T exceeds the cache capacity */
+#define STV_EWORKSPACE (-4) /* workspace missing or too small for the split plan */
+#define STV_EHIP (-5)       /* the HIP runtime reported an error at launch */
+
+#define STV_MAX_TREE_ROWS 64
+
+/* One layer's quantized cache (layout above).  Passed by [host] pointer. */
+typedef struct stv_kv_layer {
+    const uint32_t *k_codes;
+    const uint16_t *k_scales;
+    const uint32_t *v_codes;
+    const uint16_t *v_scales;
+    int32_t n_kv_heads;
+    int32_t head_dim;
+    int32_t capacity;
+} stv_kv_layer;
+
+/* Description of the last failure on the calling thread ("" after success). */
+const char *stv_last_error(void);
+
+/* ABI version; bumped on any incompatible change.  Currently 1. */
+int32_t stv_abi_version(void);
+
+/*
+ * stv_kv_quant_pack -- write new tokens' K or V rows into the 3-bit cache
+ * (the 3-bit KV cache of elpis, "Setup"; the pages do not state the rule).
+ * Call once for K and once for V.
+ *   x       fp32 [n_tok][n_kv_heads][head_dim], the new rows
+ *   pos0    first cache position written; positions pos0 .. pos0+n_tok-1
+ *           are overwritten, every other position is left untouched
+ *   codes, scales   the cache arrays of that tensor (layout above)
+ * Rule per 32-element block: s = fp16_rne(amax / 3) (the largest finite fp16
+ * if that overflows), code = clamp(rint(x / s), -4, 3) + 4, all codes 4 when
+ * s is zero; the division is correctly rounded and rint rounds half to even.
+ * Errors: STV_EINVAL (null pointer, n_tok < 0, bad head_dim or heads),
+ * STV_ECAPACITY (pos0 < 0 or pos0 + n_tok > capacity), STV_EHIP.
+ */
+int stv_kv_quant_pack(const float *x, int32_t n_tok, int32_t pos0, uint32_t *codes,
+                      uint16_t *scales, int32_t n_kv_heads, int32_t head_dim,
+                      int32_t capacity, void *stream);
+
+/*
+ * stv_attention_plan -- the split plan a verify (causal = 0) or prefill
+ * (causal = 1) call with these sizes will use, and the workspace it needs.
+ *   n_splits_req  0 lets the library choose; otherwise the requested number
+ *                 of context splits (the effective count may be lower: each
+ *                 split covers a whole number of 32-key tiles)
+ *   n_splits_out  [host] effective split count S
+ *   workspace_bytes_out [host] bytes of workspace the call needs (0 when S = 1)
+ * Errors: STV_EINVAL, STV_ECAPACITY is not checked here (no capacity given).
+ */
+int stv_attention_plan(int32_t T, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                       int32_t ctx_len, int32_t causal, int32_t n_splits_req,
+                       int32_t *n_splits_out, size_t *workspace_bytes_out);
+
+/*
+ * stv_verify_attention -- attention of T draft-tree rows over the cache
+ * (elpis, "Why fast": decode verify with int8 Q.K^T; "How": the token tree).
+ *   q           fp32 [T][n_q_heads][head_dim]; query head h reads kv head
+ *               h / (n_q_heads / n_kv_heads)
+ *   T           1 .. 64 tree rows
+ *   kv          [host] the layer's cache.  Keys 0 .. ctx_len-1 are the
+ *               context; the T rows' own K/V must already sit at positions
+ *               ctx_len .. ctx_len+T-1 (written with stv_kv_quant_pack)
+ *   anc_mask    [host] uint64 [T]: bit a of anc_mask[i] is set iff tree row a
+ *               is row i or an ancestor of it.  Every row must have its own
+ *               bit and no bit above it, and the rest of its bits must be
+ *               exactly the mask of its highest other row (its parent), so
+ *               the rows form a forest and each row sees a root-to-node path
+ *   softmax_scale  multiplies the logits (commonly 1/sqrt(head_dim))
+ *   out         fp32 [T][n_q_heads][head_dim]
+ *   out_lse     nullable fp32 [T][n_q_heads]: natural-log log-sum-exp of each
+ *               row's scaled logits, for merging with results over other
+ *               key ranges
+ *   workspace, workspace_bytes  device scratch of at least the plan's bytes
+ *               (may be NULL when the plan has S = 1)
+ *   n_splits    0 = automatic, else requested split count (see the plan)
+ *   dbg_logits  nullable int32 [T][n_q_heads][ctx_len+T][head_dim/32]: the
+ *               exact per-block integer Q.K^T sums; entries of keys a row
+ *               cannot see are unspecified
+ *   dbg_q       nullable int8 [T][n_q_heads][head_dim]: the quantized Q
+ *   dbg_qscale  nullable fp32 [T][n_q_heads]: the Q scales
+ * Per-row Q quantizer: amax = max|q|; inv = 127 / amax (correctly rounded);
+ * q8 = clamp(rint(q * inv), -127, 127); sq = amax / 127; a zero row gives
+ * sq = 0 and zero codes.  Logit of key j: softmax_scale * sq *
+ * sum_b k_scale[j][b] * S_b[j] with S_b the int32 block sums.
+ * Errors: STV_EINVAL, STV_EMASK, STV_ECAPACITY, STV_EWORKSPACE, STV_EHIP.
+ */
+int stv_verify_attention(const float *q, int32_t T, int32_t n_q_heads,
+                         const stv_kv_layer *kv, int32_t ctx_len, const uint64_t *anc_mask,
+                         float softmax_scale, float *out, float *out_lse, void *workspace,
+                         size_t workspace_bytes, int32_t n_splits, int32_t *dbg_logits,
+                         int8_t *dbg_q, float *dbg_qscale, void *stream);
+
+/*
+ * stv_prefill_attention -- the chunked-prefill variant (elpis, "Why fast":
+ * prefill int8 Q.K^T, the K/V double-buffered ring, the prefill merge): T
+ * new rows, row t sees keys 0 .. ctx_len+t.  Arguments as for
+ * stv_verify_attention without anc_mask; T may be any positive count with
+ * T * n_q_heads < 2^31.
+ * Errors: STV_EINVAL, STV_ECAPACITY, STV_EWORKSPACE, STV_EHIP.
+ */
+int stv_prefill_attention(const float *q, int32_t T, int32_t n_q_heads,
+                          const stv_kv_layer *kv, int32_t ctx_len, float softmax_scale,
+                          float *out, float *out_lse, void *workspace, size_t workspace_bytes,
+                          int32_t n_splits, int32_t *dbg_logits, int8_t *dbg_q,
+                          float *dbg_qscale, void *stream);
+
+/*
+ * stv_attention_partials -- the split phase alone: each of the S context
+ * splits of the plan writes its normalised partial output and its
+ * log-sum-exp, to be joined by stv_split_merge (elpis-lossless, "Trust
+ * base": split-K; the same partials serve a context range computed on
+ * another device).  stv_verify_attention with S > 1 is exactly this call
+ * followed by stv_split_merge.
+ *   q, T, n_q_heads, kv, ctx_len, softmax_scale, n_splits: as for
+ *               stv_verify_attention / stv_prefill_attention
+ *   anc_mask    [host] uint64 [T] tree masks (as for verify), or NULL for
+ *               the causal chunk rule of prefill
+ *   part_o      fp32 [S][T][n_q_heads][head_dim], S from stv_attention_plan
+ *   part_lse    fp32 [S][T][n_q_heads], natural log; -inf where a split saw
+ *               no key of that row (its part_o row is then zero)
+ * Split s covers keys [s*P, min(ctx_len+T, (s+1)*P)) with
+ * P = 32 * ceil(ceil((ctx_len+T)/32) / S).
+ * Errors: STV_EINVAL, STV_EMASK, STV_ECAPACITY, STV_EHIP.
+ */
+int stv_attention_partials(const float *q, int32_t T, int32_t n_q_heads,
+                           const stv_kv_layer *kv, int32_t ctx_len, const uint64_t *anc_mask,
+                           float softmax_scale, int32_t n_splits, float *part_o,
+                           float *part_lse, void *stream);
+
+/*
+ * stv_split_merge -- join split partials with a log-sum-exp merge
+ * (elpis-lossless, "Trust base": the split-K barrier; elpis, "Why fast":
+ * the prefill merge).
+ *   part_o    fp32 [S][rows][D], each split's normalised output
+ *   part_lse  fp32 [S][rows], natural log; -inf marks a split that saw no key
+ *   out       fp32 [rows][D] = sum_s exp(lse_s - LSE) * part_o[s], with
+ *             LSE = log sum_s exp(lse_s); rows whose splits are all -inf
+ *             get zeros
+ *   out_lse   nullable fp32 [rows], receives LSE
+ * Splits are summed in order s = 0 .. S-1.  D: 1 .. 1024.
+ * Errors: STV_EINVAL, STV_EHIP.
+ */
+int stv_split_merge(const float *part_o, const float *part_lse, int32_t S, int32_t rows,
+                    int32_t D, float *out, float *out_lse, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* STV_H */

@@ -56,6 +56,8 @@ def _load():
         lib.orc_attention.argtypes = [P, i32, i32, P, P, P, P, i32, i32, i32, i32, P,
                                       ctypes.c_double, i32, i32, P, i32, P, P, P, P, P]
         lib.orc_attention.restype = i32
+        lib.orc_set_threads.argtypes = [i32]
+        lib.orc_set_threads.restype = i32
         lib.orc_merge.argtypes = [P, P, i32, i32, i32, P, P]
         lib.orc_merge.restype = None
         _lib = lib
@@ -68,6 +70,11 @@ def _ptr(a):
 
 def _c(a, dtype):
     return np.ascontiguousarray(a, dtype=dtype)
+
+
+def set_threads(n: int = 0) -> int:
+    """Set (n > 0) and return the number of threads the row loop uses."""
+    return int(_load().orc_set_threads(int(n)))
 
 
 # ------------------------------------------------------------------ format

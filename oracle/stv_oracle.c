@@ -306,6 +306,25 @@ ORC_EXPORT int orc_attention(const float *q, int T, int Hq,
     return bad ? -1 : 0;
 }
 
+/* ------------------------------------------------------------- threading */
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Sets the OpenMP thread count of the row loop; returns the count in use. */
+ORC_EXPORT int orc_set_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0)
+        omp_set_num_threads(n);
+    return omp_get_max_threads();
+#else
+    (void)n;
+    return 1;
+#endif
+}
+
 /* ----------------------------------------------------------------- merge */
 
 /* part_o: [S][rows][D] (each normalised), part_lse: [S][rows] (natural log,

@@ -1,0 +1,305 @@
+"""Speculative tree-verify attention over a 3-bit KV cache, for MI355X.
+
+Thin ctypes binding of ``libstv.so`` (hand-written HIP kernels for gfx950
+behind the C ABI declared in ``include/stv.h``).  This module only checks and
+marshals arguments; PyTorch supplies device memory and the current stream.
+Every step of the computation runs in the library's kernels, and nothing
+here falls back to another implementation: if the library is missing, the
+calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libstv.so")
+
+STV_OK = 0
+STV_EINVAL = -1
+STV_EMASK = -2
+STV_ECAPACITY = -3
+STV_EWORKSPACE = -4
+STV_EHIP = -5
+
+__all__ = [
+    "StvError", "KVCache", "load_library", "kv_quant_pack", "attention_plan",
+    "verify_attention", "prefill_attention", "attention_partials", "split_merge",
+    "STV_OK", "STV_EINVAL", "STV_EMASK", "STV_ECAPACITY", "STV_EWORKSPACE", "STV_EHIP",
+]
+
+
+class StvError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"stv error {code}: {msg}")
+        self.code = code
+
+
+class _KVLayer(ctypes.Structure):
+    _fields_ = [("k_codes", ctypes.c_void_p), ("k_scales", ctypes.c_void_p),
+                ("v_codes", ctypes.c_void_p), ("v_scales", ctypes.c_void_p),
+                ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("capacity", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def load_library():
+    """Load libstv.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run `python -m "
+                               "speculative_tree_verify_amd.build_lib` first")
+        lib = ctypes.CDLL(LIB_PATH)
+        P, i32 = ctypes.c_void_p, ctypes.c_int32
+        lib.stv_last_error.restype = ctypes.c_char_p
+        lib.stv_last_error.argtypes = []
+        lib.stv_abi_version.restype = i32
+        lib.stv_abi_version.argtypes = []
+        lib.stv_kv_quant_pack.restype = ctypes.c_int
+        lib.stv_kv_quant_pack.argtypes = [P, i32, i32, P, P, i32, i32, i32, P]
+        lib.stv_attention_plan.restype = ctypes.c_int
+        lib.stv_attention_plan.argtypes = [i32, i32, i32, i32, i32, i32, i32,
+                                           ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_size_t)]
+        lib.stv_verify_attention.restype = ctypes.c_int
+        lib.stv_verify_attention.argtypes = [P, i32, i32, ctypes.POINTER(_KVLayer), i32, P,
+                                             ctypes.c_float, P, P, P, ctypes.c_size_t, i32,
+                                             P, P, P, P]
+        lib.stv_prefill_attention.restype = ctypes.c_int
+        lib.stv_prefill_attention.argtypes = [P, i32, i32, ctypes.POINTER(_KVLayer), i32,
+                                              ctypes.c_float, P, P, P, ctypes.c_size_t, i32,
+                                              P, P, P, P]
+        lib.stv_attention_partials.restype = ctypes.c_int
+        lib.stv_attention_partials.argtypes = [P, i32, i32, ctypes.POINTER(_KVLayer), i32, P,
+                                               ctypes.c_float, i32, P, P, P]
+        lib.stv_split_merge.restype = ctypes.c_int
+        lib.stv_split_merge.argtypes = [P, P, i32, i32, i32, P, P, P]
+        _lib = lib
+    return _lib
+
+
+def _check(rc: int):
+    if rc != STV_OK:
+        raise StvError(rc, load_library().stv_last_error().decode())
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dev_ptr(t, dtype, name, shape=None):
+    torch = _torch()
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise TypeError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t.data_ptr()
+
+
+def _stream(device):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+@dataclass
+class KVCache:
+    """One layer's 3-bit cache on the GPU.
+
+    k_codes, v_codes: int32 [Hkv][capacity][D/32][3] (32-bit words)
+    k_scales, v_scales: float16 [Hkv][capacity][D/32]
+    """
+    k_codes: "object"
+    k_scales: "object"
+    v_codes: "object"
+    v_scales: "object"
+
+    @property
+    def n_kv_heads(self) -> int:
+        return int(self.k_codes.shape[0])
+
+    @property
+    def capacity(self) -> int:
+        return int(self.k_codes.shape[1])
+
+    @property
+    def head_dim(self) -> int:
+        return int(self.k_codes.shape[2]) * 32
+
+    @classmethod
+    def empty(cls, n_kv_heads: int, head_dim: int, capacity: int, device="cuda"):
+        torch = _torch()
+        nb = head_dim // 32
+        z = lambda shape, dt: torch.zeros(shape, dtype=dt, device=device)  # noqa: E731
+        return cls(z((n_kv_heads, capacity, nb, 3), torch.int32),
+                   z((n_kv_heads, capacity, nb), torch.float16),
+                   z((n_kv_heads, capacity, nb, 3), torch.int32),
+                   z((n_kv_heads, capacity, nb), torch.float16))
+
+    @classmethod
+    def from_host(cls, host, device="cuda"):
+        """Copy host arrays (uint32 codes, uint16 fp16-bit scales) to the GPU."""
+        torch = _torch()
+
+        def up(a, view):
+            return torch.from_numpy(np.ascontiguousarray(a).view(view)).to(device)
+        return cls(up(host.k_codes, np.int32), up(host.k_scales, np.float16),
+                   up(host.v_codes, np.int32), up(host.v_scales, np.float16))
+
+    def _layer(self) -> _KVLayer:
+        torch = _torch()
+        nb = self.head_dim // 32
+        shp_c = (self.n_kv_heads, self.capacity, nb, 3)
+        shp_s = (self.n_kv_heads, self.capacity, nb)
+        return _KVLayer(_dev_ptr(self.k_codes, torch.int32, "k_codes", shp_c),
+                        _dev_ptr(self.k_scales, torch.float16, "k_scales", shp_s),
+                        _dev_ptr(self.v_codes, torch.int32, "v_codes", shp_c),
+                        _dev_ptr(self.v_scales, torch.float16, "v_scales", shp_s),
+                        self.n_kv_heads, self.head_dim, self.capacity)
+
+
+def kv_quant_pack(x, pos0: int, codes, scales):
+    """Quantize x [n_tok][Hkv][D] fp32 into cache positions pos0.. of one tensor."""
+    torch = _torch()
+    n_tok, hkv, d = x.shape
+    cap = int(codes.shape[1])
+    _dev_ptr(codes, torch.int32, "codes", (hkv, cap, d // 32, 3))
+    _dev_ptr(scales, torch.float16, "scales", (hkv, cap, d // 32))
+    rc = load_library().stv_kv_quant_pack(
+        _dev_ptr(x, torch.float32, "x"), n_tok, pos0, codes.data_ptr(), scales.data_ptr(),
+        hkv, d, cap, _stream(x.device))
+    _check(rc)
+
+
+def attention_plan(T: int, n_q_heads: int, n_kv_heads: int, head_dim: int, ctx_len: int,
+                   causal: bool, n_splits: int = 0) -> tuple[int, int]:
+    """(effective split count, workspace bytes) of a call with these sizes."""
+    s = ctypes.c_int32()
+    ws = ctypes.c_size_t()
+    _check(load_library().stv_attention_plan(T, n_q_heads, n_kv_heads, head_dim, ctx_len,
+                                             int(bool(causal)), n_splits, ctypes.byref(s),
+                                             ctypes.byref(ws)))
+    return int(s.value), int(ws.value)
+
+
+def _attention(q, kv: KVCache, ctx_len: int, mask, softmax_scale, out, out_lse, workspace,
+               n_splits, debug, causal):
+    torch = _torch()
+    T, hq, d = q.shape
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((T, hq, d), dtype=torch.float32, device=q.device)
+    S, ws_bytes = attention_plan(T, hq, kv.n_kv_heads, d, ctx_len, causal, n_splits)
+    if ws_bytes and workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    ws_ptr = None
+    ws_len = 0
+    if workspace is not None:
+        ws_ptr = _dev_ptr(workspace, torch.uint8, "workspace")
+        ws_len = workspace.numel()
+    dbg = None
+    dbg_ptrs = (None, None, None)
+    if debug:
+        names = ("logits", "q8", "qscale") if debug is True else tuple(debug)
+        shapes = {"logits": ((T, hq, ctx_len + T, d // 32), torch.int32),
+                  "q8": ((T, hq, d), torch.int8), "qscale": ((T, hq), torch.float32)}
+        dbg = {k: torch.zeros(shapes[k][0], dtype=shapes[k][1], device=q.device) for k in names}
+        dbg_ptrs = tuple(dbg[k].data_ptr() if k in dbg else None
+                         for k in ("logits", "q8", "qscale"))
+    layer = kv._layer()
+    lib = load_library()
+    common = (_dev_ptr(out, torch.float32, "out", (T, hq, d)),
+              _dev_ptr(out_lse, torch.float32, "out_lse", (T, hq)))
+    if causal:
+        rc = lib.stv_prefill_attention(
+            _dev_ptr(q, torch.float32, "q"), T, hq, ctypes.byref(layer), ctx_len,
+            float(softmax_scale), *common, ws_ptr, ws_len, n_splits, *dbg_ptrs,
+            _stream(q.device))
+    else:
+        m = np.ascontiguousarray(np.asarray(mask, dtype=np.uint64))
+        if m.shape != (T,):
+            raise ValueError(f"anc_mask must have shape ({T},)")
+        rc = lib.stv_verify_attention(
+            _dev_ptr(q, torch.float32, "q"), T, hq, ctypes.byref(layer), ctx_len,
+            m.ctypes.data, float(softmax_scale), *common, ws_ptr, ws_len, n_splits,
+            *dbg_ptrs, _stream(q.device))
+    _check(rc)
+    # keep host/device buffers alive until the enqueued work has consumed them
+    # (the mask is copied into kernel arguments at launch; the workspace is
+    # owned by the caller's allocator and stream-ordered)
+    return (out, dbg) if debug else out
+
+
+def verify_attention(q, kv: KVCache, ctx_len: int, anc_mask, softmax_scale=None, out=None,
+                     out_lse=None, workspace=None, n_splits: int = 0, debug: bool = False):
+    """Tree-verify attention: q [T][Hq][D] fp32 over kv, rows masked by anc_mask [T] uint64.
+
+    Returns out [T][Hq][D], and with debug a dict of debug tensors: debug=True
+    asks for all of "logits" (int32 per-block Q.K^T sums), "q8" and "qscale";
+    a tuple of those names asks for a subset."""
+    return _attention(q, kv, ctx_len, anc_mask, softmax_scale, out, out_lse, workspace,
+                      n_splits, debug, causal=False)
+
+
+def prefill_attention(q, kv: KVCache, ctx_len: int, softmax_scale=None, out=None,
+                      out_lse=None, workspace=None, n_splits: int = 0, debug: bool = False):
+    """Chunked-prefill attention: row t sees keys 0 .. ctx_len + t."""
+    return _attention(q, kv, ctx_len, None, softmax_scale, out, out_lse, workspace,
+                      n_splits, debug, causal=True)
+
+
+def attention_partials(q, kv: KVCache, ctx_len: int, anc_mask=None, softmax_scale=None,
+                       n_splits: int = 0, part_o=None, part_lse=None):
+    """Split phase only: returns (part_o [S][T][Hq][D], part_lse [S][T][Hq]).
+
+    anc_mask None selects the causal chunk rule (prefill)."""
+    torch = _torch()
+    T, hq, d = q.shape
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d)
+    S, _ = attention_plan(T, hq, kv.n_kv_heads, d, ctx_len, anc_mask is None, n_splits)
+    if part_o is None:
+        part_o = torch.empty((S, T, hq, d), dtype=torch.float32, device=q.device)
+    if part_lse is None:
+        part_lse = torch.empty((S, T, hq), dtype=torch.float32, device=q.device)
+    m_ptr = None
+    if anc_mask is not None:
+        m = np.ascontiguousarray(np.asarray(anc_mask, dtype=np.uint64))
+        if m.shape != (T,):
+            raise ValueError(f"anc_mask must have shape ({T},)")
+        m_ptr = m.ctypes.data
+    layer = kv._layer()
+    rc = load_library().stv_attention_partials(
+        _dev_ptr(q, torch.float32, "q"), T, hq, ctypes.byref(layer), ctx_len, m_ptr,
+        float(softmax_scale), n_splits, _dev_ptr(part_o, torch.float32, "part_o", (S, T, hq, d)),
+        _dev_ptr(part_lse, torch.float32, "part_lse", (S, T, hq)), _stream(q.device))
+    _check(rc)
+    return part_o, part_lse
+
+
+def split_merge(part_o, part_lse, out=None, out_lse=None):
+    """Log-sum-exp merge of part_o [S][rows][D] with part_lse [S][rows]."""
+    torch = _torch()
+    S, rows, d = part_o.shape
+    if out is None:
+        out = torch.empty((rows, d), dtype=torch.float32, device=part_o.device)
+    rc = load_library().stv_split_merge(
+        _dev_ptr(part_o, torch.float32, "part_o"),
+        _dev_ptr(part_lse, torch.float32, "part_lse", (S, rows)), S, rows, d,
+        _dev_ptr(out, torch.float32, "out", (rows, d)),
+        _dev_ptr(out_lse, torch.float32, "out_lse", (rows,)), _stream(part_o.device))
+    _check(rc)
+    return out

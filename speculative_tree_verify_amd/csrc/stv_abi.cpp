@@ -1,0 +1,273 @@
+// C-ABI host layer: argument validation (all before any HIP call), the
+// split plan, and kernel launches.  See include/stv.h for the contract.
+#include "stv.h"
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "stv_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int ok() {
+    g_err[0] = '\0';
+    return STV_OK;
+}
+
+bool head_dim_ok(int D) { return D == 64 || D == 128 || D == 256; }
+
+int check_heads(int Hq, int Hkv, int D) {
+    if (Hkv <= 0 || Hq <= 0) return fail(STV_EINVAL, "head counts must be positive (Hq=%d, Hkv=%d)", Hq, Hkv);
+    if (Hq % Hkv) return fail(STV_EINVAL, "n_q_heads (%d) must be a multiple of n_kv_heads (%d)", Hq, Hkv);
+    if (!head_dim_ok(D)) return fail(STV_EINVAL, "head_dim %d unsupported (64, 128 or 256)", D);
+    return STV_OK;
+}
+
+// Rows must form a forest: own bit set, no higher bit, and the remaining
+// bits equal to the mask of the highest of them (the parent).
+int check_mask(const uint64_t *m, int T) {
+    for (int i = 0; i < T; ++i) {
+        const uint64_t own = 1ull << i;
+        if (!(m[i] & own)) return fail(STV_EMASK, "anc_mask[%d] lacks its own bit", i);
+        if (i < 63 && (m[i] >> (i + 1))) return fail(STV_EMASK, "anc_mask[%d] has a bit above row %d", i, i);
+        const uint64_t rest = m[i] & ~own;
+        if (rest) {
+            const int p = 63 - __builtin_clzll(rest);
+            if (m[p] != rest)
+                return fail(STV_EMASK, "anc_mask[%d] is not its parent's (row %d) mask plus itself", i, p);
+        }
+    }
+    return STV_OK;
+}
+
+int check_kv(const stv_kv_layer *kv, int Hq, int L, int T) {
+    if (!kv) return fail(STV_EINVAL, "kv is NULL");
+    if (!kv->k_codes || !kv->k_scales || !kv->v_codes || !kv->v_scales)
+        return fail(STV_EINVAL, "kv has a NULL array");
+    int rc = check_heads(Hq, kv->n_kv_heads, kv->head_dim);
+    if (rc) return rc;
+    if (kv->capacity <= 0) return fail(STV_EINVAL, "capacity must be positive");
+    if (L < 0) return fail(STV_EINVAL, "ctx_len must be >= 0");
+    if ((long long)L + T > kv->capacity)
+        return fail(STV_ECAPACITY, "ctx_len + T = %lld exceeds capacity %d", (long long)L + T, kv->capacity);
+    return STV_OK;
+}
+
+// With partials_o set, only the split kernel runs and every split (even when
+// S == 1) writes its partial to partials_o / partials_lse.
+int attention_common(const float *q, int T, int Hq, const stv_kv_layer *kv, int L,
+                     const uint64_t *mask, bool causal, float scale, float *out, float *out_lse,
+                     void *ws, size_t ws_bytes, int n_splits, int32_t *dbg_logits, int8_t *dbg_q,
+                     float *dbg_qscale, void *stream, float *partials_o = nullptr,
+                     float *partials_lse = nullptr) {
+    const bool partials_only = partials_o != nullptr;
+    if (!q || (!out && !partials_only)) return fail(STV_EINVAL, "q and out must not be NULL");
+    if (partials_only && !partials_lse) return fail(STV_EINVAL, "part_lse must not be NULL");
+    if (T < 1) return fail(STV_EINVAL, "T must be >= 1 (got %d)", T);
+    if (!causal && T > STV_MAX_TREE_ROWS) return fail(STV_EINVAL, "verify supports at most 64 tree rows (got %d)", T);
+    if ((long long)T * Hq >= (1ll << 31)) return fail(STV_EINVAL, "T * n_q_heads too large");
+    if (n_splits < 0) return fail(STV_EINVAL, "n_splits must be >= 0");
+    if (!isfinite(scale)) return fail(STV_EINVAL, "softmax_scale must be finite");
+    int rc = check_kv(kv, Hq, L, T);
+    if (rc) return rc;
+    if (!causal) {
+        if (!mask) return fail(STV_EINVAL, "anc_mask must not be NULL");
+        rc = check_mask(mask, T);
+        if (rc) return rc;
+    }
+    const int D = kv->head_dim, Hkv = kv->n_kv_heads;
+    if (dbg_logits && (long long)T * Hq * (L + T) * (D / 32) >= (1ll << 40))
+        return fail(STV_EINVAL, "dbg_logits would be too large");
+    const stv::Plan plan = stv::make_plan(T, Hq, Hkv, D, L, causal, n_splits);
+    if (!partials_only && plan.S > 1 && (!ws || ws_bytes < plan.ws_bytes))
+        return fail(STV_EWORKSPACE, "workspace of %zu bytes needed for %d splits (got %zu)",
+                    plan.ws_bytes, plan.S, ws ? ws_bytes : (size_t)0);
+
+    stv::AttnArgs a;
+    memset(&a, 0, sizeof a);
+    a.q = q;
+    a.kc = kv->k_codes;
+    a.ks = kv->k_scales;
+    a.vc = kv->v_codes;
+    a.vs = kv->v_scales;
+    a.out = out;
+    a.out_lse = out_lse;
+    const size_t rows = (size_t)T * Hq;
+    if (partials_only) {
+        a.part_o = partials_o;
+        a.part_lse = partials_lse;
+    } else if (plan.S > 1) {
+        a.part_o = static_cast<float *>(ws);
+        a.part_lse = a.part_o + (size_t)plan.S * rows * D;
+    }
+    a.dbg_logits = dbg_logits;
+    a.dbg_q = dbg_q;
+    a.dbg_qscale = dbg_qscale;
+    a.T = T;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.G = Hq / Hkv;
+    a.cap = kv->capacity;
+    a.L = L;
+    a.N = L + T;
+    a.R = T * a.G;
+    a.S = plan.S;
+    a.split_len = plan.split_len;
+    a.NRG = plan.NRG;
+    a.n_hs_pad = ((Hkv * plan.S + 7) / 8) * 8;
+    a.scale_log2 = scale * 1.44269504088896340736f;
+    if (!causal)
+        for (int i = 0; i < T; ++i) a.mask[i] = mask[i];
+
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const bool debug = dbg_logits || dbg_q || dbg_qscale;
+    hipError_t e = stv::launch_attention(a, D, plan.NW, causal, debug, st);
+    if (e != hipSuccess) return fail(STV_EHIP, "attention launch failed: %s", hipGetErrorString(e));
+    if (!partials_only && plan.S > 1) {
+        e = stv::launch_merge(a.part_o, a.part_lse, plan.S, (int)rows, D, out, out_lse, st);
+        if (e != hipSuccess) return fail(STV_EHIP, "merge launch failed: %s", hipGetErrorString(e));
+    }
+    return ok();
+}
+
+}  // namespace
+
+namespace stv {
+
+Plan make_plan(int T, int Hq, int Hkv, int D, int L, bool causal, int n_splits_req) {
+    Plan p;
+    const int G = Hq / Hkv;
+    const long long R = (long long)T * G;
+    const long long row_tiles = (R + kRowTile - 1) / kRowTile;
+    p.NW = row_tiles >= 4 ? 4 : (row_tiles >= 2 ? 2 : 1);
+    p.NRG = (int)((row_tiles + p.NW - 1) / p.NW);
+    const long long N = (long long)L + T;
+    const long long n_tiles = (N + kKeyTile - 1) / kKeyTile;
+    long long S;
+    if (n_splits_req > 0) {
+        S = n_splits_req;
+    } else {
+        // Aim for about two resident work-groups per CU on 256 CUs, with
+        // at least four tiles per split.
+        const long long target = 256LL * (8 / p.NW);
+        const long long groups = (long long)Hkv * p.NRG;
+        S = (target + groups - 1) / groups;
+        const long long max_s = n_tiles / 4 > 0 ? n_tiles / 4 : 1;
+        if (S > max_s) S = max_s;
+        if (causal && groups >= 512) S = 1;
+    }
+    if (S < 1) S = 1;
+    if (S > n_tiles) S = n_tiles > 0 ? n_tiles : 1;
+    // Whole tiles per split; dropping splits that would be empty, then
+    // spreading the tiles evenly over the rest, keeps S and makes split s
+    // cover keys [s*P, min(N, (s+1)*P)) with P = 32*ceil(ceil(N/32)/S).
+    long long tiles_per_split = (n_tiles + S - 1) / S;
+    S = (n_tiles + tiles_per_split - 1) / tiles_per_split;
+    if (S < 1) S = 1;
+    tiles_per_split = (n_tiles + S - 1) / S;
+    p.split_len = (int)(tiles_per_split * kKeyTile);
+    p.S = (int)S;
+    const size_t rows = (size_t)T * Hq;
+    p.ws_bytes = p.S > 1 ? (size_t)p.S * rows * ((size_t)D + 1) * sizeof(float) : 0;
+    (void)D;
+    return p;
+}
+
+}  // namespace stv
+
+extern "C" {
+
+const char *stv_last_error(void) { return g_err; }
+
+int32_t stv_abi_version(void) { return 1; }
+
+int stv_kv_quant_pack(const float *x, int32_t n_tok, int32_t pos0, uint32_t *codes,
+                      uint16_t *scales, int32_t n_kv_heads, int32_t head_dim, int32_t capacity,
+                      void *stream) {
+    if (n_tok < 0) return fail(STV_EINVAL, "n_tok must be >= 0");
+    if (n_kv_heads <= 0) return fail(STV_EINVAL, "n_kv_heads must be positive");
+    if (!head_dim_ok(head_dim)) return fail(STV_EINVAL, "head_dim %d unsupported (64, 128 or 256)", head_dim);
+    if (capacity <= 0) return fail(STV_EINVAL, "capacity must be positive");
+    if (pos0 < 0 || (long long)pos0 + n_tok > capacity)
+        return fail(STV_ECAPACITY, "positions %d..%lld outside capacity %d", pos0,
+                    (long long)pos0 + n_tok - 1, capacity);
+    if (n_tok == 0) return ok();
+    if (!x || !codes || !scales) return fail(STV_EINVAL, "x, codes and scales must not be NULL");
+    hipError_t e = stv::launch_kv_pack(x, n_tok, pos0, codes, scales, n_kv_heads, head_dim,
+                                       capacity, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(STV_EHIP, "kv pack launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int stv_attention_plan(int32_t T, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                       int32_t ctx_len, int32_t causal, int32_t n_splits_req,
+                       int32_t *n_splits_out, size_t *workspace_bytes_out) {
+    if (T < 1) return fail(STV_EINVAL, "T must be >= 1");
+    if (!causal && T > STV_MAX_TREE_ROWS) return fail(STV_EINVAL, "verify supports at most 64 tree rows");
+    int rc = check_heads(n_q_heads, n_kv_heads, head_dim);
+    if (rc) return rc;
+    if (ctx_len < 0) return fail(STV_EINVAL, "ctx_len must be >= 0");
+    if (n_splits_req < 0) return fail(STV_EINVAL, "n_splits must be >= 0");
+    if ((long long)T * n_q_heads >= (1ll << 31)) return fail(STV_EINVAL, "T * n_q_heads too large");
+    const stv::Plan p = stv::make_plan(T, n_q_heads, n_kv_heads, head_dim, ctx_len, causal != 0,
+                                       n_splits_req);
+    if (n_splits_out) *n_splits_out = p.S;
+    if (workspace_bytes_out) *workspace_bytes_out = p.ws_bytes;
+    return ok();
+}
+
+int stv_verify_attention(const float *q, int32_t T, int32_t n_q_heads, const stv_kv_layer *kv,
+                         int32_t ctx_len, const uint64_t *anc_mask, float softmax_scale,
+                         float *out, float *out_lse, void *workspace, size_t workspace_bytes,
+                         int32_t n_splits, int32_t *dbg_logits, int8_t *dbg_q,
+                         float *dbg_qscale, void *stream) {
+    return attention_common(q, T, n_q_heads, kv, ctx_len, anc_mask, false, softmax_scale, out,
+                            out_lse, workspace, workspace_bytes, n_splits, dbg_logits, dbg_q,
+                            dbg_qscale, stream);
+}
+
+int stv_prefill_attention(const float *q, int32_t T, int32_t n_q_heads, const stv_kv_layer *kv,
+                          int32_t ctx_len, float softmax_scale, float *out, float *out_lse,
+                          void *workspace, size_t workspace_bytes, int32_t n_splits,
+                          int32_t *dbg_logits, int8_t *dbg_q, float *dbg_qscale, void *stream) {
+    return attention_common(q, T, n_q_heads, kv, ctx_len, nullptr, true, softmax_scale, out,
+                            out_lse, workspace, workspace_bytes, n_splits, dbg_logits, dbg_q,
+                            dbg_qscale, stream);
+}
+
+int stv_attention_partials(const float *q, int32_t T, int32_t n_q_heads,
+                           const stv_kv_layer *kv, int32_t ctx_len, const uint64_t *anc_mask,
+                           float softmax_scale, int32_t n_splits, float *part_o,
+                           float *part_lse, void *stream) {
+    if (!part_o) return fail(STV_EINVAL, "part_o must not be NULL");
+    return attention_common(q, T, n_q_heads, kv, ctx_len, anc_mask, anc_mask == nullptr,
+                            softmax_scale, nullptr, nullptr, nullptr, 0, n_splits, nullptr,
+                            nullptr, nullptr, stream, part_o, part_lse);
+}
+
+int stv_split_merge(const float *part_o, const float *part_lse, int32_t S, int32_t rows,
+                    int32_t D, float *out, float *out_lse, void *stream) {
+    if (S < 1) return fail(STV_EINVAL, "S must be >= 1");
+    if (rows < 0) return fail(STV_EINVAL, "rows must be >= 0");
+    if (D < 1 || D > 1024) return fail(STV_EINVAL, "D must be in 1..1024");
+    if (rows == 0) return ok();
+    if (!part_o || !part_lse || !out) return fail(STV_EINVAL, "part_o, part_lse and out must not be NULL");
+    hipError_t e = stv::launch_merge(part_o, part_lse, S, rows, D, out, out_lse,
+                                     static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(STV_EHIP, "merge launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+}  // extern "C"

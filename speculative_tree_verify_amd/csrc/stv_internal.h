@@ -1,0 +1,54 @@
+// Internal interface between the C-ABI host layer (stv_abi.cpp) and the HIP
+// kernels (stv_kernels.hip).  Not installed; not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace stv {
+
+constexpr int kKeyTile = 32;     // keys per tile: the M side of one 32x32 MFMA
+constexpr int kRowTile = 32;     // query rows per wave: the N side of one 32x32 MFMA
+
+// Arguments of the split attention kernel.  Rows are ordered per kv head as
+// rho = t * G + g (tree row t, query head h = head * G + g); the flat output
+// row is t * Hq + h.
+struct AttnArgs {
+    const float *q;
+    const uint32_t *kc;
+    const uint16_t *ks;
+    const uint32_t *vc;
+    const uint16_t *vs;
+    float *out;          // [T*Hq][D], written when part_o is NULL (then S == 1)
+    float *out_lse;      // nullable [T*Hq], written when part_o is NULL
+    float *part_o;       // nullable [S][T*Hq][D]: set, every split writes its partial
+    float *part_lse;     // [S][T*Hq] when part_o is set
+    int32_t *dbg_logits; // nullable [T*Hq][N][D/32]
+    int8_t *dbg_q;       // nullable [T*Hq][D]
+    float *dbg_qscale;   // nullable [T*Hq]
+    int32_t T, Hq, Hkv, G, cap, L, N, R;
+    int32_t S, split_len, NRG, n_hs_pad;
+    float scale_log2;    // softmax_scale * log2(e)
+    uint64_t mask[64];   // verify only: ancestor masks of the tree rows
+};
+
+struct Plan {
+    int NW;          // waves (32-row tiles) per work-group
+    int NRG;         // row groups per kv head
+    int S;           // context splits
+    int split_len;   // keys per split, a multiple of kKeyTile
+    size_t ws_bytes; // workspace for the partials
+};
+
+Plan make_plan(int T, int Hq, int Hkv, int D, int L, bool causal, int n_splits_req);
+
+// Launchers return the hipError_t of the launch.
+hipError_t launch_attention(const AttnArgs &a, int D, int NW, bool causal, bool debug,
+                            hipStream_t stream);
+hipError_t launch_merge(const float *part_o, const float *part_lse, int S, int rows, int D,
+                        float *out, float *out_lse, hipStream_t stream);
+hipError_t launch_kv_pack(const float *x, int n_tok, int pos0, uint32_t *codes,
+                          uint16_t *scales, int Hkv, int D, int cap, hipStream_t stream);
+
+}  // namespace stv

@@ -29,7 +29,7 @@ import numpy as np
 __all__ = [
     "Geometry", "CONFIGS", "EXTRA_CONFIGS", "KVCache",
     "make_kv", "make_q", "make_tree_parents", "ancestor_masks",
-    "chain_parents", "all_tree_shapes",
+    "chain_parents", "all_tree_shapes", "make_new_rows",
 ]
 
 
@@ -163,3 +163,8 @@ def all_tree_shapes(n_nodes: int):
     if n_nodes == 0:
         return
     yield from rec([-1])
+
+
+def make_new_rows(rng: np.random.Generator, n_tok: int, n_kv_heads: int, head_dim: int) -> np.ndarray:
+    """fp32 K or V rows of the new tokens, before they enter the 3-bit cache."""
+    return rng.standard_normal((n_tok, n_kv_heads, head_dim), dtype=np.float32)

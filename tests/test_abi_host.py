@@ -1,0 +1,211 @@
+"""Host-side checks of the C-ABI library: it loads, exports every entry point
+that include/stv.h declares, and rejects bad arguments before any HIP call.
+
+No test here makes a call that passes validation with a device pointer, so
+nothing is ever launched: valid masks are exercised by pairing them with a
+workspace that is too small, which the library checks after the mask.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "stv.h")
+FAKE = 0x10000          # never dereferenced: every call below fails validation
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import speculative_tree_verify_amd as stv
+    if not os.path.exists(stv.LIB_PATH):
+        from speculative_tree_verify_amd import build_lib
+        build_lib.build()
+    return stv.load_library()
+
+
+@pytest.fixture(scope="module")
+def stvmod():
+    import speculative_tree_verify_amd as stv
+    return stv
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(stv_[a-z_]+)\(", text, re.M)))
+
+
+def test_header_declares_the_four_operations():
+    names = _declared()
+    for op in ("stv_kv_quant_pack", "stv_verify_attention", "stv_prefill_attention",
+               "stv_split_merge", "stv_attention_plan", "stv_last_error", "stv_abi_version"):
+        assert op in names
+
+
+def test_library_exports_every_declared_symbol(lib, stvmod):
+    out = subprocess.run(["nm", "-D", "--defined-only", stvmod.LIB_PATH], check=True,
+                         capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\sT\s+(\S+)", out))
+    for name in _declared():
+        assert name in exported, name
+        assert hasattr(lib, name)
+    assert lib.stv_abi_version() == 1
+
+
+def _layer(stvmod, hkv=4, d=256, cap=1000):
+    return stvmod._KVLayer(FAKE, FAKE, FAKE, FAKE, hkv, d, cap)
+
+
+def _verify(lib, stvmod, T=8, hq=24, layer=None, L=100, mask=None, scale=0.0625, out=FAKE,
+            ws=None, ws_bytes=0, n_splits=0, q=FAKE):
+    layer = layer or _layer(stvmod)
+    if mask is None:
+        mask = synth.ancestor_masks(synth.chain_parents(T))
+    m = np.ascontiguousarray(np.asarray(mask, dtype=np.uint64))
+    return lib.stv_verify_attention(q, T, hq, ctypes.byref(layer), L,
+                                    m.ctypes.data if m.size else None, scale, out, None,
+                                    ws, ws_bytes, n_splits, None, None, None, None)
+
+
+def _err(lib):
+    return lib.stv_last_error().decode()
+
+
+def test_verify_argument_errors(lib, stvmod):
+    E = stvmod
+    assert _verify(lib, stvmod, T=0, mask=np.zeros(0)) == E.STV_EINVAL
+    assert _verify(lib, stvmod, T=65, mask=np.zeros(65)) == E.STV_EINVAL
+    assert "64" in _err(lib)
+    assert _verify(lib, stvmod, hq=25) == E.STV_EINVAL                          # Hq % Hkv
+    assert _verify(lib, stvmod, layer=_layer(stvmod, d=96)) == E.STV_EINVAL     # D % 32 == 0 but unsupported
+    assert _verify(lib, stvmod, layer=_layer(stvmod, d=100)) == E.STV_EINVAL
+    assert _verify(lib, stvmod, layer=_layer(stvmod, hkv=0)) == E.STV_EINVAL
+    assert _verify(lib, stvmod, L=993) == E.STV_ECAPACITY                       # 993 + 8 > 1000
+    assert "capacity" in _err(lib)
+    assert _verify(lib, stvmod, L=-1) == E.STV_EINVAL
+    assert _verify(lib, stvmod, q=None) == E.STV_EINVAL
+    assert _verify(lib, stvmod, out=None) == E.STV_EINVAL
+    assert _verify(lib, stvmod, scale=float("inf")) == E.STV_EINVAL
+    assert _verify(lib, stvmod, n_splits=-2) == E.STV_EINVAL
+    layer = stvmod._KVLayer(FAKE, None, FAKE, FAKE, 4, 256, 1000)
+    assert _verify(lib, stvmod, layer=layer) == E.STV_EINVAL
+
+
+def test_verify_mask_errors(lib, stvmod):
+    E = stvmod
+    good = synth.ancestor_masks(np.array([-1, 0, 0, 1, 1, 2, 3, 6]))
+    bad = good.copy()
+    bad[3] &= ~np.uint64(1 << 3)                        # own bit missing
+    assert _verify(lib, stvmod, mask=bad) == E.STV_EMASK
+    bad = good.copy()
+    bad[2] |= np.uint64(1 << 5)                         # bit above the row
+    assert _verify(lib, stvmod, mask=bad) == E.STV_EMASK
+    bad = good.copy()
+    bad[6] = np.uint64((1 << 6) | (1 << 2))             # parent 2, but misses 2's ancestor 0
+    assert _verify(lib, stvmod, mask=bad) == E.STV_EMASK
+    bad = good.copy()
+    bad[4] = np.uint64((1 << 4) | (1 << 3) | (1 << 2) | 1)   # two branches: not a path
+    assert _verify(lib, stvmod, mask=bad) == E.STV_EMASK
+    assert "anc_mask[4]" in _err(lib)
+
+
+def _big_plan_args(stvmod, lib, T):
+    # a context long enough that the automatic plan splits it (S > 1)
+    L = 60000
+    s = ctypes.c_int32()
+    ws = ctypes.c_size_t()
+    assert lib.stv_attention_plan(T, 24, 4, 256, L, 0, 0, ctypes.byref(s), ctypes.byref(ws)) == 0
+    assert s.value > 1 and ws.value > 0
+    return L, ws.value
+
+
+def test_valid_masks_pass_validation(lib, stvmod):
+    """Every 8-row tree shape, a forest, and random 64-node trees pass the mask
+    check: the call then stops at the (deliberately small) workspace."""
+    layer = _layer(stvmod, cap=70000)
+    L, need = _big_plan_args(stvmod, lib, 8)
+    n = 0
+    for parent in synth.all_tree_shapes(8):
+        rc = _verify(lib, stvmod, T=8, layer=layer, L=L, mask=synth.ancestor_masks(parent),
+                     ws=FAKE, ws_bytes=need - 1)
+        assert rc == stvmod.STV_EWORKSPACE, _err(lib)
+        n += 1
+    assert n == 5040
+    forest = synth.ancestor_masks(np.array([-1, -1, 0, 1, -1, 4]))
+    rc = _verify(lib, stvmod, T=6, layer=layer, L=L, mask=forest, ws=FAKE, ws_bytes=0)
+    assert rc == stvmod.STV_EWORKSPACE
+    rng = np.random.default_rng(5)
+    L64, need64 = _big_plan_args(stvmod, lib, 64)
+    for _ in range(50):
+        m = synth.ancestor_masks(synth.make_tree_parents(rng, 64, 8))
+        rc = _verify(lib, stvmod, T=64, layer=layer, L=L64, mask=m, ws=FAKE, ws_bytes=need64 - 1)
+        assert rc == stvmod.STV_EWORKSPACE, _err(lib)
+        assert "workspace" in _err(lib)
+
+
+def test_prefill_argument_errors(lib, stvmod):
+    E = stvmod
+    layer = _layer(stvmod, cap=5000)
+
+    def call(T=100, L=100, ws=None, ws_bytes=0, n_splits=0):
+        return lib.stv_prefill_attention(FAKE, T, 24, ctypes.byref(layer), L, 0.0625, FAKE, None,
+                                         ws, ws_bytes, n_splits, None, None, None, None)
+    assert call(T=0) == E.STV_EINVAL
+    assert call(T=4901, L=100) == E.STV_ECAPACITY
+    assert call(n_splits=4, ws=FAKE, ws_bytes=10) == E.STV_EWORKSPACE
+
+
+def test_kv_pack_argument_errors(lib, stvmod):
+    E = stvmod
+    f = lib.stv_kv_quant_pack
+    assert f(FAKE, -1, 0, FAKE, FAKE, 4, 256, 100, None) == E.STV_EINVAL
+    assert f(FAKE, 10, 95, FAKE, FAKE, 4, 256, 100, None) == E.STV_ECAPACITY
+    assert f(FAKE, 10, -1, FAKE, FAKE, 4, 256, 100, None) == E.STV_ECAPACITY
+    assert f(FAKE, 10, 0, FAKE, FAKE, 4, 48, 100, None) == E.STV_EINVAL
+    assert f(FAKE, 10, 0, FAKE, FAKE, 0, 256, 100, None) == E.STV_EINVAL
+    assert f(None, 10, 0, FAKE, FAKE, 4, 256, 100, None) == E.STV_EINVAL
+    assert f(FAKE, 0, 100, FAKE, FAKE, 4, 256, 100, None) == E.STV_OK      # nothing to do
+    assert _err(lib) == ""
+
+
+def test_merge_argument_errors(lib, stvmod):
+    E = stvmod
+    f = lib.stv_split_merge
+    assert f(FAKE, FAKE, 0, 10, 256, FAKE, None, None) == E.STV_EINVAL
+    assert f(FAKE, FAKE, 2, -1, 256, FAKE, None, None) == E.STV_EINVAL
+    assert f(FAKE, FAKE, 2, 10, 0, FAKE, None, None) == E.STV_EINVAL
+    assert f(FAKE, FAKE, 2, 10, 2000, FAKE, None, None) == E.STV_EINVAL
+    assert f(None, FAKE, 2, 10, 256, FAKE, None, None) == E.STV_EINVAL
+    assert f(FAKE, FAKE, 2, 0, 256, FAKE, None, None) == E.STV_OK          # no rows: no launch
+
+
+@pytest.mark.parametrize("T,hq,hkv,d,L,causal", [
+    (1, 24, 4, 256, 8192, 0), (64, 24, 4, 256, 32768, 0), (64, 24, 4, 256, 262144, 0),
+    (8, 24, 4, 256, 262144, 0), (4096, 24, 4, 256, 32768, 1), (8, 4, 1, 64, 512, 0),
+])
+def test_plan_is_consistent(stvmod, T, hq, hkv, d, L, causal):
+    for req in (0, 1, 3, 17, 100000):
+        S, ws = stvmod.attention_plan(T, hq, hkv, d, L, bool(causal), req)
+        n_tiles = -(-(L + T) // 32)
+        assert 1 <= S <= n_tiles
+        if req:
+            assert S <= req
+        assert ws == (S * T * hq * (d + 1) * 4 if S > 1 else 0)
+        # the documented split layout covers every key, each split non-empty
+        P = 32 * -(-n_tiles // S)
+        assert (S - 1) * P < L + T <= S * P
+    S0, _ = stvmod.attention_plan(T, hq, hkv, d, L, bool(causal), 0)
+    S1, _ = stvmod.attention_plan(T, hq, hkv, d, L, bool(causal), 0)
+    assert S0 == S1
+
+
+def test_product_path_refuses_to_run_without_the_library(stvmod, monkeypatch, tmp_path):
+    monkeypatch.setattr(stvmod, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(stvmod, "_lib", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        stvmod.load_library()

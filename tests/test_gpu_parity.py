@@ -1,0 +1,324 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+The bar: quantized Q (int8 codes and fp32 scales) and the int32 per-block
+Q.K^T sums bit-exact; attention outputs within 2e-3 relative error per row,
+measured as max_d |o - o_ref| / max_d |o_ref| (the oracle is fp64); lse
+within 2e-3 absolute.  Inputs are seeded and synthetic (synth module).
+"""
+import math
+
+import numpy as np
+import pytest
+
+import synth
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+
+
+@pytest.fixture(scope="module")
+def gpu():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import speculative_tree_verify_amd as stv
+    stv.load_library()
+    return stv, torch
+
+
+def _visible(T, L, mask, n):
+    vis = np.zeros((T, n), dtype=bool)
+    vis[:, :L] = True
+    for t in range(T):
+        for a in range(T):
+            vis[t, L + a] = (a <= t) if mask is None else bool((int(mask[t]) >> a) & 1)
+    return vis
+
+
+def _row_err(got, ref):
+    den = np.max(np.abs(ref), axis=-1)
+    num = np.max(np.abs(got - ref), axis=-1)
+    return num / np.where(den > 0, den, 1.0)
+
+
+def _mask_for(rng, kind, T, depth=8):
+    if kind == "prefill":
+        return None
+    if kind == "chain":
+        return synth.ancestor_masks(synth.chain_parents(T))
+    return synth.ancestor_masks(synth.make_tree_parents(rng, T, depth))
+
+
+def run_case(gpu, orc, hq, hkv, d, L, T, kind, seed, n_splits=0, scale_mul=1.0,
+             cap_extra=3, rows=None, check_logits=True, host=None, q=None, mask=None):
+    """Oracle vs GPU on one input.  The outputs come from the production
+    kernel (no debug outputs requested); a second call with debug outputs
+    checks the int8 Q and the int32 logits bit for bit."""
+    stv, torch = gpu
+    rng = np.random.default_rng(seed)
+    if host is None:
+        host = synth.make_kv(rng, hkv, d, L + T, L + T + cap_extra)
+    if q is None:
+        q = synth.make_q(rng, T, hq, d)
+    if mask is None and kind != "prefill":
+        mask = _mask_for(rng, kind, T)
+    scale = scale_mul / math.sqrt(d)
+    ref = orc.attention(q, host, L, mask, scale, rows=rows, want_logits=check_logits)
+    kv = stv.KVCache.from_host(host)
+    qd = torch.from_numpy(q).cuda()
+    lse = torch.empty((T, hq), dtype=torch.float32, device="cuda")
+
+    def call(debug):
+        if kind == "prefill":
+            return stv.prefill_attention(qd, kv, L, scale, out_lse=lse, n_splits=n_splits,
+                                         debug=debug)
+        return stv.verify_attention(qd, kv, L, mask, scale, out_lse=lse, n_splits=n_splits,
+                                    debug=debug)
+
+    flat = np.arange(T * hq) if rows is None else np.asarray(rows)
+    flat_d = torch.from_numpy(flat).cuda()
+    out = call(False)
+    torch.cuda.synchronize()
+    out_g = out.reshape(T * hq, d)[flat_d].cpu().numpy()
+    lse_g = lse.reshape(-1)[flat_d].cpu().numpy()
+    err = _row_err(out_g, ref["out"])
+    assert np.all(np.isfinite(out_g))
+    assert err.max() <= TOL, f"max row error {err.max():.3g}"
+    assert np.max(np.abs(lse_g - ref["lse"])) <= TOL
+
+    names = ("logits", "q8", "qscale") if check_logits else ("q8", "qscale")
+    out2, dbg = call(names)
+    torch.cuda.synchronize()
+    q8 = dbg["q8"].reshape(T * hq, d)[flat_d].cpu().numpy()
+    qs = dbg["qscale"].reshape(-1)[flat_d].cpu().numpy()
+    assert np.array_equal(q8, ref["qi8"]), "int8 Q differs"
+    assert np.array_equal(qs.view(np.uint32), ref["sq"].view(np.uint32)), "Q scale differs"
+    if check_logits:
+        lg = dbg["logits"].reshape(T * hq, L + T, d // 32)[flat_d].cpu().numpy()
+        vis = _visible(T, L, mask, L + T)
+        for i, r in enumerate(flat):
+            v = vis[r // hq]
+            assert np.array_equal(lg[i][v], ref["logits"][i][v]), f"int32 logits differ, row {r}"
+    err2 = _row_err(out2.reshape(T * hq, d)[flat_d].cpu().numpy(), ref["out"])
+    assert err2.max() <= TOL
+    return out, err.max()
+
+
+CASES = [
+    # name,            Hq, Hkv,  D,    L,   T, kind,     seed, n_splits
+    ("tiny_auto",        4, 1,   64,  512,   8, "chain",   0, 0),
+    ("tiny_1split",      4, 1,   64,  512,   8, "chain",   0, 1),
+    ("tiny_3split",      4, 1,   64,  512,   8, "chain",   0, 3),
+    ("tree64_ragged",   24, 4,  256, 1000,  64, "tree",  101, 0),
+    ("tree64_1split",   24, 4,  256,  333,  64, "tree",  102, 1),
+    ("tree8_d128",       8, 2,  128,  777,   8, "tree",  103, 0),
+    ("tree17_d128",      8, 2,  128,  333,  17, "tree",  104, 5),
+    ("decode_t1",       24, 4,  256, 2049,   1, "tree",  105, 0),
+    ("decode_t1_L0",    24, 4,  256,    0,   1, "tree",  106, 0),
+    ("tree_L0",          4, 2,   64,    0,   5, "tree",  107, 0),
+    ("tree_1key_ctx",    4, 2,   64,    1,  33, "tree",  108, 0),
+    ("prefill_small",   12, 2,  128,  100,  70, "prefill", 109, 0),
+    ("prefill_splits",  24, 4,  256,   64,  40, "prefill", 110, 4),
+    ("prefill_L0",       6, 3,   64,    0,  97, "prefill", 111, 0),
+]
+
+
+@pytest.mark.parametrize("name,hq,hkv,d,L,T,kind,seed,ns", CASES, ids=[c[0] for c in CASES])
+def test_parity(gpu, orc, name, hq, hkv, d, L, T, kind, seed, ns):
+    run_case(gpu, orc, hq, hkv, d, L, T, kind, seed, n_splits=ns)
+
+
+@pytest.mark.parametrize("scale_mul", [8.0, 32.0])
+def test_parity_peaked(gpu, orc, scale_mul):
+    """Large logit scales make the softmax nearly one-hot (the workload's own
+    distributions give diffuse attention, which averages errors away)."""
+    run_case(gpu, orc, 24, 4, 256, 700, 16, "tree", 120, scale_mul=scale_mul)
+    run_case(gpu, orc, 12, 2, 128, 90, 50, "prefill", 121, scale_mul=scale_mul)
+
+
+def test_parity_planted_keys(gpu, orc):
+    """Context keys whose codes follow sign(q) of one row dominate that row."""
+    rng = np.random.default_rng(122)
+    hq, hkv, d, L, T = 8, 2, 128, 400, 8
+    host = synth.make_kv(rng, hkv, d, L + T, L + T)
+    q = synth.make_q(rng, T, hq, d)
+    for t in range(T):
+        h = (3 * t) % hq
+        j = int(rng.integers(0, L))
+        codes = np.where(q[t, h] > 0, 7, 1).astype(int)
+        for b in range(d // 32):
+            host.k_codes[h // (hq // hkv), j, b] = orc.pack_block(codes[32 * b:32 * b + 32])
+    run_case(gpu, orc, hq, hkv, d, L, T, "tree", 123, host=host, q=q)
+
+
+def test_residue_sweep(gpu, orc):
+    """Context lengths over every residue of the 32-key tile, and split
+    boundaries moved with them (a length-dependent corruption shows up as
+    a parity failure at one residue)."""
+    rng = np.random.default_rng(130)
+    for r in range(32):
+        L = 2048 + r
+        run_case(gpu, orc, 4, 1, 64, L, 8, "tree", 1000 + r, n_splits=int(rng.integers(0, 9)))
+
+
+def test_all_8_row_tree_shapes(gpu, orc):
+    """Every one of the 5,040 8-row tree shapes against the oracle."""
+    stv, torch = gpu
+    hq, hkv, d, L, T = 4, 1, 64, 40, 8
+    rng = np.random.default_rng(131)
+    host = synth.make_kv(rng, hkv, d, L + T, L + T)
+    q = synth.make_q(rng, T, hq, d)
+    kv = stv.KVCache.from_host(host)
+    qd = torch.from_numpy(q).cuda()
+    scale = 4.0 / math.sqrt(d)
+    masks, outs = [], []
+    for parent in synth.all_tree_shapes(T):
+        m = synth.ancestor_masks(parent)
+        masks.append(m)
+        outs.append(stv.verify_attention(qd, kv, L, m, scale))
+    torch.cuda.synchronize()
+    worst = 0.0
+    for m, o in zip(masks, outs):
+        ref = orc.attention(q, host, L, m, scale)
+        err = _row_err(o.reshape(T * hq, d).cpu().numpy(), ref["out"]).max()
+        worst = max(worst, err)
+    assert len(masks) == 5040
+    assert worst <= TOL, worst
+
+
+def test_determinism(gpu, orc):
+    stv, torch = gpu
+    rng = np.random.default_rng(140)
+    host = synth.make_kv(rng, 4, 256, 5000 + 64, 5000 + 64)
+    q = torch.from_numpy(synth.make_q(rng, 64, 24, 256)).cuda()
+    mask = synth.ancestor_masks(synth.make_tree_parents(rng, 64, 8))
+    kv = stv.KVCache.from_host(host)
+    a = stv.verify_attention(q, kv, 5000, mask)
+    b = stv.verify_attention(q, kv, 5000, mask)
+    c = stv.prefill_attention(q, kv, 5000)
+    d2 = stv.prefill_attention(q, kv, 5000)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b) and torch.equal(c, d2)
+
+
+def test_split_merge_parity(gpu, orc):
+    stv, torch = gpu
+    rng = np.random.default_rng(150)
+    for S, rows, d in ((1, 5, 64), (7, 33, 256), (64, 3, 128), (3, 10, 200)):
+        po = rng.standard_normal((S, rows, d)).astype(np.float32)
+        pl = (rng.standard_normal((S, rows)) * 5).astype(np.float32)
+        pl[rng.random((S, rows)) < 0.2] = -np.inf
+        pl[:, 0] = -np.inf                              # a row no split saw
+        out_ref, lse_ref = orc.merge(po.astype(np.float64), pl.astype(np.float64))
+        out_lse = torch.empty(rows, dtype=torch.float32, device="cuda")
+        out = stv.split_merge(torch.from_numpy(po).cuda(), torch.from_numpy(pl).cuda(),
+                              out_lse=out_lse)
+        torch.cuda.synchronize()
+        o = out.cpu().numpy()
+        ls = out_lse.cpu().numpy()
+        empty = ~np.isfinite(lse_ref)                   # rows no split saw
+        assert empty[0]
+        assert np.all(o[empty] == 0) and np.all(ls[empty] == -np.inf)
+        seen = ~empty
+        err = np.max(np.abs(o[seen] - out_ref[seen]), axis=-1) / np.max(np.abs(out_ref[seen]), axis=-1)
+        assert err.max() <= 1e-5
+        assert np.max(np.abs(ls[seen] - lse_ref[seen])) <= 1e-5 * np.max(np.abs(lse_ref[seen]) + 1)
+
+
+def test_kv_quant_pack_parity(gpu, orc):
+    stv, torch = gpu
+    rng = np.random.default_rng(160)
+    for hkv, d, cap, n, pos0 in ((4, 256, 300, 64, 17), (1, 64, 50, 7, 43), (2, 128, 4200, 4096, 100)):
+        x = (rng.standard_normal((n, hkv, d)) * 10.0 ** rng.uniform(-3, 3, (n, hkv, 1))).astype(np.float32)
+        x[0, 0, :32] = 0.0                         # zero block
+        x[min(1, n - 1), 0, 32:64] = 1e-9          # scale rounds to zero
+        x[n - 1, hkv - 1, :32] = 1e6               # scale saturates
+        codes = rng.integers(0, 2**32, size=(hkv, cap, d // 32, 3), dtype=np.uint32)
+        scales = rng.integers(0, 2**16, size=(hkv, cap, d // 32), dtype=np.uint16)
+        cd = torch.from_numpy(codes.view(np.int32)).cuda()
+        sd = torch.from_numpy(scales.view(np.float16)).cuda()
+        stv.kv_quant_pack(torch.from_numpy(x).cuda(), pos0, cd, sd)
+        torch.cuda.synchronize()
+        orc.kv_quant_pack(x, pos0, codes, scales)
+        assert np.array_equal(cd.cpu().numpy().view(np.uint32), codes)
+        assert np.array_equal(sd.cpu().numpy().view(np.uint16), scales)
+
+
+def test_pack_then_verify_end_to_end(gpu, orc):
+    """The new rows' K/V go through kv_quant_pack, then attention reads only
+    the cache: both sides run the same sequence."""
+    stv, torch = gpu
+    rng = np.random.default_rng(170)
+    hq, hkv, d, L, T = 24, 4, 256, 3000, 16
+    host = synth.make_kv(rng, hkv, d, L, L + T)
+    knew = rng.standard_normal((T, hkv, d)).astype(np.float32)
+    vnew = rng.standard_normal((T, hkv, d)).astype(np.float32)
+    q = synth.make_q(rng, T, hq, d)
+    mask = synth.ancestor_masks(synth.make_tree_parents(rng, T, 8))
+    kv = stv.KVCache.from_host(host)
+    stv.kv_quant_pack(torch.from_numpy(knew).cuda(), L, kv.k_codes, kv.k_scales)
+    stv.kv_quant_pack(torch.from_numpy(vnew).cuda(), L, kv.v_codes, kv.v_scales)
+    out = stv.verify_attention(torch.from_numpy(q).cuda(), kv, L, mask)
+    torch.cuda.synchronize()
+    orc.kv_quant_pack(knew, L, host.k_codes, host.k_scales)
+    orc.kv_quant_pack(vnew, L, host.v_codes, host.v_scales)
+    ref = orc.attention(q, host, L, mask)
+    err = _row_err(out.reshape(T * hq, d).cpu().numpy(), ref["out"])
+    assert err.max() <= TOL
+
+
+# Full-size workloads, in the launch configuration the benchmark times (the
+# automatic split plan), checked on rows the oracle computes one by one.
+FULL = [(g, r) for g, r in [(synth.CONFIGS[1], 24), (synth.CONFIGS[2], 8), (synth.CONFIGS[3], 6),
+                            (synth.CONFIGS[4], 6), (synth.EXTRA_CONFIGS[0], 6),
+                            (synth.EXTRA_CONFIGS[1], 6)]]
+
+
+@pytest.mark.parametrize("geom,n_rows", FULL, ids=[g.name for g, _ in FULL])
+def test_full_size_sampled(gpu, orc, geom, n_rows):
+    rng = np.random.default_rng(geom.seed)
+    host = synth.make_kv(rng, geom.n_kv_heads, geom.head_dim, geom.n_keys)
+    q = synth.make_q(rng, geom.n_rows, geom.n_q_heads, geom.head_dim)
+    kind = "prefill" if geom.kind == "prefill" else "tree"
+    mask = None
+    if kind == "tree":
+        mask = synth.ancestor_masks(synth.make_tree_parents(rng, geom.n_rows, geom.max_depth))
+    total = geom.n_rows * geom.n_q_heads
+    pick = np.random.default_rng(geom.seed + 100)
+    rows = np.unique(np.concatenate([[0, total - 1], pick.integers(0, total, n_rows - 2)]))
+    run_case(gpu, orc, geom.n_q_heads, geom.n_kv_heads, geom.head_dim, geom.ctx_len,
+             geom.n_rows, kind, geom.seed, host=host, q=q, mask=mask, rows=rows,
+             check_logits=geom.n_keys * geom.n_rows <= 64 * 40000)
+
+
+def test_partials_then_merge_equals_verify(gpu, orc):
+    """The split phase plus the merge entry point reproduce the verify call
+    bit for bit (the verify call runs exactly these two kernels)."""
+    stv, torch = gpu
+    rng = np.random.default_rng(180)
+    hq, hkv, d, L, T = 24, 4, 256, 9000, 12
+    host = synth.make_kv(rng, hkv, d, L + T)
+    q = torch.from_numpy(synth.make_q(rng, T, hq, d)).cuda()
+    mask = synth.ancestor_masks(synth.make_tree_parents(rng, T, 8))
+    kv = stv.KVCache.from_host(host)
+    lse = torch.empty((T, hq), dtype=torch.float32, device="cuda")
+    out = stv.verify_attention(q, kv, L, mask, out_lse=lse)
+    po, pl = stv.attention_partials(q, kv, L, mask)
+    S = po.shape[0]
+    assert S > 1
+    lse2 = torch.empty(T * hq, dtype=torch.float32, device="cuda")
+    out2 = stv.split_merge(po.reshape(S, T * hq, d), pl.reshape(S, T * hq), out_lse=lse2)
+    torch.cuda.synchronize()
+    assert torch.equal(out.reshape(T * hq, d), out2)
+    assert torch.equal(lse.reshape(-1), lse2)
+    # the partials themselves match the oracle's partials over the same key ranges
+    n_keys = L + T
+    split_len = 32 * -(-(-(-n_keys // 32)) // S)        # 32 * ceil(ceil(N / 32) / S)
+    qh = q.cpu().numpy()
+    for s in (0, S // 2, S - 1):
+        k0, k1 = s * split_len, min(n_keys, (s + 1) * split_len)
+        ref = orc.attention(qh, host, L, mask, k_begin=k0, k_end=k1, rows=[0, 7, T * hq - 1])
+        got = po[s].reshape(T * hq, d)[[0, 7, T * hq - 1]].cpu().numpy()
+        assert _row_err(got, ref["out"]).max() <= TOL
+        gl = pl[s].reshape(-1)[[0, 7, T * hq - 1]].cpu().numpy()
+        assert np.max(np.abs(gl - ref["lse"])) <= TOL
