@@ -12,7 +12,10 @@ SOURCES = [os.path.join(HERE, "csrc", "stv_kernels.hip"), os.path.join(HERE, "cs
 ARCH = "gfx950"
 
 # Packed fp32 VALU forms stay off: float code is compiled to scalar-lane ops.
-HIP_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+HIP_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             # MFMA accumulators live in VGPRs, so the VALU softmax rescale needs no
+             # AGPR round trips
+             "-mllvm", "-amdgpu-mfma-vgpr-form"]
 
 
 def build(verbose: bool = False) -> str:

@@ -121,19 +121,151 @@ __global__ void kv_pack_kernel(const float *__restrict__ x, int n_tok, int pos0,
 
 // ------------------------------------------------------------ attention
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// LDS layout of one 32-key tile.
+//   kq : int8 K, [32 keys][D + 16] bytes (row pad keeps the A-operand reads
+//        of 16 consecutive lanes on distinct banks)
+//   vt : fp16 V^T, element (d, key) at d*VTS + (d/32)*VBPAD + key halves.
+//        VTS = 40 keeps the B128 operand reads conflict-free; the per-block
+//        pad of 16 dwords spreads the four blocks written by one wave over
+//        all 64 banks.
+//   skf: fp32 K scales, [D/32][32 keys]
+template <int D>
+struct TileLds {
+    static constexpr int NB = D / 32;
+    static constexpr int KQS = D + 16;
+    static constexpr int VTS = kKeyTile + 8;
+    static constexpr int VBPAD = 32;
+    int8_t kq[kKeyTile * KQS];
+    _Float16 vt[D * VTS + NB * VBPAD];
+    float skf[NB * kKeyTile];
+};
+
+// One (key, block) item of the K side: 3 code words and the fp16 scale.
+struct KItem {
+    uint32_t w[3];
+    uint16_t s;
+};
+// One (key pair, block, element half) item of the V side: 3 code words of
+// each key and both scales.
+struct VItem {
+    uint32_t w0[3], w1[3];
+    uint16_t s0, s1;
+};
+
+template <int D, int NT>
+struct TileIo {
+    static constexpr int NB = D / 32;
+    static constexpr int KI = kKeyTile * NB;           // K items per tile
+    static constexpr int VI = (kKeyTile / 2) * NB * 2;  // V items per tile
+    static constexpr int KPT = (KI + NT - 1) / NT;
+    static constexpr int VPT = (VI + NT - 1) / NT;
+    KItem k[KPT];
+    VItem v[VPT];
+
+    __device__ __forceinline__ void load(const AttnArgs &a, size_t head_base, int kb, int k1,
+                                         int tid) {
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) {
+            const int item = tid + i * NT;
+            const int kk = item / NB, b = item % NB;
+            const int key = kb + kk;
+            k[i].w[0] = k[i].w[1] = k[i].w[2] = 0u;
+            k[i].s = 0;
+            if (item < KI && key < k1) {
+                const size_t blk = (head_base + key) * NB + b;
+                const uint32_t *src = a.kc + blk * 3;
+                k[i].w[0] = src[0];
+                k[i].w[1] = src[1];
+                k[i].w[2] = src[2];
+                k[i].s = a.ks[blk];
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) {
+            const int item = tid + i * NT;
+            const int m = item % 16, b = (item / 16) % NB;
+            const int key = kb + 2 * m;
+            VItem &it = v[i];
+            it.w0[0] = it.w0[1] = it.w0[2] = 0u;
+            it.w1[0] = it.w1[1] = it.w1[2] = 0u;
+            it.s0 = it.s1 = 0;
+            if (item < VI && key < k1) {
+                const size_t blk = (head_base + key) * NB + b;
+                const uint32_t *src = a.vc + blk * 3;
+                it.w0[0] = src[0];
+                it.w0[1] = src[1];
+                it.w0[2] = src[2];
+                it.s0 = a.vs[blk];
+                if (key + 1 < k1) {
+                    it.w1[0] = src[3 * NB + 0];
+                    it.w1[1] = src[3 * NB + 1];
+                    it.w1[2] = src[3 * NB + 2];
+                    it.s1 = a.vs[blk + NB];
+                }
+            }
+        }
+    }
+
+    __device__ __forceinline__ void store(TileLds<D> &t, int tid) const {
+        using L = TileLds<D>;
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) {
+            const int item = tid + i * NT;
+            if (item < KI) {
+                const int kk = item / NB, b = item % NB;
+                uint32_t o[8];
+                unpack_bytes(k[i].w[0], k[i].w[1], k[i].w[2], o);
+                const u32x4 lo = {codes_to_i8(o[0]), codes_to_i8(o[1]), codes_to_i8(o[2]),
+                                  codes_to_i8(o[3])};
+                const u32x4 hi = {codes_to_i8(o[4]), codes_to_i8(o[5]), codes_to_i8(o[6]),
+                                  codes_to_i8(o[7])};
+                *reinterpret_cast<u32x4 *>(t.kq + kk * L::KQS + 32 * b) = lo;
+                *reinterpret_cast<u32x4 *>(t.kq + kk * L::KQS + 32 * b + 16) = hi;
+                t.skf[b * kKeyTile + kk] = half_bits_to_float(k[i].s);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) {
+            const int item = tid + i * NT;
+            if (item < VI) {
+                const int m = item % 16, b = (item / 16) % NB, h = item / (16 * NB);
+                const VItem &it = v[i];
+                uint32_t oa[8], ob[8];
+                unpack_bytes(it.w0[0], it.w0[1], it.w0[2], oa);
+                unpack_bytes(it.w1[0], it.w1[1], it.w1[2], ob);
+                const f16x2 svp = {__builtin_bit_cast(_Float16, it.s0),
+                                   __builtin_bit_cast(_Float16, it.s1)};
+                const f16x2 off = {(_Float16)1028.0f, (_Float16)1028.0f};
+                uint32_t *vt32 = reinterpret_cast<uint32_t *>(t.vt);
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const uint32_t wa = h ? oa[4 + q4] : oa[q4];
+                    const uint32_t wb = h ? ob[4 + q4] : ob[q4];
+#pragma unroll
+                    for (int i2 = 0; i2 < 4; ++i2) {
+                        // (key 2m, key 2m+1) codes of element e into the two
+                        // halves; 0x6400 | c is the binary16 value 1024 + c.
+                        const uint32_t bits = ((wa >> (8 * i2)) & 0xFFu) |
+                                              (((wb >> (8 * i2)) & 0xFFu) << 16) | 0x64006400u;
+                        const f16x2 val = (__builtin_bit_cast(f16x2, bits) - off) * svp;
+                        const int d = 32 * b + 16 * h + 4 * q4 + i2;
+                        vt32[(d * L::VTS + b * L::VBPAD) / 2 + m] = __builtin_bit_cast(uint32_t, val);
+                    }
+                }
+            }
+        }
+    }
+};
+
 template <int D, int NW, bool CAUSAL, bool DEBUG>
 __global__ __launch_bounds__(NW * 64) void attn_split_kernel(const AttnArgs a) {
     constexpr int NB = D / 32;
     constexpr int KT = kKeyTile;
-    constexpr int KQS = D + 16;           // bytes per key row of the int8 K tile
-    constexpr int VTS = KT + 8;           // halves per d row of the V^T tile
-    constexpr int PAIRS = KT * NB;        // (key, block) pairs per tile
     constexpr int NT = NW * 64;
-    constexpr int PPT = (PAIRS + NT - 1) / NT;
-
-    __shared__ __attribute__((aligned(16))) int8_t kq[KT * KQS];
-    __shared__ __attribute__((aligned(16))) _Float16 vt[D * VTS];
-    __shared__ __attribute__((aligned(16))) float skf[NB * KT];
+    using L = TileLds<D>;
+    __shared__ __attribute__((aligned(16))) L lds;
 
     // ---- work-group -> (kv head, split, row group).  Row groups of one
     // (head, split) get ids 8 apart so they share an XCD and its L2.
@@ -160,7 +292,7 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(const AttnArgs a) {
     const bool wave_active = (rg * NW + wave) * kRowTile < a.R;
 
     // ---- key range of this work-group
-    int k0 = split * a.split_len;
+    const int k0 = split * a.split_len;
     int k1 = min(a.N, k0 + a.split_len);
     if (CAUSAL) {
         const int rho_last = min(a.R, (rg + 1) * NW * kRowTile) - 1;
@@ -231,102 +363,42 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(const AttnArgs a) {
     // are exactly the key runs the P.V MFMA wants from that lane.
     const int ai = l32 >> 3;
     const int krow = 16 * (ai >> 1) + 8 * ((l32 >> 2) & 1) + 4 * (ai & 1) + (l32 & 3);
+    const int8_t *kq_lane = lds.kq + krow * L::KQS + 16 * hl;
+    const _Float16 *vt_lane = lds.vt + l32 * L::VTS + 8 * hl;
 
     f32x16 oacc[NB];
 #pragma unroll
     for (int dt = 0; dt < NB; ++dt) oacc[dt] = f32x16{};
+    // Running max in base-2 logit units.  It only moves when a tile's max
+    // exceeds it by more than 8 (so exp2 stays below 256, well inside fp16),
+    // which makes rescaling the accumulators rare.
     float m_run = -INFINITY;
     float l_run = 0.0f;
 
     const size_t head_base = (size_t)head * a.cap;
-
-    // ---- register prefetch of one tile
-    uint32_t rk[PPT][3], rv[PPT][3];
-    uint16_t rks[PPT], rvs[PPT];
-    auto load_tile = [&](int kb) {
-#pragma unroll
-        for (int i = 0; i < PPT; ++i) {
-            const int p = tid + i * NT;
-            const int key = kb + p / NB;
-            const int b = p % NB;
-            rk[i][0] = rk[i][1] = rk[i][2] = 0u;
-            rv[i][0] = rv[i][1] = rv[i][2] = 0u;
-            rks[i] = 0;
-            rvs[i] = 0;
-            if (p < PAIRS && key < k1) {
-                const size_t blk = (head_base + key) * NB + b;
-                const uint32_t *kw = a.kc + blk * 3;
-                const uint32_t *vw = a.vc + blk * 3;
-                rk[i][0] = kw[0];
-                rk[i][1] = kw[1];
-                rk[i][2] = kw[2];
-                rv[i][0] = vw[0];
-                rv[i][1] = vw[1];
-                rv[i][2] = vw[2];
-                rks[i] = a.ks[blk];
-                rvs[i] = a.vs[blk];
-            }
-        }
-    };
-
-    if (k0 < k1) load_tile(k0);
+    TileIo<D, NT> io;
+    if (k0 < k1) io.load(a, head_base, k0, k1, tid);
 
     for (int kb = k0; kb < k1; kb += KT) {
-        // ---- unpack the tile held in registers into LDS
-#pragma unroll
-        for (int i = 0; i < PPT; ++i) {
-            const int p = tid + i * NT;
-            if (p < PAIRS) {
-                const int kk = p / NB;
-                const int b = p % NB;
-                uint32_t o[8];
-                unpack_bytes(rk[i][0], rk[i][1], rk[i][2], o);
-                u32x4 lo = {codes_to_i8(o[0]), codes_to_i8(o[1]), codes_to_i8(o[2]),
-                            codes_to_i8(o[3])};
-                u32x4 hi = {codes_to_i8(o[4]), codes_to_i8(o[5]), codes_to_i8(o[6]),
-                            codes_to_i8(o[7])};
-                *reinterpret_cast<u32x4 *>(kq + kk * KQS + 32 * b) = lo;
-                *reinterpret_cast<u32x4 *>(kq + kk * KQS + 32 * b + 16) = hi;
-                skf[b * KT + kk] = half_bits_to_float(rks[i]);
-
-                unpack_bytes(rv[i][0], rv[i][1], rv[i][2], o);
-                const _Float16 sv = __builtin_bit_cast(_Float16, rvs[i]);
-                const f16x2 svp = {sv, sv};
-                const f16x2 off = {(_Float16)1028.0f, (_Float16)1028.0f};
-#pragma unroll
-                for (int qq = 0; qq < 8; ++qq) {
-                    // 0x6400 | c is the binary16 value 1024 + c; minus 1028 is c - 4.
-                    const uint32_t lo_bits = (o[qq] & 0x00070007u) | 0x64006400u;
-                    const uint32_t hi_bits = ((o[qq] >> 8) & 0x00070007u) | 0x64006400u;
-                    const f16x2 vlo = (__builtin_bit_cast(f16x2, lo_bits) - off) * svp;
-                    const f16x2 vhi = (__builtin_bit_cast(f16x2, hi_bits) - off) * svp;
-                    _Float16 *col = vt + (32 * b + 4 * qq) * VTS + kk;
-                    col[0 * VTS] = vlo.x;
-                    col[2 * VTS] = vlo.y;
-                    col[1 * VTS] = vhi.x;
-                    col[3 * VTS] = vhi.y;
-                }
-            }
-        }
+        io.store(lds, tid);
         __syncthreads();
-
-        if (kb + KT < k1) load_tile(kb + KT);
+        if (kb + KT < k1) io.load(a, head_base, kb + KT, k1, tid);
 
         if (wave_active) {
             // ---- Q.K^T: one int8 MFMA per 32-element block, fp32 epilogue
             f32x16 acc = f32x16{};
 #pragma unroll
             for (int b = 0; b < NB; ++b) {
-                const i32x4 kop = *reinterpret_cast<const i32x4 *>(kq + krow * KQS + 32 * b + 16 * hl);
+                const i32x4 kop = *reinterpret_cast<const i32x4 *>(kq_lane + 32 * b);
                 const i32x16 s = __builtin_amdgcn_mfma_i32_32x32x32_i8(kop, qreg[b], i32x16{}, 0, 0, 0);
-                const f32x4 s0 = *reinterpret_cast<const f32x4 *>(skf + b * KT + 8 * hl);
-                const f32x4 s1 = *reinterpret_cast<const f32x4 *>(skf + b * KT + 8 * hl + 4);
-                const f32x4 s2 = *reinterpret_cast<const f32x4 *>(skf + b * KT + 16 + 8 * hl);
-                const f32x4 s3 = *reinterpret_cast<const f32x4 *>(skf + b * KT + 16 + 8 * hl + 4);
+                const f32x4 s0 = *reinterpret_cast<const f32x4 *>(lds.skf + b * KT + 8 * hl);
+                const f32x4 s1 = *reinterpret_cast<const f32x4 *>(lds.skf + b * KT + 8 * hl + 4);
+                const f32x4 s2 = *reinterpret_cast<const f32x4 *>(lds.skf + b * KT + 16 + 8 * hl);
+                const f32x4 s3 = *reinterpret_cast<const f32x4 *>(lds.skf + b * KT + 16 + 8 * hl + 4);
                 const float skr[16] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w,
                                        s2.x, s2.y, s2.z, s2.w, s3.x, s3.y, s3.z, s3.w};
 #pragma unroll
-                for (int r = 0; r < 16; ++r) acc[r] += skr[r] * (float)s[r];
+                for (int r = 0; r < 16; ++r) acc[r] = fmaf(skr[r], (float)s[r], acc[r]);
                 if (DEBUG && a.dbg_logits && row_ok) {
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
@@ -357,41 +429,41 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(const AttnArgs a) {
 #pragma unroll
             for (int r = 1; r < 16; ++r) tmax = fmaxf(tmax, y[r]);
             tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-            const float m_new = fmaxf(m_run, tmax);
-            float alpha = 1.0f;
-            float p[16];
-            if (m_new == -INFINITY) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) p[r] = 0.0f;
-            } else {
-                alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-#pragma unroll
-                for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(y[r] - m_new);
-            }
-            float psum = 0.0f;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) psum += p[r];
-            l_run = l_run * alpha + psum;
-            if (__any(alpha != 1.0f)) {
+            const float m_new = tmax > m_run + 8.0f ? tmax : m_run;
+            if (__any(m_new != m_run)) {
+                const float alpha = m_new != m_run ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+                l_run *= alpha;
 #pragma unroll
                 for (int dt = 0; dt < NB; ++dt)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+                m_run = m_new;
             }
-            m_run = m_new;
+            const float mm = m_run == -INFINITY ? 0.0f : m_run;
+            float p[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(y[r] - mm);
+            float psum = 0.0f;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) psum += p[r];
+            l_run += psum;
 
             // ---- P.V: B operand = P (lane = row, 8 keys), A operand = V^T rows
             f16x8 pk[2];
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-                for (int e = 0; e < 8; ++e) pk[ks][e] = (_Float16)p[8 * ks + e];
+                for (int e = 0; e < 8; e += 2) {
+                    const f16x2 h2 = __builtin_convertvector(f32x2{p[8 * ks + e], p[8 * ks + e + 1]}, f16x2);
+                    pk[ks][e] = h2.x;
+                    pk[ks][e + 1] = h2.y;
+                }
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
                 for (int dt = 0; dt < NB; ++dt) {
                     const f16x8 vop = *reinterpret_cast<const f16x8 *>(
-                        vt + (dt * 32 + l32) * VTS + 16 * ks + 8 * hl);
+                        vt_lane + (dt * 32) * L::VTS + dt * L::VBPAD + 16 * ks);
                     oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vop, pk[ks], oacc[dt], 0, 0, 0);
                 }
             }
@@ -428,27 +500,104 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(const AttnArgs a) {
 
 // ---------------------------------------------------------------- merge
 
-__global__ void merge_kernel(const float *__restrict__ part_o, const float *__restrict__ part_lse,
-                             int S, int rows, int D, float *__restrict__ out,
-                             float *__restrict__ out_lse) {
+// One work-group per output row.  The weights exp(lse_s - M) come from a
+// block-wide max and sum; then thread (g, c) accumulates element c over the
+// splits s = g, g + G, ... and the G partial sums are added in order g = 0, 1,
+// ... through LDS, so the result does not depend on timing.
+constexpr int kMergeThreads = 256;
+
+__device__ __forceinline__ float block_reduce(float v, float *red, bool is_max) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const float w = __shfl_xor(v, o);
+        v = is_max ? fmaxf(v, w) : v + w;
+    }
+    __syncthreads();
+    if (lane == 0) red[wave] = v;
+    __syncthreads();
+    v = red[0];
+    for (int i = 1; i < kMergeThreads / 64; ++i) v = is_max ? fmaxf(v, red[i]) : v + red[i];
+    return v;
+}
+
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(
+    const float *__restrict__ part_o, const float *__restrict__ part_lse, int S, int rows, int D,
+    float *__restrict__ out, float *__restrict__ out_lse) {
+    __shared__ float red[kMergeThreads / 64];
+    __shared__ float wgt[1024];
+    __shared__ float acc_lds[kMergeThreads * 4];
     const int row = blockIdx.x;
+    const int tid = threadIdx.x;
     float M = -INFINITY;
-    for (int s = 0; s < S; ++s) M = fmaxf(M, part_lse[(size_t)s * rows + row]);
+    for (int s = tid; s < S; s += kMergeThreads) M = fmaxf(M, part_lse[(size_t)s * rows + row]);
+    M = block_reduce(M, red, true);
     float W = 0.0f;
     if (M != -INFINITY)
-        for (int s = 0; s < S; ++s) W += expf(part_lse[(size_t)s * rows + row] - M);
+        for (int s = tid; s < S; s += kMergeThreads) {
+            const float ls = part_lse[(size_t)s * rows + row];
+            const float w = ls == -INFINITY ? 0.0f : expf(ls - M);
+            W += w;
+            if (s < 1024) wgt[s] = w;
+        }
+    W = block_reduce(W, red, false);
     const float invW = W > 0.0f ? 1.0f / W : 0.0f;
-    for (int d = threadIdx.x; d < D; d += blockDim.x) {
-        float o = 0.0f;
-        if (M != -INFINITY)
+    if (out_lse && tid == 0) out_lse[row] = M == -INFINITY ? -INFINITY : M + logf(W);
+
+    const bool vec = (D & 3) == 0 && D <= 4 * kMergeThreads;
+    const int C = vec ? D / 4 : D;                     // columns (float4 or float)
+    const int G = vec ? kMergeThreads / C : 1;         // split groups
+    const int g = tid / C, c = tid - (tid / C) * C;
+    __syncthreads();
+    if (M == -INFINITY) {
+        for (int d = tid; d < D; d += kMergeThreads) out[(size_t)row * D + d] = 0.0f;
+        return;
+    }
+    if (vec) {
+        f32x4 o = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (g < G) {
+            for (int s = g; s < S; s += G) {
+                const float w = s < 1024 ? wgt[s]
+                                         : (part_lse[(size_t)s * rows + row] == -INFINITY
+                                                ? 0.0f
+                                                : expf(part_lse[(size_t)s * rows + row] - M));
+                if (w != 0.0f) {
+                    const f32x4 v = *reinterpret_cast<const f32x4 *>(
+                        part_o + ((size_t)s * rows + row) * D + 4 * c);
+                    o.x += w * v.x;
+                    o.y += w * v.y;
+                    o.z += w * v.z;
+                    o.w += w * v.w;
+                }
+            }
+            *reinterpret_cast<f32x4 *>(acc_lds + 4 * tid) = o;
+        }
+        __syncthreads();
+        if (g == 0) {
+            f32x4 sum = *reinterpret_cast<const f32x4 *>(acc_lds + 4 * c);
+            for (int k = 1; k < G; ++k) {
+                const f32x4 v = *reinterpret_cast<const f32x4 *>(acc_lds + 4 * (k * C + c));
+                sum.x += v.x;
+                sum.y += v.y;
+                sum.z += v.z;
+                sum.w += v.w;
+            }
+            sum.x *= invW;
+            sum.y *= invW;
+            sum.z *= invW;
+            sum.w *= invW;
+            *reinterpret_cast<f32x4 *>(out + (size_t)row * D + 4 * c) = sum;
+        }
+    } else {
+        for (int d = tid; d < D; d += kMergeThreads) {
+            float o = 0.0f;
             for (int s = 0; s < S; ++s) {
                 const float ls = part_lse[(size_t)s * rows + row];
-                if (ls != -INFINITY)
-                    o += expf(ls - M) * part_o[((size_t)s * rows + row) * D + d];
+                if (ls != -INFINITY) o += expf(ls - M) * part_o[((size_t)s * rows + row) * D + d];
             }
-        out[(size_t)row * D + d] = o * invW;
+            out[(size_t)row * D + d] = o * invW;
+        }
     }
-    if (out_lse && threadIdx.x == 0) out_lse[row] = M == -INFINITY ? -INFINITY : M + logf(W);
 }
 
 template <int D, int NW, bool CAUSAL, bool DEBUG>
@@ -490,9 +639,8 @@ hipError_t launch_attention(const AttnArgs &a, int D, int NW, bool causal, bool 
 hipError_t launch_merge(const float *part_o, const float *part_lse, int S, int rows, int D,
                         float *out, float *out_lse, hipStream_t stream) {
     if (rows == 0) return hipSuccess;
-    const int threads = D >= 256 ? 256 : ((D + 63) / 64) * 64;
-    hipLaunchKernelGGL(merge_kernel, dim3(rows), dim3(threads), 0, stream, part_o, part_lse, S,
-                       rows, D, out, out_lse);
+    hipLaunchKernelGGL(merge_kernel, dim3(rows), dim3(kMergeThreads), 0, stream, part_o, part_lse,
+                       S, rows, D, out, out_lse);
     return hipGetLastError();
 }
 
