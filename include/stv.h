@@ -121,7 +121,7 @@ int stv_attention_plan(int32_t T, int32_t n_q_heads, int32_t n_kv_heads, int32_t
  *               bit and no bit above it, and the rest of its bits must be
  *               exactly the mask of its highest other row (its parent), so
  *               the rows form a forest and each row sees a root-to-node path
- *   softmax_scale  multiplies the logits (commonly 1/sqrt(head_dim))
+ *   softmax_scale  positive, multiplies the logits (commonly 1/sqrt(head_dim))
  *   out         fp32 [T][n_q_heads][head_dim]
  *   out_lse     nullable fp32 [T][n_q_heads]: natural-log log-sum-exp of each
  *               row's scaled logits, for merging with results over other

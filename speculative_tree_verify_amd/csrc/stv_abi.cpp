@@ -7,6 +7,9 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+#include <vector>
+
 #include "stv_internal.h"
 
 namespace {
@@ -79,7 +82,7 @@ int attention_common(const float *q, int T, int Hq, const stv_kv_layer *kv, int 
     if (!causal && T > STV_MAX_TREE_ROWS) return fail(STV_EINVAL, "verify supports at most 64 tree rows (got %d)", T);
     if ((long long)T * Hq >= (1ll << 31)) return fail(STV_EINVAL, "T * n_q_heads too large");
     if (n_splits < 0) return fail(STV_EINVAL, "n_splits must be >= 0");
-    if (!isfinite(scale)) return fail(STV_EINVAL, "softmax_scale must be finite");
+    if (!(scale > 0.0f) || !isfinite(scale)) return fail(STV_EINVAL, "softmax_scale must be positive and finite");
     int rc = check_kv(kv, Hq, L, T);
     if (rc) return rc;
     if (!causal) {
@@ -146,6 +149,36 @@ int attention_common(const float *q, int T, int Hq, const stv_kv_layer *kv, int 
 
 namespace stv {
 
+long long attention_slots(int D, int NW, bool causal) {
+    // MI355X: 256 CUs; the D = 256 four-wave kernel holds two work-groups per CU.
+    constexpr long long kFallback = 256LL * 2;
+    struct Entry {
+        int dev, D, NW;
+        bool causal;
+        long long slots;
+    };
+    static std::mutex mu;
+    static std::vector<Entry> cache;
+    int dev = 0, count = 0;
+    if (hipGetDeviceCount(&count) != hipSuccess || count <= 0 || hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return kFallback;
+    }
+    std::lock_guard<std::mutex> lock(mu);
+    for (const Entry &e : cache)
+        if (e.dev == dev && e.D == D && e.NW == NW && e.causal == causal) return e.slots;
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0) {
+        (void)hipGetLastError();
+        return kFallback;
+    }
+    const int per_cu = attention_wgs_per_cu(D, NW, causal);
+    const long long slots = per_cu > 0 ? (long long)cus * per_cu : kFallback;
+    cache.push_back({dev, D, NW, causal, slots});
+    return slots;
+}
+
 Plan make_plan(int T, int Hq, int Hkv, int D, int L, bool causal, int n_splits_req) {
     Plan p;
     const int G = Hq / Hkv;
@@ -159,14 +192,14 @@ Plan make_plan(int T, int Hq, int Hkv, int D, int L, bool causal, int n_splits_r
     if (n_splits_req > 0) {
         S = n_splits_req;
     } else {
-        // Aim for about two resident work-groups per CU on 256 CUs, with
-        // at least four tiles per split.
-        const long long target = 256LL * (8 / p.NW);
+        // Fill the device's resident work-group slots exactly once: one
+        // round of equal work-groups, no straggling partial round.  Splits
+        // keep at least four tiles.
+        const long long slots = attention_slots(D, p.NW, causal);
         const long long groups = (long long)Hkv * p.NRG;
-        S = (target + groups - 1) / groups;
+        S = groups >= slots ? 1 : slots / groups;
         const long long max_s = n_tiles / 4 > 0 ? n_tiles / 4 : 1;
         if (S > max_s) S = max_s;
-        if (causal && groups >= 512) S = 1;
     }
     if (S < 1) S = 1;
     if (S > n_tiles) S = n_tiles > 0 ? n_tiles : 1;

@@ -41,6 +41,14 @@ struct Plan {
     size_t ws_bytes; // workspace for the partials
 };
 
+// Work-groups of the attention kernel that fit on one CU at once, from the
+// runtime's occupancy calculator; 0 when no device answers.
+int attention_wgs_per_cu(int D, int NW, bool causal);
+
+// Resident work-group slots of the current device for that kernel variant
+// (CUs x work-groups per CU); a fixed MI355X figure when no device answers.
+long long attention_slots(int D, int NW, bool causal);
+
 Plan make_plan(int T, int Hq, int Hkv, int D, int L, bool causal, int n_splits_req);
 
 // Launchers return the hipError_t of the launch.

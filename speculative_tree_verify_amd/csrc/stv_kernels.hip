@@ -266,6 +266,10 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(const AttnArgs a) {
     constexpr int NT = NW * 64;
     using L = TileLds<D>;
     __shared__ __attribute__((aligned(16))) L lds;
+    // int8 Q of each wave's 32 rows, [NW][32 rows][D + 16] bytes: read back as
+    // the B operand of every Q.K^T MFMA, which keeps 32 VGPRs free for
+    // double-buffering the MFMA results.
+    __shared__ __attribute__((aligned(16))) int8_t qlds[NW * kRowTile * L::KQS];
 
     // ---- work-group -> (kv head, split, row group).  Row groups of one
     // (head, split) get ids 8 apart so they share an XCD and its L2.
@@ -303,9 +307,10 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(const AttnArgs a) {
     // ---- prologue: per-row int8 quantization of Q.  Lane (l32, hl) holds
     // row l32 of the wave and elements 32b + 16hl + [0, 16) of every block b:
     // the B operand layout of the 32x32x32 int8 MFMA.
-    i32x4 qreg[NB];
     float sq = 0.0f;
+    int8_t *q_lane = qlds + (wave * kRowTile + l32) * L::KQS + 16 * hl;
     {
+        i32x4 qreg[NB];
         const float *qrow = a.q + (size_t)flat * D + 16 * hl;
         float amax = 0.0f;
         if (row_ok) {
@@ -339,6 +344,8 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(const AttnArgs a) {
                 qreg[b][j] = (int32_t)word;
             }
         }
+#pragma unroll
+        for (int b = 0; b < NB; ++b) *reinterpret_cast<i32x4 *>(q_lane + 32 * b) = qreg[b];
         if (DEBUG && split == 0 && row_ok) {
             if (a.dbg_q) {
 #pragma unroll
@@ -385,12 +392,20 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(const AttnArgs a) {
         if (kb + KT < k1) io.load(a, head_base, kb + KT, k1, tid);
 
         if (wave_active) {
-            // ---- Q.K^T: one int8 MFMA per 32-element block, fp32 epilogue
+            // ---- Q.K^T: one int8 MFMA per 32-element block, fp32 epilogue.
+            // The MFMA of block b + 1 is issued before the epilogue of block b
+            // reads its results, so the matrix unit and the VALU overlap.
             f32x16 acc = f32x16{};
+            i32x16 s_cur = __builtin_amdgcn_mfma_i32_32x32x32_i8(
+                *reinterpret_cast<const i32x4 *>(kq_lane),
+                *reinterpret_cast<const i32x4 *>(q_lane), i32x16{}, 0, 0, 0);
 #pragma unroll
             for (int b = 0; b < NB; ++b) {
-                const i32x4 kop = *reinterpret_cast<const i32x4 *>(kq_lane + 32 * b);
-                const i32x16 s = __builtin_amdgcn_mfma_i32_32x32x32_i8(kop, qreg[b], i32x16{}, 0, 0, 0);
+                i32x16 s_next;
+                if (b + 1 < NB)
+                    s_next = __builtin_amdgcn_mfma_i32_32x32x32_i8(
+                        *reinterpret_cast<const i32x4 *>(kq_lane + 32 * (b + 1)),
+                        *reinterpret_cast<const i32x4 *>(q_lane + 32 * (b + 1)), i32x16{}, 0, 0, 0);
                 const f32x4 s0 = *reinterpret_cast<const f32x4 *>(lds.skf + b * KT + 8 * hl);
                 const f32x4 s1 = *reinterpret_cast<const f32x4 *>(lds.skf + b * KT + 8 * hl + 4);
                 const f32x4 s2 = *reinterpret_cast<const f32x4 *>(lds.skf + b * KT + 16 + 8 * hl);
@@ -398,22 +413,22 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(const AttnArgs a) {
                 const float skr[16] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w,
                                        s2.x, s2.y, s2.z, s2.w, s3.x, s3.y, s3.z, s3.w};
 #pragma unroll
-                for (int r = 0; r < 16; ++r) acc[r] = fmaf(skr[r], (float)s[r], acc[r]);
+                for (int r = 0; r < 16; ++r) acc[r] = fmaf(skr[r], (float)s_cur[r], acc[r]);
                 if (DEBUG && a.dbg_logits && row_ok) {
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const int key = kb + (r < 8 ? 8 * hl + r : 16 + 8 * hl + (r - 8));
                         if (key < k1)
-                            a.dbg_logits[((size_t)flat * a.N + key) * NB + b] = s[r];
+                            a.dbg_logits[((size_t)flat * a.N + key) * NB + b] = s_cur[r];
                     }
                 }
+                if (b + 1 < NB) s_cur = s_next;
             }
 
-            // ---- scale, mask, online softmax in base 2
-            float y[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) y[r] = acc[r] * c_row;
-            if (kb + KT > vis_from) {
+            // ---- mask, online softmax in base 2.  c_row >= 0, so the row max
+            // of the scaled logits is c_row times the max of acc.
+            const bool masked = kb + KT > vis_from;
+            if (masked) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int key = kb + (r < 8 ? 8 * hl + r : 16 + 8 * hl + (r - 8));
@@ -422,13 +437,15 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(const AttnArgs a) {
                         const int u = key - a.L;
                         vis = CAUSAL ? (u <= t) : (((mrow >> u) & 1ull) != 0ull);
                     }
-                    if (!vis) y[r] = -INFINITY;
+                    if (!vis) acc[r] = -INFINITY;
                 }
             }
-            float tmax = y[0];
+            float amax = acc[0];
 #pragma unroll
-            for (int r = 1; r < 16; ++r) tmax = fmaxf(tmax, y[r]);
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+            for (int r = 1; r < 16; ++r) amax = fmaxf(amax, acc[r]);
+            amax = fmaxf(amax, __shfl_xor(amax, 32));
+            // a row with c_row == 0 has all visible logits 0
+            const float tmax = amax == -INFINITY ? -INFINITY : amax * c_row;
             const float m_new = tmax > m_run + 8.0f ? tmax : m_run;
             if (__any(m_new != m_run)) {
                 const float alpha = m_new != m_run ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
@@ -441,15 +458,19 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(const AttnArgs a) {
             }
             const float mm = m_run == -INFINITY ? 0.0f : m_run;
             float p[16];
+            if (masked) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(y[r] - mm);
-            float psum = 0.0f;
+                for (int r = 0; r < 16; ++r)
+                    p[r] = acc[r] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(fmaf(acc[r], c_row, -mm));
+            } else {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) psum += p[r];
-            l_run += psum;
-
-            // ---- P.V: B operand = P (lane = row, 8 keys), A operand = V^T rows
+                for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(fmaf(acc[r], c_row, -mm));
+            }
+            // ---- P.V: B operand = P (lane = row, 8 keys), A operand = V^T rows.
+            // The row sum adds the same fp16 values the MFMA multiplies.
             f16x8 pk[2];
+            float psum = 0.0f;
+            const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
@@ -457,7 +478,9 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(const AttnArgs a) {
                     const f16x2 h2 = __builtin_convertvector(f32x2{p[8 * ks + e], p[8 * ks + e + 1]}, f16x2);
                     pk[ks][e] = h2.x;
                     pk[ks][e + 1] = h2.y;
+                    psum = __builtin_amdgcn_fdot2(h2, ones, psum, false);
                 }
+            l_run += psum;
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
@@ -624,7 +647,36 @@ hipError_t launch_nw(const AttnArgs &a, int NW, bool causal, bool debug, hipStre
     }
 }
 
+template <int D, int NW, bool CAUSAL>
+int occupancy_t() {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &n, reinterpret_cast<const void *>(&attn_split_kernel<D, NW, CAUSAL, false>), NW * 64,
+            0) != hipSuccess)
+        return 0;
+    return n;
+}
+
+template <int D>
+int occupancy_d(int NW, bool causal) {
+    switch (NW) {
+        case 1: return causal ? occupancy_t<D, 1, true>() : occupancy_t<D, 1, false>();
+        case 2: return causal ? occupancy_t<D, 2, true>() : occupancy_t<D, 2, false>();
+        case 4: return causal ? occupancy_t<D, 4, true>() : occupancy_t<D, 4, false>();
+        default: return 0;
+    }
+}
+
 }  // namespace
+
+int attention_wgs_per_cu(int D, int NW, bool causal) {
+    switch (D) {
+        case 64: return occupancy_d<64>(NW, causal);
+        case 128: return occupancy_d<128>(NW, causal);
+        case 256: return occupancy_d<256>(NW, causal);
+        default: return 0;
+    }
+}
 
 hipError_t launch_attention(const AttnArgs &a, int D, int NW, bool causal, bool debug,
                             hipStream_t stream) {

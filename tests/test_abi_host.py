@@ -91,6 +91,8 @@ def test_verify_argument_errors(lib, stvmod):
     assert _verify(lib, stvmod, q=None) == E.STV_EINVAL
     assert _verify(lib, stvmod, out=None) == E.STV_EINVAL
     assert _verify(lib, stvmod, scale=float("inf")) == E.STV_EINVAL
+    assert _verify(lib, stvmod, scale=0.0) == E.STV_EINVAL
+    assert _verify(lib, stvmod, scale=-0.5) == E.STV_EINVAL
     assert _verify(lib, stvmod, n_splits=-2) == E.STV_EINVAL
     layer = stvmod._KVLayer(FAKE, None, FAKE, FAKE, 4, 256, 1000)
     assert _verify(lib, stvmod, layer=layer) == E.STV_EINVAL
