@@ -197,7 +197,21 @@ Plan make_plan(int T, int Hq, int Hkv, int D, int L, bool causal, int n_splits_r
         // keep at least four tiles.
         const long long slots = attention_slots(D, p.NW, causal);
         const long long groups = (long long)Hkv * p.NRG;
-        S = groups >= slots ? 1 : slots / groups;
+        if (groups < slots) {
+            S = slots / groups;
+        } else {
+            // More row groups than slots: pick the split count (1..4) that
+            // wastes the least of the last round, preferring fewer splits.
+            S = 1;
+            double best = 1e30;
+            for (long long s = 1; s <= 4; ++s) {
+                const double rounds_per_split = (double)((groups * s + slots - 1) / slots) / (double)s;
+                if (rounds_per_split < best - 1e-9) {
+                    best = rounds_per_split;
+                    S = s;
+                }
+            }
+        }
         const long long max_s = n_tiles / 4 > 0 ? n_tiles / 4 : 1;
         if (S > max_s) S = max_s;
     }

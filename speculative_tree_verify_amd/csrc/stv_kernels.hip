@@ -60,6 +60,22 @@ __device__ __forceinline__ uint32_t codes_to_i8(uint32_t o) {
     return ((o | 0x80808080u) - 0x04040404u) ^ 0x80808080u;
 }
 
+// High bytes of the binary16 values c - 4 for c = 0..7 (-4, -3, -2, -1, 0,
+// 1, 2, 3: 0xC400 0xC200 0xC000 0xBC00 0x0000 0x3C00 0x4000 0x4200), as the
+// two source words of a v_perm_b32 byte select (bytes 0-3 from kC4Lo).
+constexpr uint32_t kC4Lo = 0xBCC0C2C4u;
+constexpr uint32_t kC4Hi = 0x42403C00u;
+
+// Combine a value with the same lane of the other 32-lane half.
+__device__ __forceinline__ float max_halves(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ float half_bits_to_float(uint16_t h) {
     return (float)__builtin_bit_cast(_Float16, h);
 }
@@ -237,19 +253,20 @@ struct TileIo {
                 unpack_bytes(it.w1[0], it.w1[1], it.w1[2], ob);
                 const f16x2 svp = {__builtin_bit_cast(_Float16, it.s0),
                                    __builtin_bit_cast(_Float16, it.s1)};
-                const f16x2 off = {(_Float16)1028.0f, (_Float16)1028.0f};
                 uint32_t *vt32 = reinterpret_cast<uint32_t *>(t.vt);
 #pragma unroll
                 for (int q4 = 0; q4 < 4; ++q4) {
-                    const uint32_t wa = h ? oa[4 + q4] : oa[q4];
-                    const uint32_t wb = h ? ob[4 + q4] : ob[q4];
+                    // Byte-select table lookup: code c -> high byte of the
+                    // binary16 value c - 4 (whose low byte is zero).
+                    const uint32_t ta = __builtin_amdgcn_perm(kC4Hi, kC4Lo, h ? oa[4 + q4] : oa[q4]);
+                    const uint32_t tb = __builtin_amdgcn_perm(kC4Hi, kC4Lo, h ? ob[4 + q4] : ob[q4]);
 #pragma unroll
                     for (int i2 = 0; i2 < 4; ++i2) {
-                        // (key 2m, key 2m+1) codes of element e into the two
-                        // halves; 0x6400 | c is the binary16 value 1024 + c.
-                        const uint32_t bits = ((wa >> (8 * i2)) & 0xFFu) |
-                                              (((wb >> (8 * i2)) & 0xFFu) << 16) | 0x64006400u;
-                        const f16x2 val = (__builtin_bit_cast(f16x2, bits) - off) * svp;
+                        // binary16 pair (key 2m, key 2m+1) of element e: bytes
+                        // [0, ta.i2, 0, tb.i2]
+                        const uint32_t sel = 0x000C000Cu | (uint32_t)i2 << 8 | (uint32_t)(4 + i2) << 24;
+                        const uint32_t bits = __builtin_amdgcn_perm(tb, ta, sel);
+                        const f16x2 val = __builtin_bit_cast(f16x2, bits) * svp;
                         const int d = 32 * b + 16 * h + 4 * q4 + i2;
                         vt32[(d * L::VTS + b * L::VBPAD) / 2 + m] = __builtin_bit_cast(uint32_t, val);
                     }
@@ -443,7 +460,7 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(const AttnArgs a) {
             float amax = acc[0];
 #pragma unroll
             for (int r = 1; r < 16; ++r) amax = fmaxf(amax, acc[r]);
-            amax = fmaxf(amax, __shfl_xor(amax, 32));
+            amax = max_halves(amax);
             // a row with c_row == 0 has all visible logits 0
             const float tmax = amax == -INFINITY ? -INFINITY : amax * c_row;
             const float m_new = tmax > m_run + 8.0f ? tmax : m_run;
@@ -481,6 +498,7 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(const AttnArgs a) {
                     psum = __builtin_amdgcn_fdot2(h2, ones, psum, false);
                 }
             l_run += psum;
+            __builtin_amdgcn_s_setprio(1);
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
@@ -490,13 +508,14 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(const AttnArgs a) {
                     oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vop, pk[ks], oacc[dt], 0, 0, 0);
                 }
             }
+            __builtin_amdgcn_s_setprio(0);
         }
         __syncthreads();
     }
 
     // ---- epilogue
     if (!wave_active) return;
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const float l_tot = sum_halves(l_run);
     const float inv_l = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
     const float lse = l_tot > 0.0f ? (m_run + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
     if (!row_ok) return;
