@@ -101,8 +101,8 @@ class Workload:
     def step(self, i, ev=None):
         stv, g = self.stv, self.g
         kv = self.caches[i % len(self.caches)]
-        stv.kv_quant_pack(self.knew, g.ctx_len, kv.k_codes, kv.k_scales)
-        stv.kv_quant_pack(self.vnew, g.ctx_len, kv.v_codes, kv.v_scales)
+        stv.kv_quant_pack(self.knew, g.ctx_len, kv, "k")
+        stv.kv_quant_pack(self.vnew, g.ctx_len, kv, "v")
         if ev is not None:
             ev[0].record()
         if self.S == 1:

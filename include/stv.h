@@ -27,11 +27,19 @@
  *    bitwise identical outputs (fixed split partition, fixed merge order).
  *  - NaN or Inf in the inputs is not checked and propagates.
  *
- * Cache layout (one layer; K and V each):
- *  codes  uint32 [Hkv][capacity][D/32][3]  three words per 32 elements
- *  scales uint16 [Hkv][capacity][D/32]     fp16 bit patterns
- * Element e of a 32-element block holds code c in [0, 7] standing for
- * scale * (c - 4).  Bit layout ("byte-plane"), with e = 4*qq + i:
+ * Cache layout (one layer).  A "block" is three 32-bit words holding 32
+ * codes c in [0, 7]; a code stands for scale * (c - 4).
+ *  K, token-major:
+ *    k_codes  uint32 [Hkv][capacity][D/32][3]   block (key, b): elements 32b..32b+31
+ *    k_scales uint16 [Hkv][capacity][D/32]      fp16 bits, one per block
+ *  V, key-transposed in groups of 32 keys (ng = ceil(capacity / 32)):
+ *    v_codes  uint32 [Hkv][ng][D][3]            block (group, d): element d of
+ *                                               keys 32*group .. 32*group+31
+ *    v_scales uint16 [Hkv][ng][D/32][32]        fp16 bits: scale of elements
+ *                                               32b..32b+31 of each key
+ * K streams with the model dimension contiguous, V with the key dimension
+ * contiguous: the dimension each product contracts over.
+ * Bit layout of a block ("byte-plane"), code e = 4*qq + i:
  *   qq 0,1: word 0 bits [8i + 3qq, +3)      qq 2,3: word 1 bits [8i + 3(qq-2), +3)
  *   qq 4,5: word 2 bits [8i + 3(qq-4), +3)
  *   qq 6:   code bits 0-1 at word 0 bits [8i+6, 8i+8), bit 2 at word 2 bit 8i+6
@@ -58,6 +66,9 @@ extern "C" {
 
 #define STV_MAX_TREE_ROWS 64
 
+#define STV_K 0              /* stv_kv_quant_pack: the K layout */
+#define STV_V 1              /* stv_kv_quant_pack: the V layout */
+
 /* One layer's quantized cache (layout above).  Passed by [host] pointer. */
 typedef struct stv_kv_layer {
     const uint32_t *k_codes;
@@ -78,20 +89,23 @@ int32_t stv_abi_version(void);
 /*
  * stv_kv_quant_pack -- write new tokens' K or V rows into the 3-bit cache
  * (the 3-bit KV cache of elpis, "Setup"; the pages do not state the rule).
- * Call once for K and once for V.
+ * Call once for K (which = STV_K) and once for V (which = STV_V).
  *   x       fp32 [n_tok][n_kv_heads][head_dim], the new rows
  *   pos0    first cache position written; positions pos0 .. pos0+n_tok-1
- *           are overwritten, every other position is left untouched
+ *           are overwritten, every other position is left untouched (for V
+ *           only those keys' bits and scales change in the shared blocks)
  *   codes, scales   the cache arrays of that tensor (layout above)
  * Rule per 32-element block: s = fp16_rne(amax / 3) (the largest finite fp16
  * if that overflows), code = clamp(rint(x / s), -4, 3) + 4, all codes 4 when
  * s is zero; the division is correctly rounded and rint rounds half to even.
- * Errors: STV_EINVAL (null pointer, n_tok < 0, bad head_dim or heads),
- * STV_ECAPACITY (pos0 < 0 or pos0 + n_tok > capacity), STV_EHIP.
+ * Calls for the same tensor that touch the same 32-key group of V must not
+ * run concurrently (they rewrite shared words).
+ * Errors: STV_EINVAL (null pointer, n_tok < 0, bad head_dim, heads or
+ * which), STV_ECAPACITY (pos0 < 0 or pos0 + n_tok > capacity), STV_EHIP.
  */
-int stv_kv_quant_pack(const float *x, int32_t n_tok, int32_t pos0, uint32_t *codes,
-                      uint16_t *scales, int32_t n_kv_heads, int32_t head_dim,
-                      int32_t capacity, void *stream);
+int stv_kv_quant_pack(const float *x, int32_t n_tok, int32_t pos0, int32_t which,
+                      uint32_t *codes, uint16_t *scales, int32_t n_kv_heads,
+                      int32_t head_dim, int32_t capacity, void *stream);
 
 /*
  * stv_attention_plan -- the split plan a verify (causal = 0) or prefill

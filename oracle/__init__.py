@@ -51,8 +51,9 @@ def _load():
         lib.orc_quantize_q_row.restype = None
         lib.orc_quantize_kv_block.argtypes = [P, P]
         lib.orc_quantize_kv_block.restype = ctypes.c_uint16
-        lib.orc_kv_quant_pack.argtypes = [P, i32, i32, P, P, i32, i32, i32]
-        lib.orc_kv_quant_pack.restype = None
+        for fn in (lib.orc_k_quant_pack, lib.orc_v_quant_pack):
+            fn.argtypes = [P, i32, i32, P, P, i32, i32, i32]
+            fn.restype = None
         lib.orc_attention.argtypes = [P, i32, i32, P, P, P, P, i32, i32, i32, i32, P,
                                       ctypes.c_double, i32, i32, P, i32, P, P, P, P, P]
         lib.orc_attention.restype = i32
@@ -141,16 +142,42 @@ def quantize_kv_block(x) -> tuple[np.ndarray, int]:
     return w, int(s)
 
 
-def kv_quant_pack(x, pos0: int, codes: np.ndarray, scales: np.ndarray) -> None:
-    """x: [n_tok][Hkv][D] fp32, written in place into codes/scales."""
+def kv_quant_pack(x, pos0: int, codes: np.ndarray, scales: np.ndarray, which: str) -> None:
+    """x: [n_tok][Hkv][D] fp32, written in place into codes/scales of the K
+    (token-major) or V (key-transposed) layout; which is "k" or "v"."""
     x = _c(x, np.float32)
     n_tok, hkv, d = x.shape
+    nb = d // 32
     assert codes.dtype == np.uint32 and codes.flags.c_contiguous
     assert scales.dtype == np.uint16 and scales.flags.c_contiguous
-    cap = codes.shape[1]
-    assert codes.shape == (hkv, cap, d // 32, 3) and scales.shape == (hkv, cap, d // 32)
+    if which == "k":
+        cap = codes.shape[1]
+        assert codes.shape == (hkv, cap, nb, 3) and scales.shape == (hkv, cap, nb)
+        fn = _load().orc_k_quant_pack
+    elif which == "v":
+        ng = codes.shape[1]
+        cap = 32 * ng
+        assert codes.shape == (hkv, ng, d, 3) and scales.shape == (hkv, ng, nb, 32)
+        fn = _load().orc_v_quant_pack
+    else:
+        raise ValueError(which)
     assert 0 <= pos0 and pos0 + n_tok <= cap
-    _load().orc_kv_quant_pack(_ptr(x), n_tok, pos0, _ptr(codes), _ptr(scales), hkv, d, cap)
+    fn(_ptr(x), n_tok, pos0, _ptr(codes), _ptr(scales), hkv, d, cap)
+
+
+def v_values(kv, head: int, key: int) -> np.ndarray:
+    """Dequantized V row (fp64) of one key, read through the V layout."""
+    d = kv.head_dim
+    ng = kv.v_codes.shape[1]
+    lib = _load()
+    out = np.empty(d)
+    grp, e = divmod(key, 32)
+    for b in range(d // 32):
+        s = f16_bits_to_f64(int(kv.v_scales[head, grp, b, e]))
+        for i in range(32):
+            w = _c(kv.v_codes[head, grp, 32 * b + i], np.uint32)
+            out[32 * b + i] = s * (lib.orc_code_get(_ptr(w), e) - 4)
+    return out
 
 
 # --------------------------------------------------------------- attention
@@ -161,7 +188,7 @@ def attention(q, kv, ctx_len: int, mask=None, scale: float | None = None,
     """The oracle's attention for the rows listed (flattened t*Hq + h).
 
     kv: an object with k_codes, k_scales, v_codes, v_scales, n_kv_heads,
-    head_dim, capacity.  mask: uint64 [T] ancestor masks, or None for the
+    head_dim, capacity (K token-major, V key-transposed; see stv_oracle.c).  mask: uint64 [T] ancestor masks, or None for the
     causal chunk rule.  Returns dict(out fp64 [n][D], lse fp64 [n],
     qi8 int8 [n][D], sq fp32 [n], logits int64 [n][L+T][NB] or None).
     """

@@ -46,6 +46,11 @@
  *       3) + 4, and code 4 everywhere when s16 is zero.
  *  (c6) the K scale is one fp16 per 32 consecutive elements of one (token,
  *       kv head) row; the softmax scale is a caller argument.
+ *  (c8) storage: K is token-major, codes [Hkv][cap][D/32][3 words] and scales
+ *       [Hkv][cap][D/32]; V is key-transposed in groups of 32 keys, codes
+ *       [Hkv][ng][D][3 words] where element d of key 32*grp + e is code e of
+ *       the block (grp, d), and scales [Hkv][ng][D/32][32] (ng = ceil(cap/32)).
+ *       The bit layout of a three-word block is the same for both.
  *  (c7) tree keys sit at L + node index; key L + a is visible to row i iff
  *       bit a of mask[i] is set; a NULL mask means the causal chunk rule
  *       (key L + u visible to row t iff u <= t).
@@ -192,10 +197,13 @@ ORC_EXPORT uint16_t orc_quantize_kv_block(const float *x, uint32_t *w)
     return s16;
 }
 
-/* x: [n_tok][Hkv][D] fp32; codes: [Hkv][cap][D/32][3]; scales: [Hkv][cap][D/32].
- * Writes positions pos0 .. pos0+n_tok-1. */
-ORC_EXPORT void orc_kv_quant_pack(const float *x, int n_tok, int pos0, uint32_t *codes,
-                                  uint16_t *scales, int Hkv, int D, int cap)
+/* Number of 32-key groups of the V layout for a capacity. */
+static size_t n_groups(int cap) { return ((size_t)cap + 31) / 32; }
+
+/* K: x [n_tok][Hkv][D] fp32 into codes [Hkv][cap][D/32][3], scales
+ * [Hkv][cap][D/32]; writes positions pos0 .. pos0+n_tok-1 only. */
+ORC_EXPORT void orc_k_quant_pack(const float *x, int n_tok, int pos0, uint32_t *codes,
+                                 uint16_t *scales, int Hkv, int D, int cap)
 {
     int nb = D / 32;
     for (int t = 0; t < n_tok; ++t)
@@ -207,10 +215,44 @@ ORC_EXPORT void orc_kv_quant_pack(const float *x, int n_tok, int pos0, uint32_t 
             }
 }
 
+/* V: the same rule per (token, head, block); stored key-transposed, codes
+ * [Hkv][ng][D][3] and scales [Hkv][ng][D/32][32].  Only the bits and scales of
+ * keys pos0 .. pos0+n_tok-1 change. */
+ORC_EXPORT void orc_v_quant_pack(const float *x, int n_tok, int pos0, uint32_t *codes,
+                                 uint16_t *scales, int Hkv, int D, int cap)
+{
+    int nb = D / 32;
+    size_t ng = n_groups(cap);
+    for (int t = 0; t < n_tok; ++t)
+        for (int g = 0; g < Hkv; ++g)
+            for (int b = 0; b < nb; ++b) {
+                int pos = pos0 + t, grp = pos / 32, e = pos % 32;
+                uint32_t w[3];
+                uint16_t s16 = orc_quantize_kv_block(x + ((size_t)t * Hkv + g) * D + 32 * b, w);
+                scales[(((size_t)g * ng + grp) * nb + b) * 32 + e] = s16;
+                for (int i = 0; i < 32; ++i) {
+                    int d = 32 * b + i;
+                    uint32_t *dst = codes + (((size_t)g * ng + grp) * D + d) * 3;
+                    orc_code_set(dst, e, orc_code_get(w, i));
+                }
+            }
+}
+
+/* Code and scale of V element d of key j (kv head g). */
+static int v_code(const uint32_t *vc, size_t ng, int D, int g, int j, int d)
+{
+    return orc_code_get(vc + (((size_t)g * ng + (size_t)(j / 32)) * D + d) * 3, j % 32);
+}
+
+static double v_scale(const uint16_t *vs, size_t ng, int nb, int g, int j, int b)
+{
+    return orc_f16_to_f64(vs[(((size_t)g * ng + (size_t)(j / 32)) * nb + b) * 32 + j % 32]);
+}
+
 /* ------------------------------------------------------------- attention */
 
 /* Returns 0 on success, -1 on bad arguments.
- * q: [T][Hq][D]; caches as above; mask: [T] (NULL = causal chunk rule).
+ * q: [T][Hq][D]; caches as in (c8); mask: [T] (NULL = causal chunk rule).
  * Only keys j in [k_begin, k_end) take part (a split-K partial); pass
  * 0, L+T for the whole call.  rows: flattened t*Hq + h (NULL = all rows in
  * order).  Outputs are per listed row: out [n][D], lse [n], and optionally
@@ -229,6 +271,7 @@ ORC_EXPORT int orc_attention(const float *q, int T, int Hq,
         L + T > cap || (mask && T > 64))
         return -1;
     int nb = D / 32, G = Hq / Hkv, N = L + T;
+    size_t ng = n_groups(cap);
     if (!rows)
         n_rows = T * Hq;
     int bad = 0;
@@ -287,12 +330,10 @@ ORC_EXPORT int orc_attention(const float *q, int T, int Hq,
                     continue;
                 double p = exp(x[j] - m);
                 l += p;
-                const uint32_t *vw = vc + (((size_t)g * cap + j) * nb) * 3;
-                const uint16_t *vsj = vs + ((size_t)g * cap + j) * nb;
                 for (int b = 0; b < nb; ++b) {
-                    double sv = orc_f16_to_f64(vsj[b]);
+                    double sv = v_scale(vs, ng, nb, g, j, b);
                     for (int e = 0; e < 32; ++e)
-                        o[32 * b + e] += p * (sv * (double)(orc_code_get(vw + 3 * b, e) - 4));
+                        o[32 * b + e] += p * (sv * (double)(v_code(vc, ng, D, g, j, 32 * b + e) - 4));
                 }
             }
             for (int d = 0; d < D; ++d)

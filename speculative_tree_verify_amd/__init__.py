@@ -63,7 +63,7 @@ def load_library():
         lib.stv_abi_version.restype = i32
         lib.stv_abi_version.argtypes = []
         lib.stv_kv_quant_pack.restype = ctypes.c_int
-        lib.stv_kv_quant_pack.argtypes = [P, i32, i32, P, P, i32, i32, i32, P]
+        lib.stv_kv_quant_pack.argtypes = [P, i32, i32, i32, P, P, i32, i32, i32, P]
         lib.stv_attention_plan.restype = ctypes.c_int
         lib.stv_attention_plan.argtypes = [i32, i32, i32, i32, i32, i32, i32,
                                            ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_size_t)]
@@ -114,12 +114,18 @@ def _stream(device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
+STV_K = 0
+STV_V = 1
+
+
 @dataclass
 class KVCache:
-    """One layer's 3-bit cache on the GPU.
+    """One layer's 3-bit cache on the GPU (layouts as in include/stv.h).
 
-    k_codes, v_codes: int32 [Hkv][capacity][D/32][3] (32-bit words)
-    k_scales, v_scales: float16 [Hkv][capacity][D/32]
+    k_codes: int32 [Hkv][capacity][D/32][3] (32-bit words), k_scales: float16
+    [Hkv][capacity][D/32]; v_codes: int32 [Hkv][ng][D][3], v_scales: float16
+    [Hkv][ng][D/32][32] with ng = ceil(capacity / 32).  The capacity is that
+    of the K arrays.
     """
     k_codes: "object"
     k_scales: "object"
@@ -142,11 +148,12 @@ class KVCache:
     def empty(cls, n_kv_heads: int, head_dim: int, capacity: int, device="cuda"):
         torch = _torch()
         nb = head_dim // 32
+        ng = (capacity + 31) // 32
         z = lambda shape, dt: torch.zeros(shape, dtype=dt, device=device)  # noqa: E731
         return cls(z((n_kv_heads, capacity, nb, 3), torch.int32),
                    z((n_kv_heads, capacity, nb), torch.float16),
-                   z((n_kv_heads, capacity, nb, 3), torch.int32),
-                   z((n_kv_heads, capacity, nb), torch.float16))
+                   z((n_kv_heads, ng, head_dim, 3), torch.int32),
+                   z((n_kv_heads, ng, nb, 32), torch.float16))
 
     @classmethod
     def from_host(cls, host, device="cuda"):
@@ -160,27 +167,31 @@ class KVCache:
 
     def _layer(self) -> _KVLayer:
         torch = _torch()
-        nb = self.head_dim // 32
-        shp_c = (self.n_kv_heads, self.capacity, nb, 3)
-        shp_s = (self.n_kv_heads, self.capacity, nb)
-        return _KVLayer(_dev_ptr(self.k_codes, torch.int32, "k_codes", shp_c),
-                        _dev_ptr(self.k_scales, torch.float16, "k_scales", shp_s),
-                        _dev_ptr(self.v_codes, torch.int32, "v_codes", shp_c),
-                        _dev_ptr(self.v_scales, torch.float16, "v_scales", shp_s),
-                        self.n_kv_heads, self.head_dim, self.capacity)
+        hkv, cap, d = self.n_kv_heads, self.capacity, self.head_dim
+        nb, ng = d // 32, (cap + 31) // 32
+        return _KVLayer(_dev_ptr(self.k_codes, torch.int32, "k_codes", (hkv, cap, nb, 3)),
+                        _dev_ptr(self.k_scales, torch.float16, "k_scales", (hkv, cap, nb)),
+                        _dev_ptr(self.v_codes, torch.int32, "v_codes", (hkv, ng, d, 3)),
+                        _dev_ptr(self.v_scales, torch.float16, "v_scales", (hkv, ng, nb, 32)),
+                        hkv, d, cap)
 
 
-def kv_quant_pack(x, pos0: int, codes, scales):
-    """Quantize x [n_tok][Hkv][D] fp32 into cache positions pos0.. of one tensor."""
+def kv_quant_pack(x, pos0: int, cache: KVCache, which: str):
+    """Quantize x [n_tok][Hkv][D] fp32 into positions pos0.. of the cache's K
+    (which="k") or V (which="v") arrays."""
     torch = _torch()
     n_tok, hkv, d = x.shape
-    cap = int(codes.shape[1])
-    _dev_ptr(codes, torch.int32, "codes", (hkv, cap, d // 32, 3))
-    _dev_ptr(scales, torch.float16, "scales", (hkv, cap, d // 32))
+    if which not in ("k", "v"):
+        raise ValueError("which must be 'k' or 'v'")
+    layer = cache._layer()
+    if hkv != cache.n_kv_heads or d != cache.head_dim:
+        raise ValueError("x does not match the cache's heads or head_dim")
+    codes, scales = (cache.k_codes, cache.k_scales) if which == "k" else (cache.v_codes, cache.v_scales)
     rc = load_library().stv_kv_quant_pack(
-        _dev_ptr(x, torch.float32, "x"), n_tok, pos0, codes.data_ptr(), scales.data_ptr(),
-        hkv, d, cap, _stream(x.device))
+        _dev_ptr(x, torch.float32, "x"), n_tok, pos0, STV_K if which == "k" else STV_V,
+        codes.data_ptr(), scales.data_ptr(), hkv, d, cache.capacity, _stream(x.device))
     _check(rc)
+    del layer
 
 
 def attention_plan(T: int, n_q_heads: int, n_kv_heads: int, head_dim: int, ctx_len: int,

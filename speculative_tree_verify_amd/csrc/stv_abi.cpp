@@ -15,6 +15,7 @@
 namespace {
 
 thread_local char g_err[512] = "";
+constexpr int kKeyTileC = stv::kKeyTile;
 
 int fail(int code, const char *fmt, ...) {
     va_list ap;
@@ -123,6 +124,7 @@ int attention_common(const float *q, int T, int Hq, const stv_kv_layer *kv, int 
     a.Hkv = Hkv;
     a.G = Hq / Hkv;
     a.cap = kv->capacity;
+    a.ngroups = (kv->capacity + kKeyTileC - 1) / kKeyTileC;
     a.L = L;
     a.N = L + T;
     a.R = T * a.G;
@@ -240,9 +242,10 @@ const char *stv_last_error(void) { return g_err; }
 
 int32_t stv_abi_version(void) { return 1; }
 
-int stv_kv_quant_pack(const float *x, int32_t n_tok, int32_t pos0, uint32_t *codes,
-                      uint16_t *scales, int32_t n_kv_heads, int32_t head_dim, int32_t capacity,
-                      void *stream) {
+int stv_kv_quant_pack(const float *x, int32_t n_tok, int32_t pos0, int32_t which,
+                      uint32_t *codes, uint16_t *scales, int32_t n_kv_heads, int32_t head_dim,
+                      int32_t capacity, void *stream) {
+    if (which != STV_K && which != STV_V) return fail(STV_EINVAL, "which must be STV_K or STV_V");
     if (n_tok < 0) return fail(STV_EINVAL, "n_tok must be >= 0");
     if (n_kv_heads <= 0) return fail(STV_EINVAL, "n_kv_heads must be positive");
     if (!head_dim_ok(head_dim)) return fail(STV_EINVAL, "head_dim %d unsupported (64, 128 or 256)", head_dim);
@@ -253,7 +256,7 @@ int stv_kv_quant_pack(const float *x, int32_t n_tok, int32_t pos0, uint32_t *cod
     if (n_tok == 0) return ok();
     if (!x || !codes || !scales) return fail(STV_EINVAL, "x, codes and scales must not be NULL");
     hipError_t e = stv::launch_kv_pack(x, n_tok, pos0, codes, scales, n_kv_heads, head_dim,
-                                       capacity, static_cast<hipStream_t>(stream));
+                                       capacity, which == STV_V, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(STV_EHIP, "kv pack launch failed: %s", hipGetErrorString(e));
     return ok();
 }

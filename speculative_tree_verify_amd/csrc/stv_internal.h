@@ -27,7 +27,7 @@ struct AttnArgs {
     int32_t *dbg_logits; // nullable [T*Hq][N][D/32]
     int8_t *dbg_q;       // nullable [T*Hq][D]
     float *dbg_qscale;   // nullable [T*Hq]
-    int32_t T, Hq, Hkv, G, cap, L, N, R;
+    int32_t T, Hq, Hkv, G, cap, ngroups, L, N, R;
     int32_t S, split_len, NRG, n_hs_pad;
     float scale_log2;    // softmax_scale * log2(e)
     uint64_t mask[64];   // verify only: ancestor masks of the tree rows
@@ -57,6 +57,7 @@ hipError_t launch_attention(const AttnArgs &a, int D, int NW, bool causal, bool 
 hipError_t launch_merge(const float *part_o, const float *part_lse, int S, int rows, int D,
                         float *out, float *out_lse, hipStream_t stream);
 hipError_t launch_kv_pack(const float *x, int n_tok, int pos0, uint32_t *codes,
-                          uint16_t *scales, int Hkv, int D, int cap, hipStream_t stream);
+                          uint16_t *scales, int Hkv, int D, int cap, bool is_v,
+                          hipStream_t stream);
 
 }  // namespace stv

@@ -82,9 +82,60 @@ __device__ __forceinline__ float half_bits_to_float(uint16_t h) {
 
 // ------------------------------------------------------------- kv pack
 
-__global__ void kv_pack_kernel(const float *__restrict__ x, int n_tok, int pos0,
-                               uint32_t *__restrict__ codes, uint16_t *__restrict__ scales,
-                               int Hkv, int D, int cap) {
+// Quantize the 32 elements v[] with the symmetric rule: scale fp16(amax / 3)
+// saturated to the largest finite value; code clamp(rint(x / s), -4, 3) + 4,
+// all 4 when the scale is zero.  Divisions are IEEE correctly rounded.
+__device__ __forceinline__ uint16_t block_scale(const float v[32]) {
+    float amax = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) amax = fmaxf(amax, fabsf(v[e]));
+    _Float16 sh = (_Float16)(amax / 3.0f);            // RNE to binary16
+    uint16_t s16 = __builtin_bit_cast(uint16_t, sh);
+    if ((s16 & 0x7FFFu) == 0x7C00u) s16 = 0x7BFFu;     // saturate to 65504
+    return s16;
+}
+
+__device__ __forceinline__ uint32_t code_of(float x, float s) {
+    if (s == 0.0f) return 4u;
+    float r = rintf(x / s);
+    r = fminf(fmaxf(r, -4.0f), 3.0f);
+    return (uint32_t)((int)r + 4);
+}
+
+// Set element e's code in a three-word block (byte-plane layout).
+__device__ __forceinline__ void set_code(uint32_t &w0, uint32_t &w1, uint32_t &w2, int e,
+                                         uint32_t c) {
+    const int qq = e >> 2, i = e & 3;
+    if (qq < 6) {
+        const int sh = 8 * i + 3 * (qq & 1);
+        const uint32_t m = 7u << sh;
+        uint32_t &w = qq < 2 ? w0 : (qq < 4 ? w1 : w2);
+        w = (w & ~m) | (c << sh);
+    } else {
+        const int sh = 8 * i + 6;
+        uint32_t &w = qq == 6 ? w0 : w1;
+        w = (w & ~(3u << sh)) | ((c & 3u) << sh);
+        const int hb = 8 * i + 6 + (qq - 6);
+        w2 = (w2 & ~(1u << hb)) | ((c >> 2) << hb);
+    }
+}
+
+__device__ __forceinline__ void load32(const float *src, float v[32]) {
+    const f32x4 *p = reinterpret_cast<const f32x4 *>(src);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const f32x4 f = p[j];
+        v[4 * j + 0] = f.x;
+        v[4 * j + 1] = f.y;
+        v[4 * j + 2] = f.z;
+        v[4 * j + 3] = f.w;
+    }
+}
+
+// K: one thread per (token, head, block); token-major layout.
+__global__ void k_pack_kernel(const float *__restrict__ x, int n_tok, int pos0,
+                              uint32_t *__restrict__ codes, uint16_t *__restrict__ scales,
+                              int Hkv, int D, int cap) {
     const int NB = D / 32;
     const long long total = (long long)n_tok * Hkv * NB;
     const long long id = (long long)blockIdx.x * blockDim.x + threadIdx.x;
@@ -92,37 +143,16 @@ __global__ void kv_pack_kernel(const float *__restrict__ x, int n_tok, int pos0,
     const int b = (int)(id % NB);
     const int g = (int)((id / NB) % Hkv);
     const int t = (int)(id / ((long long)NB * Hkv));
-    const f32x4 *src = reinterpret_cast<const f32x4 *>(x + ((size_t)t * Hkv + g) * D + 32 * b);
     float v[32];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        f32x4 f = src[j];
-        v[4 * j + 0] = f.x;
-        v[4 * j + 1] = f.y;
-        v[4 * j + 2] = f.z;
-        v[4 * j + 3] = f.w;
-    }
-    float amax = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 32; ++e) amax = fmaxf(amax, fabsf(v[e]));
-    _Float16 sh = (_Float16)(amax / 3.0f);            // RNE to binary16
-    uint16_t s16 = __builtin_bit_cast(uint16_t, sh);
-    if ((s16 & 0x7FFFu) == 0x7C00u) s16 = 0x7BFFu;     // saturate to 65504
+    load32(x + ((size_t)t * Hkv + g) * D + 32 * b, v);
+    const uint16_t s16 = block_scale(v);
     const float s = half_bits_to_float(s16);
     uint32_t o[8];
 #pragma unroll
     for (int qq = 0; qq < 8; ++qq) {
         uint32_t word = 0;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            int c = 4;
-            if (s != 0.0f) {
-                float r = rintf(v[4 * qq + i] / s);
-                r = fminf(fmaxf(r, -4.0f), 3.0f);
-                c = (int)r + 4;
-            }
-            word |= (uint32_t)c << (8 * i);
-        }
+        for (int i = 0; i < 4; ++i) word |= code_of(v[4 * qq + i], s) << (8 * i);
         o[qq] = word;
     }
     uint32_t w0, w1, w2;
@@ -133,6 +163,52 @@ __global__ void kv_pack_kernel(const float *__restrict__ x, int n_tok, int pos0,
     dst[1] = w1;
     dst[2] = w2;
     scales[pos * NB + b] = s16;
+}
+
+// V, first pass: one thread per (token, head, block) writes the scale into
+// the key-transposed scale layout [Hkv][ng][D/32][32].
+__global__ void v_scale_kernel(const float *__restrict__ x, int n_tok, int pos0,
+                               uint16_t *__restrict__ scales, int Hkv, int D, int ng) {
+    const int NB = D / 32;
+    const long long total = (long long)n_tok * Hkv * NB;
+    const long long id = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (id >= total) return;
+    const int b = (int)(id % NB);
+    const int g = (int)((id / NB) % Hkv);
+    const int t = (int)(id / ((long long)NB * Hkv));
+    float v[32];
+    load32(x + ((size_t)t * Hkv + g) * D + 32 * b, v);
+    const int pos = pos0 + t;
+    scales[(((size_t)g * ng + pos / 32) * NB + b) * 32 + (pos & 31)] = block_scale(v);
+}
+
+// V, second pass: one thread per (head, group, element d) rewrites the three
+// words holding that element of the group's 32 keys, changing only the keys
+// in [pos0, pos0 + n_tok).
+__global__ void v_code_kernel(const float *__restrict__ x, int n_tok, int pos0,
+                              uint32_t *__restrict__ codes, const uint16_t *__restrict__ scales,
+                              int Hkv, int D, int ng, int grp0, int n_grp) {
+    const int NB = D / 32;
+    const long long total = (long long)n_grp * Hkv * D;
+    const long long id = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (id >= total) return;
+    const int d = (int)(id % D);
+    const int g = (int)((id / D) % Hkv);
+    const int grp = grp0 + (int)(id / ((long long)D * Hkv));
+    uint32_t *w = codes + (((size_t)g * ng + grp) * D + d) * 3;
+    uint32_t w0 = w[0], w1 = w[1], w2 = w[2];
+    const uint16_t *srow = scales + (((size_t)g * ng + grp) * NB + d / 32) * 32;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+        const int pos = grp * 32 + e;
+        if (pos >= pos0 && pos < pos0 + n_tok) {
+            const float xv = x[((size_t)(pos - pos0) * Hkv + g) * D + d];
+            set_code(w0, w1, w2, e, code_of(xv, half_bits_to_float(srow[e])));
+        }
+    }
+    w[0] = w0;
+    w[1] = w1;
+    w[2] = w2;
 }
 
 // ------------------------------------------------------------ attention
@@ -147,6 +223,7 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 //        pad of 16 dwords spreads the four blocks written by one wave over
 //        all 64 banks.
 //   skf: fp32 K scales, [D/32][32 keys]
+//   svs: fp16 V scales as stored, [D/32][32 keys]
 template <int D>
 struct TileLds {
     static constexpr int NB = D / 32;
@@ -156,6 +233,7 @@ struct TileLds {
     int8_t kq[kKeyTile * KQS];
     _Float16 vt[D * VTS + NB * VBPAD];
     float skf[NB * kKeyTile];
+    alignas(16) uint16_t svs[D];   // the tile's V scales, [D/32][32 keys]
 };
 
 // One (key, block) item of the K side: 3 code words and the fp16 scale.
@@ -163,25 +241,34 @@ struct KItem {
     uint32_t w[3];
     uint16_t s;
 };
-// One (key pair, block, element half) item of the V side: 3 code words of
-// each key and both scales.
+// One element row d of the V side: the 3 words holding element d of the
+// tile's 32 keys, and one of the tile's V scales (entry d: block d / 32,
+// key d % 32), which the thread's own wave needs for its rows.
 struct VItem {
-    uint32_t w0[3], w1[3];
-    uint16_t s0, s1;
+    uint32_t w[3];
+    uint16_t s;
 };
+
+// A wave-local handoff through LDS: the wave's own earlier LDS writes are
+// visible to all of its lanes afterwards.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
 
 template <int D, int NT>
 struct TileIo {
     static constexpr int NB = D / 32;
     static constexpr int KI = kKeyTile * NB;           // K items per tile
-    static constexpr int VI = (kKeyTile / 2) * NB * 2;  // V items per tile
+    static constexpr int VI = D;                        // V rows per tile (= V scales)
     static constexpr int KPT = (KI + NT - 1) / NT;
     static constexpr int VPT = (VI + NT - 1) / NT;
     KItem k[KPT];
     VItem v[VPT];
 
-    __device__ __forceinline__ void load(const AttnArgs &a, size_t head_base, int kb, int k1,
-                                         int tid) {
+    __device__ __forceinline__ void load(const AttnArgs &a, int head, int kb, int k1, int tid) {
+        const size_t head_base = (size_t)head * a.cap;
 #pragma unroll
         for (int i = 0; i < KPT; ++i) {
             const int item = tid + i * NT;
@@ -198,28 +285,20 @@ struct TileIo {
                 k[i].s = a.ks[blk];
             }
         }
+        const size_t grp_base = (size_t)head * a.ngroups + (size_t)(kb / kKeyTile);
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
-            const int item = tid + i * NT;
-            const int m = item % 16, b = (item / 16) % NB;
-            const int key = kb + 2 * m;
+            const int d = tid + i * NT;
             VItem &it = v[i];
-            it.w0[0] = it.w0[1] = it.w0[2] = 0u;
-            it.w1[0] = it.w1[1] = it.w1[2] = 0u;
-            it.s0 = it.s1 = 0;
-            if (item < VI && key < k1) {
-                const size_t blk = (head_base + key) * NB + b;
-                const uint32_t *src = a.vc + blk * 3;
-                it.w0[0] = src[0];
-                it.w0[1] = src[1];
-                it.w0[2] = src[2];
-                it.s0 = a.vs[blk];
-                if (key + 1 < k1) {
-                    it.w1[0] = src[3 * NB + 0];
-                    it.w1[1] = src[3 * NB + 1];
-                    it.w1[2] = src[3 * NB + 2];
-                    it.s1 = a.vs[blk + NB];
-                }
+            it.w[0] = it.w[1] = it.w[2] = 0u;
+            it.s = 0;
+            if (d < VI) {
+                const uint32_t *src = a.vc + (grp_base * D + d) * 3;
+                it.w[0] = src[0];
+                it.w[1] = src[1];
+                it.w[2] = src[2];
+                // keys past the range get scale 0, so their V^ is exactly 0
+                if (kb + (d & 31) < k1) it.s = a.vs[grp_base * D + d];
             }
         }
     }
@@ -242,35 +321,40 @@ struct TileIo {
                 t.skf[b * kKeyTile + kk] = half_bits_to_float(k[i].s);
             }
         }
+        // V scales: every wave stages the entries its own rows need.
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
-            const int item = tid + i * NT;
-            if (item < VI) {
-                const int m = item % 16, b = (item / 16) % NB, h = item / (16 * NB);
-                const VItem &it = v[i];
-                uint32_t oa[8], ob[8];
-                unpack_bytes(it.w0[0], it.w0[1], it.w0[2], oa);
-                unpack_bytes(it.w1[0], it.w1[1], it.w1[2], ob);
-                const f16x2 svp = {__builtin_bit_cast(_Float16, it.s0),
-                                   __builtin_bit_cast(_Float16, it.s1)};
-                uint32_t *vt32 = reinterpret_cast<uint32_t *>(t.vt);
+            const int d = tid + i * NT;
+            if (d < VI) t.svs[d] = v[i].s;
+        }
+        wave_lds_sync();
 #pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) {
+        for (int i = 0; i < VPT; ++i) {
+            const int d = tid + i * NT;
+            if (d < VI) {
+                const VItem &it = v[i];
+                uint32_t o[8];
+                unpack_bytes(it.w[0], it.w[1], it.w[2], o);   // keys 4qq..4qq+3 in o[qq]
+                const uint32_t *sv32 = reinterpret_cast<const uint32_t *>(t.svs + (d & ~31));
+                uint32_t row[16];
+#pragma unroll
+                for (int qq = 0; qq < 8; ++qq) {
                     // Byte-select table lookup: code c -> high byte of the
                     // binary16 value c - 4 (whose low byte is zero).
-                    const uint32_t ta = __builtin_amdgcn_perm(kC4Hi, kC4Lo, h ? oa[4 + q4] : oa[q4]);
-                    const uint32_t tb = __builtin_amdgcn_perm(kC4Hi, kC4Lo, h ? ob[4 + q4] : ob[q4]);
-#pragma unroll
-                    for (int i2 = 0; i2 < 4; ++i2) {
-                        // binary16 pair (key 2m, key 2m+1) of element e: bytes
-                        // [0, ta.i2, 0, tb.i2]
-                        const uint32_t sel = 0x000C000Cu | (uint32_t)i2 << 8 | (uint32_t)(4 + i2) << 24;
-                        const uint32_t bits = __builtin_amdgcn_perm(tb, ta, sel);
-                        const f16x2 val = __builtin_bit_cast(f16x2, bits) * svp;
-                        const int d = 32 * b + 16 * h + 4 * q4 + i2;
-                        vt32[(d * L::VTS + b * L::VBPAD) / 2 + m] = __builtin_bit_cast(uint32_t, val);
-                    }
+                    const uint32_t tt = __builtin_amdgcn_perm(kC4Hi, kC4Lo, o[qq]);
+                    const uint32_t p01 = __builtin_amdgcn_perm(tt, tt, 0x010C000Cu);
+                    const uint32_t p23 = __builtin_amdgcn_perm(tt, tt, 0x030C020Cu);
+                    const f16x2 v01 = __builtin_bit_cast(f16x2, p01) *
+                                      __builtin_bit_cast(f16x2, sv32[2 * qq]);
+                    const f16x2 v23 = __builtin_bit_cast(f16x2, p23) *
+                                      __builtin_bit_cast(f16x2, sv32[2 * qq + 1]);
+                    row[2 * qq] = __builtin_bit_cast(uint32_t, v01);
+                    row[2 * qq + 1] = __builtin_bit_cast(uint32_t, v23);
                 }
+                u32x4 *dst = reinterpret_cast<u32x4 *>(t.vt + d * L::VTS + (d / 32) * L::VBPAD);
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    dst[j] = u32x4{row[4 * j], row[4 * j + 1], row[4 * j + 2], row[4 * j + 3]};
             }
         }
     }
@@ -399,14 +483,13 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(const AttnArgs a) {
     float m_run = -INFINITY;
     float l_run = 0.0f;
 
-    const size_t head_base = (size_t)head * a.cap;
     TileIo<D, NT> io;
-    if (k0 < k1) io.load(a, head_base, k0, k1, tid);
+    if (k0 < k1) io.load(a, head, k0, k1, tid);
 
     for (int kb = k0; kb < k1; kb += KT) {
         io.store(lds, tid);
         __syncthreads();
-        if (kb + KT < k1) io.load(a, head_base, kb + KT, k1, tid);
+        if (kb + KT < k1) io.load(a, head, kb + KT, k1, tid);
 
         if (wave_active) {
             // ---- Q.K^T: one int8 MFMA per 32-element block, fp32 epilogue.
@@ -716,13 +799,25 @@ hipError_t launch_merge(const float *part_o, const float *part_lse, int S, int r
 }
 
 hipError_t launch_kv_pack(const float *x, int n_tok, int pos0, uint32_t *codes, uint16_t *scales,
-                          int Hkv, int D, int cap, hipStream_t stream) {
-    const long long total = (long long)n_tok * Hkv * (D / 32);
-    if (total == 0) return hipSuccess;
+                          int Hkv, int D, int cap, bool is_v, hipStream_t stream) {
+    const long long items = (long long)n_tok * Hkv * (D / 32);
+    if (items == 0) return hipSuccess;
     const int threads = 256;
-    const long long blocks = (total + threads - 1) / threads;
-    hipLaunchKernelGGL(kv_pack_kernel, dim3((unsigned)blocks), dim3(threads), 0, stream, x, n_tok,
-                       pos0, codes, scales, Hkv, D, cap);
+    if (!is_v) {
+        hipLaunchKernelGGL(k_pack_kernel, dim3((unsigned)((items + threads - 1) / threads)),
+                           dim3(threads), 0, stream, x, n_tok, pos0, codes, scales, Hkv, D, cap);
+        return hipGetLastError();
+    }
+    const int ng = (cap + 31) / 32;
+    hipLaunchKernelGGL(v_scale_kernel, dim3((unsigned)((items + threads - 1) / threads)),
+                       dim3(threads), 0, stream, x, n_tok, pos0, scales, Hkv, D, ng);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int grp0 = pos0 / 32, n_grp = (pos0 + n_tok - 1) / 32 - grp0 + 1;
+    const long long rows = (long long)n_grp * Hkv * D;
+    hipLaunchKernelGGL(v_code_kernel, dim3((unsigned)((rows + threads - 1) / threads)),
+                       dim3(threads), 0, stream, x, n_tok, pos0, codes, scales, Hkv, D, ng, grp0,
+                       n_grp);
     return hipGetLastError();
 }
 

@@ -72,9 +72,13 @@ EXTRA_CONFIGS = [
 class KVCache:
     """Host arrays of one layer's quantized K/V cache.
 
-    k_codes, v_codes: uint32 [Hkv][capacity][D/32][3]
-    k_scales, v_scales: uint16 (fp16 bit patterns) [Hkv][capacity][D/32]
-    Positions >= n_filled are zero.
+    K, token-major:    k_codes uint32 [Hkv][capacity][D/32][3],
+                       k_scales uint16 (fp16 bits) [Hkv][capacity][D/32]
+    V, key-transposed: v_codes uint32 [Hkv][ng][D][3],
+                       v_scales uint16 (fp16 bits) [Hkv][ng][D/32][32]
+    with ng = ceil(capacity / 32) groups of 32 keys.  K positions >= n_filled
+    are zero; V groups past the one holding key n_filled - 1 are zero (the
+    rest of that last group holds random data, which no call reads).
     """
     k_codes: np.ndarray
     k_scales: np.ndarray
@@ -97,17 +101,19 @@ def make_kv(rng: np.random.Generator, n_kv_heads: int, head_dim: int,
         capacity = n_filled
     assert head_dim % 32 == 0 and 0 <= n_filled <= capacity
     nb = head_dim // 32
-    out = {}
-    for name in ("k", "v"):
-        codes = np.zeros((n_kv_heads, capacity, nb, 3), dtype=np.uint32)
-        scales = np.zeros((n_kv_heads, capacity, nb), dtype=np.uint16)
-        codes[:, :n_filled] = rng.integers(0, 2**32, size=(n_kv_heads, n_filled, nb, 3),
-                                           dtype=np.uint32)
-        scales[:, :n_filled] = _scales(rng, (n_kv_heads, n_filled, nb))
-        out[name + "_codes"] = codes
-        out[name + "_scales"] = scales
-    return KVCache(out["k_codes"], out["k_scales"], out["v_codes"], out["v_scales"],
-                   n_kv_heads, head_dim, capacity, n_filled)
+    k_codes = np.zeros((n_kv_heads, capacity, nb, 3), dtype=np.uint32)
+    k_scales = np.zeros((n_kv_heads, capacity, nb), dtype=np.uint16)
+    k_codes[:, :n_filled] = rng.integers(0, 2**32, size=(n_kv_heads, n_filled, nb, 3),
+                                         dtype=np.uint32)
+    k_scales[:, :n_filled] = _scales(rng, (n_kv_heads, n_filled, nb))
+    ng = (capacity + 31) // 32
+    ng_filled = (n_filled + 31) // 32
+    v_codes = np.zeros((n_kv_heads, ng, head_dim, 3), dtype=np.uint32)
+    v_scales = np.zeros((n_kv_heads, ng, nb, 32), dtype=np.uint16)
+    v_codes[:, :ng_filled] = rng.integers(0, 2**32, size=(n_kv_heads, ng_filled, head_dim, 3),
+                                          dtype=np.uint32)
+    v_scales[:, :ng_filled] = _scales(rng, (n_kv_heads, ng_filled, nb, 32))
+    return KVCache(k_codes, k_scales, v_codes, v_scales, n_kv_heads, head_dim, capacity, n_filled)
 
 
 def make_q(rng: np.random.Generator, n_rows: int, n_q_heads: int, head_dim: int) -> np.ndarray:

@@ -165,14 +165,17 @@ def test_prefill_argument_errors(lib, stvmod):
 def test_kv_pack_argument_errors(lib, stvmod):
     E = stvmod
     f = lib.stv_kv_quant_pack
-    assert f(FAKE, -1, 0, FAKE, FAKE, 4, 256, 100, None) == E.STV_EINVAL
-    assert f(FAKE, 10, 95, FAKE, FAKE, 4, 256, 100, None) == E.STV_ECAPACITY
-    assert f(FAKE, 10, -1, FAKE, FAKE, 4, 256, 100, None) == E.STV_ECAPACITY
-    assert f(FAKE, 10, 0, FAKE, FAKE, 4, 48, 100, None) == E.STV_EINVAL
-    assert f(FAKE, 10, 0, FAKE, FAKE, 0, 256, 100, None) == E.STV_EINVAL
-    assert f(None, 10, 0, FAKE, FAKE, 4, 256, 100, None) == E.STV_EINVAL
-    assert f(FAKE, 0, 100, FAKE, FAKE, 4, 256, 100, None) == E.STV_OK      # nothing to do
-    assert _err(lib) == ""
+    for which in (E.STV_K, E.STV_V):
+        assert f(FAKE, -1, 0, which, FAKE, FAKE, 4, 256, 100, None) == E.STV_EINVAL
+        assert f(FAKE, 10, 95, which, FAKE, FAKE, 4, 256, 100, None) == E.STV_ECAPACITY
+        assert f(FAKE, 10, -1, which, FAKE, FAKE, 4, 256, 100, None) == E.STV_ECAPACITY
+        assert f(FAKE, 10, 0, which, FAKE, FAKE, 4, 48, 100, None) == E.STV_EINVAL
+        assert f(FAKE, 10, 0, which, FAKE, FAKE, 0, 256, 100, None) == E.STV_EINVAL
+        assert f(None, 10, 0, which, FAKE, FAKE, 4, 256, 100, None) == E.STV_EINVAL
+        assert f(FAKE, 0, 100, which, FAKE, FAKE, 4, 256, 100, None) == E.STV_OK   # nothing to do
+        assert _err(lib) == ""
+    assert f(FAKE, 10, 0, 2, FAKE, FAKE, 4, 256, 100, None) == E.STV_EINVAL
+    assert "which" in _err(lib)
 
 
 def test_merge_argument_errors(lib, stvmod):

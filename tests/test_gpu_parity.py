@@ -226,22 +226,28 @@ def test_split_merge_parity(gpu, orc):
 
 
 def test_kv_quant_pack_parity(gpu, orc):
+    """GPU pack of K and V against the oracle's pack, bit for bit, including
+    appends that start and end inside a 32-key group of V."""
     stv, torch = gpu
     rng = np.random.default_rng(160)
-    for hkv, d, cap, n, pos0 in ((4, 256, 300, 64, 17), (1, 64, 50, 7, 43), (2, 128, 4200, 4096, 100)):
+    for hkv, d, cap, n, pos0 in ((4, 256, 300, 64, 17), (1, 64, 50, 7, 43), (2, 128, 4200, 4096, 100),
+                                 (2, 64, 96, 1, 95), (3, 128, 70, 33, 0)):
         x = (rng.standard_normal((n, hkv, d)) * 10.0 ** rng.uniform(-3, 3, (n, hkv, 1))).astype(np.float32)
         x[0, 0, :32] = 0.0                         # zero block
         x[min(1, n - 1), 0, 32:64] = 1e-9          # scale rounds to zero
         x[n - 1, hkv - 1, :32] = 1e6               # scale saturates
-        codes = rng.integers(0, 2**32, size=(hkv, cap, d // 32, 3), dtype=np.uint32)
-        scales = rng.integers(0, 2**16, size=(hkv, cap, d // 32), dtype=np.uint16)
-        cd = torch.from_numpy(codes.view(np.int32)).cuda()
-        sd = torch.from_numpy(scales.view(np.float16)).cuda()
-        stv.kv_quant_pack(torch.from_numpy(x).cuda(), pos0, cd, sd)
+        host = synth.make_kv(rng, hkv, d, cap, cap)     # random old contents everywhere
+        kv = stv.KVCache.from_host(host)
+        xd = torch.from_numpy(x).cuda()
+        stv.kv_quant_pack(xd, pos0, kv, "k")
+        stv.kv_quant_pack(xd, pos0, kv, "v")
         torch.cuda.synchronize()
-        orc.kv_quant_pack(x, pos0, codes, scales)
-        assert np.array_equal(cd.cpu().numpy().view(np.uint32), codes)
-        assert np.array_equal(sd.cpu().numpy().view(np.uint16), scales)
+        orc.kv_quant_pack(x, pos0, host.k_codes, host.k_scales, "k")
+        orc.kv_quant_pack(x, pos0, host.v_codes, host.v_scales, "v")
+        assert np.array_equal(kv.k_codes.cpu().numpy().view(np.uint32), host.k_codes)
+        assert np.array_equal(kv.k_scales.cpu().numpy().view(np.uint16), host.k_scales)
+        assert np.array_equal(kv.v_codes.cpu().numpy().view(np.uint32), host.v_codes)
+        assert np.array_equal(kv.v_scales.cpu().numpy().view(np.uint16), host.v_scales)
 
 
 def test_pack_then_verify_end_to_end(gpu, orc):
@@ -256,12 +262,12 @@ def test_pack_then_verify_end_to_end(gpu, orc):
     q = synth.make_q(rng, T, hq, d)
     mask = synth.ancestor_masks(synth.make_tree_parents(rng, T, 8))
     kv = stv.KVCache.from_host(host)
-    stv.kv_quant_pack(torch.from_numpy(knew).cuda(), L, kv.k_codes, kv.k_scales)
-    stv.kv_quant_pack(torch.from_numpy(vnew).cuda(), L, kv.v_codes, kv.v_scales)
+    stv.kv_quant_pack(torch.from_numpy(knew).cuda(), L, kv, "k")
+    stv.kv_quant_pack(torch.from_numpy(vnew).cuda(), L, kv, "v")
     out = stv.verify_attention(torch.from_numpy(q).cuda(), kv, L, mask)
     torch.cuda.synchronize()
-    orc.kv_quant_pack(knew, L, host.k_codes, host.k_scales)
-    orc.kv_quant_pack(vnew, L, host.v_codes, host.v_scales)
+    orc.kv_quant_pack(knew, L, host.k_codes, host.k_scales, "k")
+    orc.kv_quant_pack(vnew, L, host.v_codes, host.v_scales, "v")
     ref = orc.attention(q, host, L, mask)
     err = _row_err(out.reshape(T * hq, d).cpu().numpy(), ref["out"])
     assert err.max() <= TOL

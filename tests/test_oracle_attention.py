@@ -27,8 +27,19 @@ def _cache(seed, hkv, d, n, cap=None):
 
 
 def _dequant(orc, codes, scales, n):
+    """K (token-major) values [Hkv][n][D] in fp64."""
     c = orc.unpack_codes(codes[:, :n]).astype(np.float64)             # [Hkv][n][D]
     s = np.vectorize(orc.f16_bits_to_f64)(scales[:, :n].astype(np.int64))  # [Hkv][n][NB]
+    return np.repeat(s, 32, axis=-1) * (c - 4.0)
+
+
+def _dequant_v(orc, kv, n):
+    """V (key-transposed groups of 32 keys) values [Hkv][n][D] in fp64."""
+    hkv, ng, d, _ = kv.v_codes.shape
+    c = orc.unpack_codes(kv.v_codes.reshape(hkv, ng, d, 1, 3)).astype(np.float64)  # [Hkv][ng][D][32]
+    c = c.transpose(0, 1, 3, 2).reshape(hkv, ng * 32, d)[:, :n]
+    s = np.vectorize(orc.f16_bits_to_f64)(kv.v_scales.astype(np.int64))           # [Hkv][ng][NB][32]
+    s = s.transpose(0, 1, 3, 2).reshape(hkv, ng * 32, d // 32)[:, :n]
     return np.repeat(s, 32, axis=-1) * (c - 4.0)
 
 
@@ -50,7 +61,7 @@ def _brute(orc, q, kv, L, mask, scale, quantize=True):
     G = hq // kv.n_kv_heads
     n = L + T
     K = _dequant(orc, kv.k_codes, kv.k_scales, n)
-    V = _dequant(orc, kv.v_codes, kv.v_scales, n)
+    V = _dequant_v(orc, kv, n)
     vis = _visible(T, L, mask)
     out = np.zeros((T, hq, d))
     lse = np.zeros((T, hq))
@@ -109,7 +120,7 @@ def test_oracle_matches_brute_force(orc, name, hq, hkv, d, L, T, kind, seed):
     # (exp(2 * max dx) - 1) * max|v^|.
     out_raw, _ = _brute(orc, q, kv, L, mask, scale, quantize=False)
     K = _dequant(orc, kv.k_codes, kv.k_scales, L + T)
-    V = _dequant(orc, kv.v_codes, kv.v_scales, L + T)
+    V = _dequant_v(orc, kv, L + T)
     for r in range(T * hq):
         t, h = divmod(r, hq)
         dx = scale * float(res["sq"][r]) / 2 * np.abs(K[h // G]).sum(-1).max()
@@ -119,24 +130,32 @@ def test_oracle_matches_brute_force(orc, name, hq, hkv, d, L, T, kind, seed):
 
 def test_every_8_row_tree_equals_its_chains(orc):
     """All 7! = 5,040 parent arrays of the 8-row tree: each row must equal
-    the causal computation of its root-to-node path, bit for bit."""
+    the causal computation of its root-to-node path, bit for bit.  The tree
+    rows' K/V enter both caches through the oracle's own quantizer, at L + a
+    in the tree cache and at L + m (m = position on the path) in a chain's."""
     hq, hkv, d, L, T = 2, 1, 32, 24, 8
     rng = np.random.default_rng(11)
-    kv = synth.make_kv(rng, hkv, d, L + T, L + T)
+    base = synth.make_kv(rng, hkv, d, L, L + T)
     q = synth.make_q(rng, T, hq, d)
+    knew = synth.make_new_rows(rng, T, hkv, d)
+    vnew = synth.make_new_rows(rng, T, hkv, d)
     scale = 1.0 / np.sqrt(d)
+
+    def cache_with(rows):
+        c = synth.KVCache(base.k_codes.copy(), base.k_scales.copy(), base.v_codes.copy(),
+                          base.v_scales.copy(), hkv, d, L + T, L + len(rows))
+        orc.kv_quant_pack(knew[rows], L, c.k_codes, c.k_scales, "k")
+        orc.kv_quant_pack(vnew[rows], L, c.v_codes, c.v_scales, "v")
+        return c
+
+    kv = cache_with(list(range(T)))
     chain_cache = {}
 
     def chain(path):
         key = tuple(path)
         if key not in chain_cache:
             k = len(path)
-            ckv = synth.KVCache(kv.k_codes.copy(), kv.k_scales.copy(), kv.v_codes.copy(),
-                                kv.v_scales.copy(), hkv, d, L + T, L + T)
-            for m, a in enumerate(path):
-                for arr, src in ((ckv.k_codes, kv.k_codes), (ckv.k_scales, kv.k_scales),
-                                 (ckv.v_codes, kv.v_codes), (ckv.v_scales, kv.v_scales)):
-                    arr[:, L + m] = src[:, L + a]
+            ckv = cache_with(list(path))
             cq = q[list(path)]
             rows = [(k - 1) * hq + h for h in range(hq)]
             res = orc.attention(cq, ckv, L, None, scale, rows=rows)
@@ -181,7 +200,7 @@ def test_zero_q_row_is_mean_of_visible_values(orc):
     parent = synth.make_tree_parents(rng, T, 6)
     mask = synth.ancestor_masks(parent)
     res = orc.attention(q, kv, L, mask)
-    V = _dequant(orc, kv.v_codes, kv.v_scales, L + T)[0]
+    V = _dequant_v(orc, kv, L + T)[0]
     vis = _visible(T, L, mask)[3]
     want = V[vis].mean(axis=0)
     got = res["out"][3 * hq + 2]
@@ -203,7 +222,7 @@ def test_planted_dominant_key(orc):
     # A random key: scale <= 0.1 and sum_d (c_d - 4) = -32 +- 18, so its logit
     # sits about 250 below and its weight is far under 1e-100.
     res = orc.attention(q, kv, L, np.array([1], dtype=np.uint64), scale=16.0)
-    V = _dequant(orc, kv.v_codes, kv.v_scales, L + T)[0]
+    V = _dequant_v(orc, kv, L + T)[0]
     for h in range(hq):
         assert np.max(np.abs(res["out"][h] - V[jstar])) < 1e-20
 

@@ -178,19 +178,43 @@ def test_kv_quantizer_properties(orc):
 
 def test_kv_quant_pack_writes_only_its_positions(orc):
     rng = np.random.default_rng(4)
-    hkv, d, cap = 2, 64, 20
-    codes = rng.integers(0, 2**32, size=(hkv, cap, d // 32, 3), dtype=np.uint32)
-    scales = rng.integers(0, 2**16, size=(hkv, cap, d // 32), dtype=np.uint16)
-    c0, s0 = codes.copy(), scales.copy()
+    hkv, d, cap = 2, 64, 70
+    nb = d // 32
     x = rng.standard_normal((5, hkv, d)).astype(np.float32)
-    orc.kv_quant_pack(x, 7, codes, scales)
+    pos0 = 29                                   # straddles V groups 0 and 1
+    # K, token-major
+    codes = rng.integers(0, 2**32, size=(hkv, cap, nb, 3), dtype=np.uint32)
+    scales = rng.integers(0, 2**16, size=(hkv, cap, nb), dtype=np.uint16)
+    c0, s0 = codes.copy(), scales.copy()
+    orc.kv_quant_pack(x, pos0, codes, scales, "k")
     keep = np.ones(cap, bool)
-    keep[7:12] = False
+    keep[pos0:pos0 + 5] = False
     assert np.array_equal(codes[:, keep], c0[:, keep])
     assert np.array_equal(scales[:, keep], s0[:, keep])
     for t in range(5):
         for g in range(hkv):
-            for b in range(d // 32):
+            for b in range(nb):
                 w, s = orc.quantize_kv_block(x[t, g, 32 * b:32 * b + 32])
-                assert np.array_equal(codes[g, 7 + t, b], w)
-                assert scales[g, 7 + t, b] == s
+                assert np.array_equal(codes[g, pos0 + t, b], w)
+                assert scales[g, pos0 + t, b] == s
+    # V, key-transposed: element d of key j is code j % 32 of block (j // 32, d)
+    ng = (cap + 31) // 32
+    vcodes = rng.integers(0, 2**32, size=(hkv, ng, d, 3), dtype=np.uint32)
+    vscales = rng.integers(0, 2**16, size=(hkv, ng, nb, 32), dtype=np.uint16)
+    vc0, vs0 = vcodes.copy(), vscales.copy()
+    orc.kv_quant_pack(x, pos0, vcodes, vscales, "v")
+    for g in range(hkv):
+        for j in range(ng * 32):
+            grp, e = divmod(j, 32)
+            new = pos0 <= j < pos0 + 5
+            for b in range(nb):
+                if new:
+                    w, s = orc.quantize_kv_block(x[j - pos0, g, 32 * b:32 * b + 32])
+                    assert vscales[g, grp, b, e] == s
+                    want = orc.unpack_block(w)
+                else:
+                    assert vscales[g, grp, b, e] == vs0[g, grp, b, e]
+                for i in range(32):
+                    got = orc.code_get(vcodes[g, grp, 32 * b + i], e)
+                    ref = want[i] if new else orc.code_get(vc0[g, grp, 32 * b + i], e)
+                    assert got == ref
