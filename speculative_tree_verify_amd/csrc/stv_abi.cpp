@@ -138,7 +138,8 @@ int attention_common(const float *q, int T, int Hq, const stv_kv_layer *kv, int 
 
     hipStream_t st = static_cast<hipStream_t>(stream);
     const bool debug = dbg_logits || dbg_q || dbg_qscale;
-    hipError_t e = stv::launch_attention(a, D, plan.NW, causal, debug, st);
+    hipError_t e = plan.dec ? stv::launch_attention_dec(a, D, causal, debug, st)
+                            : stv::launch_attention(a, D, plan.NW, causal, debug, st);
     if (e != hipSuccess) return fail(STV_EHIP, "attention launch failed: %s", hipGetErrorString(e));
     if (!partials_only && plan.S > 1) {
         e = stv::launch_merge(a.part_o, a.part_lse, plan.S, (int)rows, D, out, out_lse, st);
@@ -151,12 +152,12 @@ int attention_common(const float *q, int T, int Hq, const stv_kv_layer *kv, int 
 
 namespace stv {
 
-long long attention_slots(int D, int NW, bool causal) {
-    // MI355X: 256 CUs; the D = 256 four-wave kernel holds two work-groups per CU.
+long long attention_slots(int D, int NW, bool causal, bool dec) {
+    // MI355X: 256 CUs; the D = 256 four-wave kernels hold two work-groups per CU.
     constexpr long long kFallback = 256LL * 2;
     struct Entry {
         int dev, D, NW;
-        bool causal;
+        bool causal, dec;
         long long slots;
     };
     static std::mutex mu;
@@ -168,16 +169,17 @@ long long attention_slots(int D, int NW, bool causal) {
     }
     std::lock_guard<std::mutex> lock(mu);
     for (const Entry &e : cache)
-        if (e.dev == dev && e.D == D && e.NW == NW && e.causal == causal) return e.slots;
+        if (e.dev == dev && e.D == D && e.NW == NW && e.causal == causal && e.dec == dec)
+            return e.slots;
     int cus = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         cus <= 0) {
         (void)hipGetLastError();
         return kFallback;
     }
-    const int per_cu = attention_wgs_per_cu(D, NW, causal);
+    const int per_cu = dec ? attention_dec_wgs_per_cu(D, causal) : attention_wgs_per_cu(D, NW, causal);
     const long long slots = per_cu > 0 ? (long long)cus * per_cu : kFallback;
-    cache.push_back({dev, D, NW, causal, slots});
+    cache.push_back({dev, D, NW, causal, dec, slots});
     return slots;
 }
 
@@ -185,9 +187,15 @@ Plan make_plan(int T, int Hq, int Hkv, int D, int L, bool causal, int n_splits_r
     Plan p;
     const int G = Hq / Hkv;
     const long long R = (long long)T * G;
-    const long long row_tiles = (R + kRowTile - 1) / kRowTile;
-    p.NW = row_tiles >= 4 ? 4 : (row_tiles >= 2 ? 2 : 1);
-    p.NRG = (int)((row_tiles + p.NW - 1) / p.NW);
+    p.dec = R <= kDecMaxRows;
+    if (p.dec) {
+        p.NW = 4;
+        p.NRG = 1;
+    } else {
+        const long long row_tiles = (R + kRowTile - 1) / kRowTile;
+        p.NW = row_tiles >= 4 ? 4 : (row_tiles >= 2 ? 2 : 1);
+        p.NRG = (int)((row_tiles + p.NW - 1) / p.NW);
+    }
     const long long N = (long long)L + T;
     const long long n_tiles = (N + kKeyTile - 1) / kKeyTile;
     long long S;
@@ -197,7 +205,7 @@ Plan make_plan(int T, int Hq, int Hkv, int D, int L, bool causal, int n_splits_r
         // Fill the device's resident work-group slots exactly once: one
         // round of equal work-groups, no straggling partial round.  Splits
         // keep at least four tiles.
-        const long long slots = attention_slots(D, p.NW, causal);
+        const long long slots = attention_slots(D, p.NW, causal, p.dec);
         const long long groups = (long long)Hkv * p.NRG;
         if (groups < slots) {
             S = slots / groups;

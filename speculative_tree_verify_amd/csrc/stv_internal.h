@@ -33,7 +33,12 @@ struct AttnArgs {
     uint64_t mask[64];   // verify only: ancestor masks of the tree rows
 };
 
+// Query rows per KV head up to which the few-row kernel (16-row MFMA tiles,
+// per-wave key tiles) runs instead of the 32-row tile kernel.
+constexpr int kDecMaxRows = 16;
+
 struct Plan {
+    bool dec;        // few-row kernel (then NW = 4 waves and NRG = 1)
     int NW;          // waves (32-row tiles) per work-group
     int NRG;         // row groups per kv head
     int S;           // context splits
@@ -41,19 +46,22 @@ struct Plan {
     size_t ws_bytes; // workspace for the partials
 };
 
-// Work-groups of the attention kernel that fit on one CU at once, from the
+// Work-groups of the attention kernels that fit on one CU at once, from the
 // runtime's occupancy calculator; 0 when no device answers.
 int attention_wgs_per_cu(int D, int NW, bool causal);
+int attention_dec_wgs_per_cu(int D, bool causal);
 
-// Resident work-group slots of the current device for that kernel variant
+// Resident work-group slots of the current device for a kernel variant
 // (CUs x work-groups per CU); a fixed MI355X figure when no device answers.
-long long attention_slots(int D, int NW, bool causal);
+long long attention_slots(int D, int NW, bool causal, bool dec);
 
 Plan make_plan(int T, int Hq, int Hkv, int D, int L, bool causal, int n_splits_req);
 
 // Launchers return the hipError_t of the launch.
 hipError_t launch_attention(const AttnArgs &a, int D, int NW, bool causal, bool debug,
                             hipStream_t stream);
+hipError_t launch_attention_dec(const AttnArgs &a, int D, bool causal, bool debug,
+                                hipStream_t stream);
 hipError_t launch_merge(const float *part_o, const float *part_lse, int S, int rows, int D,
                         float *out, float *out_lse, hipStream_t stream);
 hipError_t launch_kv_pack(const float *x, int n_tok, int pos0, uint32_t *codes,

@@ -623,6 +623,343 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(const AttnArgs a) {
     }
 }
 
+// ------------------------------------------------- attention, few query rows
+//
+// For at most 16 query rows per KV head (one token, or a few tree rows): the
+// streaming of the cache bounds the call, so every wave works on its own
+// 32-key tiles with no work-group barrier.  A lane quantizes and holds its
+// rows' int8 Q in registers; the wave unpacks its tile into its own LDS
+// region (int8 K chunks, V code chunks, scales) and runs 16x16 MFMAs:
+// Q.K^T with v_mfma_i32_16x16x32_i8 (exact int32 per 32-element block) and
+// P.V with v_mfma_f32_16x16x32_f16, V^ built in registers from the codes by
+// table lookup.  The four waves of a work-group stride over the split's
+// tiles and merge their softmax states through LDS at the end.
+
+typedef int64_t i64_t;
+typedef int32_t i32x4v __attribute__((ext_vector_type(4)));
+
+constexpr int kDecWaves = 4;
+
+template <int D>
+struct DecWaveLds {
+    static constexpr int NB = D / 32;
+    static constexpr int NDT = D / 16;
+    // int8 K, [block][chunk of 8 elements][32 keys + 4 pad][8 bytes]: the A
+    // operand read of lane (key i, chunk q) lands on distinct banks.
+    uint32_t kq[NB][4][36][2];
+    // V codes (one byte per key, codes 0..7), [d-tile][chunk slot][d % 16][8
+    // keys]; chunk q of d-tile dt sits in slot q ^ (dt & 3).
+    uint32_t vc[NDT][4][16][2];
+    float skf[NB][32];
+    alignas(16) uint16_t svs[NB][32];
+};
+
+template <int D, bool CAUSAL, bool DEBUG>
+__global__ __launch_bounds__(kDecWaves * 64) void attn_dec_kernel(const AttnArgs a) {
+    constexpr int NB = D / 32;
+    constexpr int NDT = D / 16;
+    constexpr int KT = kKeyTile;
+    using W = DecWaveLds<D>;
+    static_assert(sizeof(W) >= 16 * D * sizeof(float) + 64 * sizeof(float),
+                  "the merge stages a wave's 16 x D outputs in its tile region");
+    __shared__ __attribute__((aligned(16))) W wl[kDecWaves];
+
+    const int hs = blockIdx.x;
+    const int head = hs / a.S;
+    const int split = hs - head * a.S;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int i16 = lane & 15;          // row of this lane (and MFMA row/column index)
+    const int qc = lane >> 4;           // 8-element chunk / 4-key group of this lane
+    W &my = wl[wave];
+
+    const bool row_ok = i16 < a.R;
+    const int t = row_ok ? i16 / a.G : 0;
+    const int g = row_ok ? i16 - t * a.G : 0;
+    const int flat = t * a.Hq + head * a.G + g;
+
+    const int k0 = split * a.split_len;
+    int k1 = min(a.N, k0 + a.split_len);
+    if (CAUSAL) k1 = min(k1, a.L + (a.R - 1) / a.G + 1);
+    const int vis_from = min(k1, a.L);
+
+    // ---- Q: lane (row i16, chunk qc) holds elements 32b + 8qc + [0, 8) of
+    // every block b, the B operand layout of the 16x16x32 int8 MFMA.
+    i64_t qop[NB];
+    float sq;
+    {
+        const float *qrow = a.q + (size_t)flat * D + 8 * qc;
+        float amax = 0.0f;
+        if (row_ok) {
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const f32x4 v = *reinterpret_cast<const f32x4 *>(qrow + 32 * b + 4 * j);
+                    amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+                }
+        }
+        amax = fmaxf(amax, __shfl_xor(amax, 16));
+        amax = max_halves(amax);
+        const float inv = amax > 0.0f ? 127.0f / amax : 0.0f;
+        sq = amax / 127.0f;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            uint32_t w2[2] = {0u, 0u};
+            if (row_ok) {
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const f32x4 v = *reinterpret_cast<const f32x4 *>(qrow + 32 * b + 4 * j);
+                    const float e[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        float r = rintf(e[i] * inv);
+                        r = fminf(fmaxf(r, -127.0f), 127.0f);
+                        w2[j] |= ((uint32_t)(int)r & 0xFFu) << (8 * i);
+                    }
+                }
+            }
+            qop[b] = (i64_t)((uint64_t)w2[0] | ((uint64_t)w2[1] << 32));
+        }
+        if (DEBUG && split == 0 && wave == 0 && row_ok) {
+            if (a.dbg_q) {
+#pragma unroll
+                for (int b = 0; b < NB; ++b)
+                    *reinterpret_cast<i64_t *>(a.dbg_q + (size_t)flat * D + 32 * b + 8 * qc) = qop[b];
+            }
+            if (a.dbg_qscale && qc == 0) a.dbg_qscale[flat] = sq;
+        }
+    }
+    const float c_row = sq * a.scale_log2;
+    uint64_t mrow = 0;
+    if (!CAUSAL) {
+        for (int tt = 0; tt < a.T; ++tt)
+            if (tt == t) mrow = a.mask[tt];
+    }
+
+    f32x4 oacc[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) oacc[dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    float m_run = -INFINITY;
+    float l_run = 0.0f;
+
+    // ---- per-wave register prefetch of one tile: 4 K items, 4 V rows and
+    // 4 V scales per lane
+    constexpr int PER = (KT * NB) / 64;     // = D / 64
+    uint32_t rk[PER][3], rv[PER][3];
+    uint16_t rks[PER], rvs[PER];
+    const size_t head_k = (size_t)head * a.cap;
+    auto load_tile = [&](int kb) {
+        const size_t grp_base = (size_t)head * a.ngroups + (size_t)(kb / KT);
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int item = lane + 64 * i;
+            const int key = item & 31, b = item >> 5;
+            rk[i][0] = rk[i][1] = rk[i][2] = 0u;
+            rks[i] = 0;
+            if (kb + key < k1) {
+                const size_t blk = (head_k + kb + key) * NB + b;
+                const uint32_t *src = a.kc + blk * 3;
+                rk[i][0] = src[0];
+                rk[i][1] = src[1];
+                rk[i][2] = src[2];
+                rks[i] = a.ks[blk];
+            }
+            const int d = item;
+            const uint32_t *vsrc = a.vc + (grp_base * D + d) * 3;
+            rv[i][0] = vsrc[0];
+            rv[i][1] = vsrc[1];
+            rv[i][2] = vsrc[2];
+            // scale entry (block b, key): keys past the range get 0
+            rvs[i] = kb + key < k1 ? a.vs[grp_base * D + item] : (uint16_t)0;
+        }
+    };
+
+    const int stride = kDecWaves * KT;
+    int kb = k0 + wave * KT;
+    if (kb < k1) load_tile(kb);
+    for (; kb < k1; kb += stride) {
+        // ---- unpack the held tile into this wave's LDS region
+        wave_lds_sync();
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int item = lane + 64 * i;
+            const int key = item & 31, b = item >> 5;
+            uint32_t o[8];
+            unpack_bytes(rk[i][0], rk[i][1], rk[i][2], o);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                my.kq[b][c][key][0] = codes_to_i8(o[2 * c]);
+                my.kq[b][c][key][1] = codes_to_i8(o[2 * c + 1]);
+            }
+            my.skf[b][key] = half_bits_to_float(rks[i]);
+            const int d = item, dt = d >> 4;
+            unpack_bytes(rv[i][0], rv[i][1], rv[i][2], o);    // keys 4qq..4qq+3 in o[qq]
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                my.vc[dt][c ^ (dt & 3)][d & 15][0] = o[2 * c];
+                my.vc[dt][c ^ (dt & 3)][d & 15][1] = o[2 * c + 1];
+            }
+            my.svs[b][key] = rvs[i];
+        }
+        wave_lds_sync();
+        if (kb + stride < k1) load_tile(kb + stride);
+
+        // ---- Q.K^T: two 16-key halves per block; lane (i16, qc) gets keys
+        // 8qc + 4kh + [0, 4) for half kh, so its 8 logits are keys 8qc + [0, 8)
+        float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        const int krow0 = 8 * (i16 >> 2) + (i16 & 3);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            const f32x4 sk0 = *reinterpret_cast<const f32x4 *>(&my.skf[b][8 * qc]);
+            const f32x4 sk1 = *reinterpret_cast<const f32x4 *>(&my.skf[b][8 * qc + 4]);
+#pragma unroll
+            for (int kh = 0; kh < 2; ++kh) {
+                const i64_t kop = *reinterpret_cast<const i64_t *>(&my.kq[b][qc][krow0 + 4 * kh][0]);
+                const i32x4v sres = __builtin_amdgcn_mfma_i32_16x16x32_i8(kop, qop[b], i32x4v{}, 0, 0, 0);
+                const f32x4 sk = kh ? sk1 : sk0;
+                acc[4 * kh + 0] = fmaf(sk.x, (float)sres[0], acc[4 * kh + 0]);
+                acc[4 * kh + 1] = fmaf(sk.y, (float)sres[1], acc[4 * kh + 1]);
+                acc[4 * kh + 2] = fmaf(sk.z, (float)sres[2], acc[4 * kh + 2]);
+                acc[4 * kh + 3] = fmaf(sk.w, (float)sres[3], acc[4 * kh + 3]);
+                if (DEBUG && a.dbg_logits && row_ok) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int key = kb + 8 * qc + 4 * kh + e;
+                        if (key < k1) a.dbg_logits[((size_t)flat * a.N + key) * NB + b] = sres[e];
+                    }
+                }
+            }
+        }
+
+        // ---- mask, online softmax in base 2 (running max moves by > 8 only)
+        const bool masked = kb + KT > vis_from;
+        if (masked) {
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                const int key = kb + 8 * qc + r;
+                bool vis = key < k1;
+                if (vis && key >= a.L) {
+                    const int u = key - a.L;
+                    vis = CAUSAL ? (u <= t) : (((mrow >> u) & 1ull) != 0ull);
+                }
+                if (!vis) acc[r] = -INFINITY;
+            }
+        }
+        float amax = acc[0];
+#pragma unroll
+        for (int r = 1; r < 8; ++r) amax = fmaxf(amax, acc[r]);
+        amax = fmaxf(amax, __shfl_xor(amax, 16));
+        amax = max_halves(amax);
+        const float tmax = amax == -INFINITY ? -INFINITY : amax * c_row;
+        const float m_new = tmax > m_run + 8.0f ? tmax : m_run;
+        if (__any(m_new != m_run)) {
+            const float alpha = m_new != m_run ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+            l_run *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) oacc[dt] *= alpha;
+            m_run = m_new;
+        }
+        const float mm = m_run == -INFINITY ? 0.0f : m_run;
+        f16x8 pk;
+        float psum = 0.0f;
+        const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+            const float p0 = acc[e] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(fmaf(acc[e], c_row, -mm));
+            const float p1 = acc[e + 1] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(fmaf(acc[e + 1], c_row, -mm));
+            const f16x2 h2 = __builtin_convertvector(f32x2{p0, p1}, f16x2);
+            pk[e] = h2.x;
+            pk[e + 1] = h2.y;
+            psum = __builtin_amdgcn_fdot2(h2, ones, psum, false);
+        }
+        l_run += psum;
+
+        // ---- P.V: A operand = V^T rows (d = 16dt + i16, keys 8qc + [0, 8)),
+        // B operand = P (keys 8qc + [0, 8), row i16)
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+            const uint32_t *cw = my.vc[dt][qc ^ (dt & 3)][i16];
+            const uint32_t w0 = cw[0], w1 = cw[1];
+            // Scales of keys 8qc + [0, 8), two per word.  Each word goes
+            // through a scalar: clang bit-casts a vector component
+            // (v.y, v.z, ...) as if it were component 0.
+            const u32x4 svw = *reinterpret_cast<const u32x4 *>(&my.svs[dt >> 1][8 * qc]);
+            const uint32_t s01 = svw[0], s23 = svw[1], s45 = svw[2], s67 = svw[3];
+            const uint32_t ta = __builtin_amdgcn_perm(kC4Hi, kC4Lo, w0);
+            const uint32_t tb = __builtin_amdgcn_perm(kC4Hi, kC4Lo, w1);
+            const f16x2 v0 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(ta, ta, 0x010C000Cu)) *
+                             __builtin_bit_cast(f16x2, s01);
+            const f16x2 v1 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(ta, ta, 0x030C020Cu)) *
+                             __builtin_bit_cast(f16x2, s23);
+            const f16x2 v2 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(tb, tb, 0x010C000Cu)) *
+                             __builtin_bit_cast(f16x2, s45);
+            const f16x2 v3 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(tb, tb, 0x030C020Cu)) *
+                             __builtin_bit_cast(f16x2, s67);
+            const f16x8 vop = {v0.x, v0.y, v1.x, v1.y, v2.x, v2.y, v3.x, v3.y};
+            oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop, pk, oacc[dt], 0, 0, 0);
+        }
+        __builtin_amdgcn_s_setprio(0);
+    }
+
+    // ---- merge the four waves' softmax states through LDS, in wave order
+    float l_row = l_run + __shfl_xor(l_run, 16);
+    l_row = sum_halves(l_row);
+    __syncthreads();                                   // tile regions are free now
+    float *ostage = reinterpret_cast<float *>(&my);    // [16 rows][D], then m[16], l[16]
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+        *reinterpret_cast<f32x4 *>(ostage + i16 * D + 16 * dt + 4 * qc) = oacc[dt];
+    if (qc == 0) {
+        ostage[16 * D + i16] = m_run;
+        ostage[16 * D + 16 + i16] = l_row;
+    }
+    __syncthreads();
+    // thread -> (row r, 16 consecutive elements)
+    const int r = tid >> 4;
+    const int c0 = (tid & 15) * (D / 16);
+    if (r >= a.R) return;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w)
+        M = fmaxf(M, reinterpret_cast<const float *>(&wl[w])[16 * D + r]);
+    float wt[kDecWaves];
+    float Lsum = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) {
+        const float *st = reinterpret_cast<const float *>(&wl[w]);
+        const float mw = st[16 * D + r];
+        wt[w] = (M == -INFINITY || mw == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mw - M);
+        Lsum += wt[w] * st[16 * D + 16 + r];
+    }
+    const float inv_l = Lsum > 0.0f ? 1.0f / Lsum : 0.0f;
+    const float lse = Lsum > 0.0f ? (M + log2f(Lsum)) * 0.69314718055994531f : -INFINITY;
+    const int tr = r / a.G, gr = r - tr * a.G;
+    const int flat_r = tr * a.Hq + head * a.G + gr;
+    const size_t rows_total = (size_t)a.T * a.Hq;
+    const bool partial = a.part_o != nullptr;
+    float *dst = (partial ? a.part_o + (size_t)split * rows_total * D : a.out) + (size_t)flat_r * D;
+#pragma unroll
+    for (int j = 0; j < D / 16; j += 4) {
+        f32x4 o = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int w = 0; w < kDecWaves; ++w) {
+            const f32x4 v = *reinterpret_cast<const f32x4 *>(
+                reinterpret_cast<const float *>(&wl[w]) + r * D + c0 + j);
+            o += wt[w] * v;
+        }
+        *reinterpret_cast<f32x4 *>(dst + c0 + j) = o * inv_l;
+    }
+    if ((tid & 15) == 0) {
+        if (partial)
+            a.part_lse[(size_t)split * rows_total + flat_r] = lse;
+        else if (a.out_lse)
+            a.out_lse[flat_r] = lse;
+    }
+}
+
 // ---------------------------------------------------------------- merge
 
 // One work-group per output row.  The weights exp(lse_s - M) come from a
@@ -769,7 +1106,49 @@ int occupancy_d(int NW, bool causal) {
     }
 }
 
+template <int D, bool CAUSAL, bool DEBUG>
+hipError_t launch_dec_t(const AttnArgs &a, hipStream_t stream) {
+    hipLaunchKernelGGL((attn_dec_kernel<D, CAUSAL, DEBUG>), dim3(a.Hkv * a.S),
+                       dim3(kDecWaves * 64), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_dec_d(const AttnArgs &a, bool causal, bool debug, hipStream_t s) {
+    if (causal) return debug ? launch_dec_t<D, true, true>(a, s) : launch_dec_t<D, true, false>(a, s);
+    return debug ? launch_dec_t<D, false, true>(a, s) : launch_dec_t<D, false, false>(a, s);
+}
+
+template <int D, bool CAUSAL>
+int occupancy_dec_t() {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &n, reinterpret_cast<const void *>(&attn_dec_kernel<D, CAUSAL, false>), kDecWaves * 64,
+            0) != hipSuccess)
+        return 0;
+    return n;
+}
+
 }  // namespace
+
+int attention_dec_wgs_per_cu(int D, bool causal) {
+    switch (D) {
+        case 64: return causal ? occupancy_dec_t<64, true>() : occupancy_dec_t<64, false>();
+        case 128: return causal ? occupancy_dec_t<128, true>() : occupancy_dec_t<128, false>();
+        case 256: return causal ? occupancy_dec_t<256, true>() : occupancy_dec_t<256, false>();
+        default: return 0;
+    }
+}
+
+hipError_t launch_attention_dec(const AttnArgs &a, int D, bool causal, bool debug,
+                                hipStream_t stream) {
+    switch (D) {
+        case 64: return launch_dec_d<64>(a, causal, debug, stream);
+        case 128: return launch_dec_d<128>(a, causal, debug, stream);
+        case 256: return launch_dec_d<256>(a, causal, debug, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
 
 int attention_wgs_per_cu(int D, int NW, bool causal) {
     switch (D) {
