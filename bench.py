@@ -193,6 +193,9 @@ def main():
                     help="comma-separated extra workloads ('' for none)")
     ap.add_argument("--extra-steps", type=int, default=10)
     ap.add_argument("--cpu-rows", type=int, default=128, help="oracle sample size (0: skip)")
+    ap.add_argument("--calib-copy-mb", type=int, default=0,
+                    help="after the run, launch an elementwise copy (torch.neg) of this many MiB "
+                         "three times: the reference for scaling HBM byte counters")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -255,6 +258,20 @@ def main():
         extra[name] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in se.items()}
     if extra:
         line["extra"] = extra
+    if args.calib_copy_mb > 0:
+        del wl
+        torch.cuda.empty_cache()
+        n = args.calib_copy_mb * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        line["calib_copy"] = {"kernel": "torch.neg (fp32, contiguous)", "read_bytes": 4 * n,
+                              "write_bytes": 4 * n}
+        del src, dst
+        torch.cuda.empty_cache()
+        wl = None
     if args.cpu_rows > 0:
         del wl
         torch.cuda.empty_cache()

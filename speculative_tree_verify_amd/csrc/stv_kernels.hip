@@ -29,6 +29,10 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
+
+// Word 3 of a raw buffer descriptor on gfx9: 32-bit data format, no swizzle.
+constexpr int kBufWord3 = 0x00020000;
 
 // ------------------------------------------------------------ 3-bit blocks
 // Byte-plane layout: byte i of word qq' below holds the code of element
@@ -54,10 +58,12 @@ __device__ __forceinline__ void pack_bytes(const uint32_t o[8], uint32_t &w0, ui
     w2 = o[4] | (o[5] << 3) | ((o[6] & mh) << 4) | ((o[7] & mh) << 5);
 }
 
-// Four codes c in [0, 7] (one per byte) -> four int8 values c - 4.  Setting
-// bit 7 of every byte first keeps the byte-wise subtraction borrow-free.
+// Four codes c in [0, 7] (one per byte) -> four int8 values c - 4, by one
+// v_perm_b32 byte select from the table {-4, -3, -2, -1, 0, 1, 2, 3}.
+constexpr uint32_t kI8Lo = 0xFFFEFDFCu;     // codes 0..3 -> -4..-1
+constexpr uint32_t kI8Hi = 0x03020100u;     // codes 4..7 ->  0..3
 __device__ __forceinline__ uint32_t codes_to_i8(uint32_t o) {
-    return ((o | 0x80808080u) - 0x04040404u) ^ 0x80808080u;
+    return __builtin_amdgcn_perm(kI8Hi, kI8Lo, o);
 }
 
 // High bytes of the binary16 values c - 4 for c = 0..7 (-4, -3, -2, -1, 0,
@@ -631,9 +637,11 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(const AttnArgs a) {
 // rows' int8 Q in registers; the wave unpacks its tile into its own LDS
 // region (int8 K chunks, V code chunks, scales) and runs 16x16 MFMAs:
 // Q.K^T with v_mfma_i32_16x16x32_i8 (exact int32 per 32-element block) and
-// P.V with v_mfma_f32_16x16x32_f16, V^ built in registers from the codes by
-// table lookup.  The four waves of a work-group stride over the split's
-// tiles and merge their softmax states through LDS at the end.
+// P.V with v_mfma_f32_16x16x32_f16.  P.V takes the V codes' values c - 4
+// (exact in fp16, built by table lookup) as one operand and P times the V
+// scales of each 32-element block as the other, so sv * (c - 4) is never
+// formed.  The four waves of a work-group stride over the split's tiles and
+// merge their softmax states through LDS at the end.
 
 typedef int64_t i64_t;
 typedef int32_t i32x4v __attribute__((ext_vector_type(4)));
@@ -669,7 +677,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_dec_kernel(const AttnArgs
     const int split = hs - head * a.S;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: tile bases stay scalar
     const int i16 = lane & 15;          // row of this lane (and MFMA row/column index)
     const int qc = lane >> 4;           // 8-element chunk / 4-key group of this lane
     W &my = wl[wave];
@@ -747,64 +755,88 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_dec_kernel(const AttnArgs
     // ---- per-wave register prefetch of one tile: 4 K items, 4 V rows and
     // 4 V scales per lane
     constexpr int PER = (KT * NB) / 64;     // = D / 64
-    uint32_t rk[PER][3], rv[PER][3];
-    uint16_t rks[PER], rvs[PER];
+    struct TileRegs {
+        uint32_t k[PER][3], v[PER][3];
+        uint16_t ks[PER], vs[PER];
+    };
+    // Loads go through buffer descriptors whose base is the tile and whose
+    // size ends at the split's last key, so entries past it read as zero
+    // (code 0 with scale 0 for K) without a per-lane branch.
     const size_t head_k = (size_t)head * a.cap;
-    auto load_tile = [&](int kb) {
-        const size_t grp_base = (size_t)head * a.ngroups + (size_t)(kb / KT);
+    // A tile at or past k1 gets descriptors of size 0 (based at the split's
+    // first tile): its loads read nothing and return zeros.  Issuing them
+    // anyway keeps the number of loads in flight the same on every path, so
+    // the waits for one register set never wait for the other.
+    auto load_tile = [&](TileRegs &r, int kb) {
+        const bool valid = kb < k1;
+        const int kt = valid ? kb : k0;
+        const int nk = valid ? min(KT, k1 - kb) : 0;
+        const int vbytes = valid ? D * 12 : 0, vsbytes = valid ? D * 2 : 0;
+        const size_t grp = (size_t)head * a.ngroups + (size_t)(kt / KT);
+        const __amdgpu_buffer_rsrc_t rsk = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint32_t *>(a.kc + (head_k + kt) * NB * 3), (short)0, nk * NB * 12, kBufWord3);
+        const __amdgpu_buffer_rsrc_t rss = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t *>(a.ks + (head_k + kt) * NB), (short)0, nk * NB * 2, kBufWord3);
+        const __amdgpu_buffer_rsrc_t rsv = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint32_t *>(a.vc + grp * D * 3), (short)0, vbytes, kBufWord3);
+        const __amdgpu_buffer_rsrc_t rsvs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t *>(a.vs + grp * D), (short)0, vsbytes, kBufWord3);
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
+            // K: item = (key item % 32, block item / 32), so that the LDS
+            // writes of a load's 32 keys fall on distinct banks.  V: row
+            // d = item of the key-transposed group, and scale entry item =
+            // (block item / 32, key item % 32); the unpack zeroes the scales
+            // past the key range (no use of loaded data here, so the loads
+            // stay in flight).
             const int item = lane + 64 * i;
-            const int key = item & 31, b = item >> 5;
-            rk[i][0] = rk[i][1] = rk[i][2] = 0u;
-            rks[i] = 0;
-            if (kb + key < k1) {
-                const size_t blk = (head_k + kb + key) * NB + b;
-                const uint32_t *src = a.kc + blk * 3;
-                rk[i][0] = src[0];
-                rk[i][1] = src[1];
-                rk[i][2] = src[2];
-                rks[i] = a.ks[blk];
-            }
-            const int d = item;
-            const uint32_t *vsrc = a.vc + (grp_base * D + d) * 3;
-            rv[i][0] = vsrc[0];
-            rv[i][1] = vsrc[1];
-            rv[i][2] = vsrc[2];
-            // scale entry (block b, key): keys past the range get 0
-            rvs[i] = kb + key < k1 ? a.vs[grp_base * D + item] : (uint16_t)0;
+            const int koff = (item & 31) * NB + (item >> 5);
+            const u32x3 kw = __builtin_amdgcn_raw_buffer_load_b96(rsk, koff * 12, 0, 0);
+            r.k[i][0] = kw[0];
+            r.k[i][1] = kw[1];
+            r.k[i][2] = kw[2];
+            r.ks[i] = __builtin_amdgcn_raw_buffer_load_b16(rss, koff * 2, 0, 0);
+            const u32x3 vw = __builtin_amdgcn_raw_buffer_load_b96(rsv, item * 12, 0, 0);
+            r.v[i][0] = vw[0];
+            r.v[i][1] = vw[1];
+            r.v[i][2] = vw[2];
+            r.vs[i] = __builtin_amdgcn_raw_buffer_load_b16(rsvs, item * 2, 0, 0);
         }
     };
 
+    // Each wave keeps two tiles in flight: tile i is unpacked from one
+    // register set while the other set's loads (tile i + 1) are outstanding,
+    // and the freed set is refilled with tile i + 2 right after the unpack.
     const int stride = kDecWaves * KT;
-    int kb = k0 + wave * KT;
-    if (kb < k1) load_tile(kb);
-    for (; kb < k1; kb += stride) {
+    auto process = [&](TileRegs &r, int kb) {
         // ---- unpack the held tile into this wave's LDS region
+        const int nk = min(KT, k1 - kb);
         wave_lds_sync();
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
             const int item = lane + 64 * i;
-            const int key = item & 31, b = item >> 5;
+            const int kkey = item & 31, kbk = item >> 5;
             uint32_t o[8];
-            unpack_bytes(rk[i][0], rk[i][1], rk[i][2], o);
+            unpack_bytes(r.k[i][0], r.k[i][1], r.k[i][2], o);
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                my.kq[b][c][key][0] = codes_to_i8(o[2 * c]);
-                my.kq[b][c][key][1] = codes_to_i8(o[2 * c + 1]);
+                my.kq[kbk][c][kkey][0] = codes_to_i8(o[2 * c]);
+                my.kq[kbk][c][kkey][1] = codes_to_i8(o[2 * c + 1]);
             }
-            my.skf[b][key] = half_bits_to_float(rks[i]);
+            my.skf[kbk][kkey] = half_bits_to_float(r.ks[i]);
+            const int key = item & 31, b = item >> 5;
             const int d = item, dt = d >> 4;
-            unpack_bytes(rv[i][0], rv[i][1], rv[i][2], o);    // keys 4qq..4qq+3 in o[qq]
+            unpack_bytes(r.v[i][0], r.v[i][1], r.v[i][2], o);    // keys 4qq..4qq+3 in o[qq]
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 my.vc[dt][c ^ (dt & 3)][d & 15][0] = o[2 * c];
                 my.vc[dt][c ^ (dt & 3)][d & 15][1] = o[2 * c + 1];
             }
-            my.svs[b][key] = rvs[i];
+            my.svs[b][key] = key < nk ? r.vs[i] : (uint16_t)0;
         }
         wave_lds_sync();
-        if (kb + stride < k1) load_tile(kb + stride);
+        // the registers are free again: fetch the tile two strides ahead
+        load_tile(r, kb + 2 * stride);
 
         // ---- Q.K^T: two 16-key halves per block; lane (i16, qc) gets keys
         // 8qc + 4kh + [0, 4) for half kh, so its 8 logits are keys 8qc + [0, 8)
@@ -876,32 +908,47 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_dec_kernel(const AttnArgs
         }
         l_run += psum;
 
-        // ---- P.V: A operand = V^T rows (d = 16dt + i16, keys 8qc + [0, 8)),
-        // B operand = P (keys 8qc + [0, 8), row i16)
+        // ---- P.V: A operand = the codes' values c - 4 (exact in fp16) of
+        // V^T rows d = 16dt + i16, keys 8qc + [0, 8); B operand = P times the
+        // V scales of those keys in block d / 32 (keys 8qc + [0, 8), row i16).
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-            const uint32_t *cw = my.vc[dt][qc ^ (dt & 3)][i16];
-            const uint32_t w0 = cw[0], w1 = cw[1];
+        for (int bb = 0; bb < NB; ++bb) {
             // Scales of keys 8qc + [0, 8), two per word.  Each word goes
             // through a scalar: clang bit-casts a vector component
             // (v.y, v.z, ...) as if it were component 0.
-            const u32x4 svw = *reinterpret_cast<const u32x4 *>(&my.svs[dt >> 1][8 * qc]);
+            const u32x4 svw = *reinterpret_cast<const u32x4 *>(&my.svs[bb][8 * qc]);
             const uint32_t s01 = svw[0], s23 = svw[1], s45 = svw[2], s67 = svw[3];
-            const uint32_t ta = __builtin_amdgcn_perm(kC4Hi, kC4Lo, w0);
-            const uint32_t tb = __builtin_amdgcn_perm(kC4Hi, kC4Lo, w1);
-            const f16x2 v0 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(ta, ta, 0x010C000Cu)) *
-                             __builtin_bit_cast(f16x2, s01);
-            const f16x2 v1 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(ta, ta, 0x030C020Cu)) *
-                             __builtin_bit_cast(f16x2, s23);
-            const f16x2 v2 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(tb, tb, 0x010C000Cu)) *
-                             __builtin_bit_cast(f16x2, s45);
-            const f16x2 v3 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(tb, tb, 0x030C020Cu)) *
-                             __builtin_bit_cast(f16x2, s67);
-            const f16x8 vop = {v0.x, v0.y, v1.x, v1.y, v2.x, v2.y, v3.x, v3.y};
-            oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop, pk, oacc[dt], 0, 0, 0);
+            const f16x2 p01 = f16x2{pk[0], pk[1]} * __builtin_bit_cast(f16x2, s01);
+            const f16x2 p23 = f16x2{pk[2], pk[3]} * __builtin_bit_cast(f16x2, s23);
+            const f16x2 p45 = f16x2{pk[4], pk[5]} * __builtin_bit_cast(f16x2, s45);
+            const f16x2 p67 = f16x2{pk[6], pk[7]} * __builtin_bit_cast(f16x2, s67);
+            const f16x8 pb = {p01.x, p01.y, p23.x, p23.y, p45.x, p45.y, p67.x, p67.y};
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int dt = 2 * bb + h;
+                const uint32_t *cw = my.vc[dt][qc ^ (dt & 3)][i16];
+                const uint32_t w0 = cw[0], w1 = cw[1];
+                const uint32_t ta = __builtin_amdgcn_perm(kC4Hi, kC4Lo, w0);
+                const uint32_t tb = __builtin_amdgcn_perm(kC4Hi, kC4Lo, w1);
+                const uint32_t v0 = __builtin_amdgcn_perm(ta, ta, 0x010C000Cu);
+                const uint32_t v1 = __builtin_amdgcn_perm(ta, ta, 0x030C020Cu);
+                const uint32_t v2 = __builtin_amdgcn_perm(tb, tb, 0x010C000Cu);
+                const uint32_t v3 = __builtin_amdgcn_perm(tb, tb, 0x030C020Cu);
+                const f16x8 vop = __builtin_bit_cast(f16x8, u32x4{v0, v1, v2, v3});
+                oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop, pb, oacc[dt], 0, 0, 0);
+            }
         }
         __builtin_amdgcn_s_setprio(0);
+    };
+    TileRegs r0, r1;
+    const int kb0 = k0 + wave * KT;
+    load_tile(r0, kb0);
+    load_tile(r1, kb0 + stride);
+    for (int kb = kb0; kb < k1; kb += 2 * stride) {
+        process(r0, kb);
+        if (kb + stride >= k1) break;
+        process(r1, kb + stride);
     }
 
     // ---- merge the four waves' softmax states through LDS, in wave order
@@ -963,13 +1010,17 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_dec_kernel(const AttnArgs
 // ---------------------------------------------------------------- merge
 
 // One work-group per output row.  The weights exp(lse_s - M) come from a
-// block-wide max and sum; then thread (g, c) accumulates element c over the
-// splits s = g, g + G, ... and the G partial sums are added in order g = 0, 1,
-// ... through LDS, so the result does not depend on timing.
-constexpr int kMergeThreads = 256;
+// block-wide max and sum; then thread (g, c) accumulates column c over the
+// splits s = g, g + G, g + 2G, ... (four loads in flight), and the G partial
+// sums are added in order g = 0, 1, ... through LDS, so the result does not
+// depend on timing.  G grows with S so that few rows with many splits still
+// keep many loads in flight.
+constexpr int kMergeMaxThreads = 1024;
+constexpr int kMergeWeights = 1024;      // weights cached in LDS for s < this
 
 __device__ __forceinline__ float block_reduce(float v, float *red, bool is_max) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int n_waves = blockDim.x >> 6;
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
         const float w = __shfl_xor(v, o);
@@ -979,84 +1030,83 @@ __device__ __forceinline__ float block_reduce(float v, float *red, bool is_max) 
     if (lane == 0) red[wave] = v;
     __syncthreads();
     v = red[0];
-    for (int i = 1; i < kMergeThreads / 64; ++i) v = is_max ? fmaxf(v, red[i]) : v + red[i];
+    for (int i = 1; i < n_waves; ++i) v = is_max ? fmaxf(v, red[i]) : v + red[i];
     return v;
 }
 
-__global__ __launch_bounds__(kMergeThreads) void merge_kernel(
+__device__ __forceinline__ float merge_weight(const float *part_lse, const float *wgt, int s,
+                                              int rows, int row, float M) {
+    if (s < kMergeWeights) return wgt[s];
+    const float ls = part_lse[(size_t)s * rows + row];
+    return ls == -INFINITY ? 0.0f : expf(ls - M);
+}
+
+__global__ __launch_bounds__(kMergeMaxThreads) void merge_kernel(
     const float *__restrict__ part_o, const float *__restrict__ part_lse, int S, int rows, int D,
-    float *__restrict__ out, float *__restrict__ out_lse) {
-    __shared__ float red[kMergeThreads / 64];
-    __shared__ float wgt[1024];
-    __shared__ float acc_lds[kMergeThreads * 4];
+    int G, float *__restrict__ out, float *__restrict__ out_lse) {
+    __shared__ float red[kMergeMaxThreads / 64];
+    __shared__ float wgt[kMergeWeights];
+    __shared__ f32x4 acc_lds[kMergeMaxThreads];
     const int row = blockIdx.x;
     const int tid = threadIdx.x;
+    const int nt = blockDim.x;
     float M = -INFINITY;
-    for (int s = tid; s < S; s += kMergeThreads) M = fmaxf(M, part_lse[(size_t)s * rows + row]);
+    for (int s = tid; s < S; s += nt) M = fmaxf(M, part_lse[(size_t)s * rows + row]);
     M = block_reduce(M, red, true);
     float W = 0.0f;
     if (M != -INFINITY)
-        for (int s = tid; s < S; s += kMergeThreads) {
+        for (int s = tid; s < S; s += nt) {
             const float ls = part_lse[(size_t)s * rows + row];
             const float w = ls == -INFINITY ? 0.0f : expf(ls - M);
             W += w;
-            if (s < 1024) wgt[s] = w;
+            if (s < kMergeWeights) wgt[s] = w;
         }
     W = block_reduce(W, red, false);
     const float invW = W > 0.0f ? 1.0f / W : 0.0f;
     if (out_lse && tid == 0) out_lse[row] = M == -INFINITY ? -INFINITY : M + logf(W);
-
-    const bool vec = (D & 3) == 0 && D <= 4 * kMergeThreads;
-    const int C = vec ? D / 4 : D;                     // columns (float4 or float)
-    const int G = vec ? kMergeThreads / C : 1;         // split groups
-    const int g = tid / C, c = tid - (tid / C) * C;
     __syncthreads();
     if (M == -INFINITY) {
-        for (int d = tid; d < D; d += kMergeThreads) out[(size_t)row * D + d] = 0.0f;
+        for (int d = tid; d < D; d += nt) out[(size_t)row * D + d] = 0.0f;
         return;
     }
-    if (vec) {
+    if ((D & 3) == 0) {
+        // An empty split (lse = -inf) has weight 0 and an all-zero partial.
+        const int C = D / 4;
+        const int g = tid / C, c = tid - (tid / C) * C;
         f32x4 o = {0.0f, 0.0f, 0.0f, 0.0f};
         if (g < G) {
-            for (int s = g; s < S; s += G) {
-                const float w = s < 1024 ? wgt[s]
-                                         : (part_lse[(size_t)s * rows + row] == -INFINITY
-                                                ? 0.0f
-                                                : expf(part_lse[(size_t)s * rows + row] - M));
-                if (w != 0.0f) {
-                    const f32x4 v = *reinterpret_cast<const f32x4 *>(
-                        part_o + ((size_t)s * rows + row) * D + 4 * c);
-                    o.x += w * v.x;
-                    o.y += w * v.y;
-                    o.z += w * v.z;
-                    o.w += w * v.w;
+            const float *col = part_o + (size_t)row * D + 4 * c;
+            const size_t split_stride = (size_t)rows * D;
+            for (int s0 = g; s0 < S; s0 += 4 * G) {
+                f32x4 v[4];
+                float w[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int s = s0 + u * G;
+                    v[u] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                    w[u] = 0.0f;
+                    if (s < S) {
+                        v[u] = *reinterpret_cast<const f32x4 *>(col + (size_t)s * split_stride);
+                        w[u] = merge_weight(part_lse, wgt, s, rows, row, M);
+                    }
                 }
+#pragma unroll
+                for (int u = 0; u < 4; ++u) o += w[u] * v[u];
             }
-            *reinterpret_cast<f32x4 *>(acc_lds + 4 * tid) = o;
         }
+        acc_lds[tid] = o;
         __syncthreads();
         if (g == 0) {
-            f32x4 sum = *reinterpret_cast<const f32x4 *>(acc_lds + 4 * c);
-            for (int k = 1; k < G; ++k) {
-                const f32x4 v = *reinterpret_cast<const f32x4 *>(acc_lds + 4 * (k * C + c));
-                sum.x += v.x;
-                sum.y += v.y;
-                sum.z += v.z;
-                sum.w += v.w;
-            }
-            sum.x *= invW;
-            sum.y *= invW;
-            sum.z *= invW;
-            sum.w *= invW;
-            *reinterpret_cast<f32x4 *>(out + (size_t)row * D + 4 * c) = sum;
+            f32x4 sum = acc_lds[c];
+            for (int k = 1; k < G; ++k) sum += acc_lds[k * C + c];
+            *reinterpret_cast<f32x4 *>(out + (size_t)row * D + 4 * c) = sum * invW;
         }
     } else {
-        for (int d = tid; d < D; d += kMergeThreads) {
+        for (int d = tid; d < D; d += nt) {
             float o = 0.0f;
-            for (int s = 0; s < S; ++s) {
-                const float ls = part_lse[(size_t)s * rows + row];
-                if (ls != -INFINITY) o += expf(ls - M) * part_o[((size_t)s * rows + row) * D + d];
-            }
+            for (int s = 0; s < S; ++s)
+                o += merge_weight(part_lse, wgt, s, rows, row, M) *
+                     part_o[((size_t)s * rows + row) * D + d];
             out[(size_t)row * D + d] = o * invW;
         }
     }
@@ -1172,8 +1222,18 @@ hipError_t launch_attention(const AttnArgs &a, int D, int NW, bool causal, bool 
 hipError_t launch_merge(const float *part_o, const float *part_lse, int S, int rows, int D,
                         float *out, float *out_lse, hipStream_t stream) {
     if (rows == 0) return hipSuccess;
-    hipLaunchKernelGGL(merge_kernel, dim3(rows), dim3(kMergeThreads), 0, stream, part_o, part_lse,
-                       S, rows, D, out, out_lse);
+    // Vector path: C = D / 4 columns times G split groups, G <= S, at most
+    // 1024 threads.  Scalar path (D % 4 != 0): 256 threads over the columns.
+    int G = 1, threads = 256;
+    if ((D & 3) == 0) {
+        const int C = D / 4;
+        G = kMergeMaxThreads / C;
+        if (G > S) G = S;
+        if (G < 1) G = 1;
+        threads = ((C * G + 63) / 64) * 64;
+    }
+    hipLaunchKernelGGL(merge_kernel, dim3(rows), dim3(threads), 0, stream, part_o, part_lse, S,
+                       rows, D, G, out, out_lse);
     return hipGetLastError();
 }
 
