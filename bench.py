@@ -36,6 +36,39 @@ HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 INT8_PEAK_TOPS = 5000.0          # dense int8 MFMA
 FP16_PEAK_TFLOPS = 2500.0        # dense fp16 MFMA
 N_BUFFERS = 4                    # 4 x 235 MB > 256 MB Infinity Cache
+KERNEL_SOURCES = [os.path.join(ROOT, "speculative_tree_verify_amd", "csrc", f)
+                  for f in ("stv_kernels.hip", "stv_internal.h")]
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the attention kernel from the committed
+    rocprofv3 counter summary for this workload, or None when there is none
+    or the kernel sources changed after the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            line = line.strip().strip("`")
+            if ":" in line:
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+    if fields.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def work_of(geom: synth.Geometry, masks):
@@ -242,7 +275,7 @@ def main():
             "peak": round(blended_peak, 1),
             "unit": "TFLOP/s",
             "frac": round(achieved / blended_peak, 4),
-            "traffic": None,
+            "traffic": measured_traffic(g.name),
             "kernel_us": round(s["attn_kernel_us"], 2),
             "ideal_mfma_us": round(s["ideal_mfma_us"], 2),
             "ideal_hbm_us": round(s["ideal_hbm_us"], 2),

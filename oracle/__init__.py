@@ -61,6 +61,10 @@ def _load():
         lib.orc_set_threads.restype = i32
         lib.orc_merge.argtypes = [P, P, i32, i32, i32, P, P]
         lib.orc_merge.restype = None
+        lib.orc_tree_accept.argtypes = [P, i32, P, P, P, P]
+        lib.orc_tree_accept.restype = i32
+        lib.orc_kv_commit.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, P, i32]
+        lib.orc_kv_commit.restype = i32
         _lib = lib
     return _lib
 
@@ -235,3 +239,35 @@ def merge(part_o, part_lse):
     lse = np.empty(rows, dtype=np.float64)
     _load().orc_merge(_ptr(po), _ptr(pl), S, rows, d, _ptr(out), _ptr(lse))
     return out, lse
+
+
+# ------------------------------------------------------ tree acceptance
+
+def tree_accept(mask, draft, target):
+    """Greedy tree acceptance (see orc_tree_accept).  mask: uint64 [T]
+    ancestor masks; draft, target: int32 [T] token ids.  Returns
+    (n, path int32 [T] with -1 past n, bonus)."""
+    m = _c(np.asarray(mask, dtype=np.uint64), np.uint64)
+    T = m.size
+    dr = _c(np.asarray(draft, dtype=np.int32), np.int32)
+    tg = _c(np.asarray(target, dtype=np.int32), np.int32)
+    assert dr.size == T and tg.size == T
+    path = np.empty(T, dtype=np.int32)
+    bonus = np.zeros(1, dtype=np.int32)
+    n = _load().orc_tree_accept(_ptr(m), T, _ptr(dr), _ptr(tg), _ptr(path), _ptr(bonus))
+    if n < 1:
+        raise ValueError("bad tree_accept arguments")
+    return int(n), path, int(bonus[0])
+
+
+def kv_commit(kv, ctx_len: int, T: int, path, n: int) -> None:
+    """In-place accepted-path commit on a host cache (see orc_kv_commit)."""
+    for name in ("k_codes", "k_scales", "v_codes", "v_scales"):
+        a = getattr(kv, name)
+        assert a.flags["C_CONTIGUOUS"], name
+    p = _c(np.asarray(path, dtype=np.int32), np.int32)
+    rc = _load().orc_kv_commit(_ptr(kv.k_codes), _ptr(kv.k_scales), _ptr(kv.v_codes),
+                               _ptr(kv.v_scales), kv.n_kv_heads, kv.head_dim, kv.capacity,
+                               ctx_len, T, _ptr(p), n)
+    if rc != 0:
+        raise ValueError("bad kv_commit arguments")

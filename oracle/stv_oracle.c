@@ -404,3 +404,116 @@ ORC_EXPORT void orc_merge(const double *part_o, const double *part_lse, int S, i
             out_lse[r] = M + log(W);
     }
 }
+
+/* ---------------------------------------------------- tree acceptance */
+
+/* Greedy acceptance over a token tree (elpis "Why fast" and elpis-lossless
+ * "How": the 8-row tree, best-first nodes, commit the longest matching path
+ * plus one token; acceptance compares token ids exactly).  Readings:
+ *  (a1) node 0 is the round's root, already decided, and always committed;
+ *  (a2) node i > 0 matches when its draft token equals the target's greedy
+ *       token at its parent row (parent = highest other bit of mask[i]);
+ *  (a3) a node is acceptable when it descends from node 0 and every node on
+ *       its path other than node 0 matches;
+ *  (a4) the committed path ends at the acceptable node of greatest depth
+ *       (number of nodes on its path), the lowest node index among equals;
+ *  (a5) the extra token is the target's token at that node's row.
+ * path[0 .. n-1] receives the path's node indices in increasing order and
+ * path[n .. T-1] = -1.  Returns n (>= 1), or 0 on bad arguments. */
+ORC_EXPORT int orc_tree_accept(const uint64_t *mask, int T, const int32_t *draft,
+                               const int32_t *target, int32_t *path, int32_t *bonus)
+{
+    if (T < 1 || T > 64)
+        return 0;
+    int best = 0, best_depth = 1;
+    for (int i = 0; i < T; ++i) {
+        if (!((mask[i] >> 0) & 1ull))
+            continue;                                   /* not below node 0 */
+        int ok = 1, depth = 0;
+        for (int j = 0; j <= i; ++j) {
+            if (!((mask[i] >> j) & 1ull))
+                continue;
+            ++depth;
+            if (j == 0)
+                continue;
+            int parent = -1;                            /* highest other bit */
+            for (int k = j - 1; k >= 0; --k)
+                if ((mask[j] >> k) & 1ull) {
+                    parent = k;
+                    break;
+                }
+            if (parent < 0 || draft[j] != target[parent])
+                ok = 0;
+        }
+        if (ok && depth > best_depth) {
+            best = i;
+            best_depth = depth;
+        }
+    }
+    int n = 0;
+    for (int j = 0; j < T; ++j)
+        if ((mask[best] >> j) & 1ull)
+            path[n++] = j;
+    for (int j = n; j < T; ++j)
+        path[j] = -1;
+    *bonus = target[best];
+    return n;
+}
+
+/* Accepted-path commit: for j = 0 .. n-1 the K and V of cache position
+ * L + path[j] move to position L + j, in every kv head; everything else in
+ * the cache keeps its value (elpis-lossless "How": only the committed
+ * tokens' K/V stay in the cache, at consecutive positions).  All sources are
+ * read before any position is written.  Layouts as in (c8).  Returns 0, or
+ * -1 on bad arguments. */
+ORC_EXPORT int orc_kv_commit(uint32_t *kc, uint16_t *ks, uint32_t *vc, uint16_t *vs, int Hkv,
+                             int D, int cap, int L, int T, const int32_t *path, int n)
+{
+    int nb = D / 32;
+    size_t ng = n_groups(cap);
+    if (n < 1 || n > T || L < 0 || L + T > cap)
+        return -1;
+    for (int j = 0; j < n; ++j)
+        if (path[j] < 0 || path[j] >= T)
+            return -1;
+    size_t kwords = (size_t)n * nb * 3;
+    uint32_t *kbuf = malloc(kwords * sizeof(uint32_t) + 1);
+    uint16_t *kbs = malloc((size_t)n * nb * sizeof(uint16_t) + 1);
+    int *vcode = malloc((size_t)n * D * sizeof(int) + 1);
+    uint16_t *vsb = malloc((size_t)n * nb * sizeof(uint16_t) + 1);
+    if (!kbuf || !kbs || !vcode || !vsb) {
+        free(kbuf); free(kbs); free(vcode); free(vsb);
+        return -1;
+    }
+    for (int g = 0; g < Hkv; ++g) {
+        /* read every source first */
+        for (int j = 0; j < n; ++j) {
+            int src = L + path[j];
+            for (int b = 0; b < nb; ++b) {
+                size_t blk = ((size_t)g * cap + (size_t)src) * nb + b;
+                memcpy(kbuf + ((size_t)j * nb + b) * 3, kc + blk * 3, 3 * sizeof(uint32_t));
+                kbs[(size_t)j * nb + b] = ks[blk];
+                vsb[(size_t)j * nb + b] =
+                    vs[(((size_t)g * ng + (size_t)(src / 32)) * nb + b) * 32 + src % 32];
+            }
+            for (int d = 0; d < D; ++d)
+                vcode[(size_t)j * D + d] = v_code(vc, ng, D, g, src, d);
+        }
+        /* then write the destinations */
+        for (int j = 0; j < n; ++j) {
+            int dst = L + j;
+            for (int b = 0; b < nb; ++b) {
+                size_t blk = ((size_t)g * cap + (size_t)dst) * nb + b;
+                memcpy(kc + blk * 3, kbuf + ((size_t)j * nb + b) * 3, 3 * sizeof(uint32_t));
+                ks[blk] = kbs[(size_t)j * nb + b];
+                vs[(((size_t)g * ng + (size_t)(dst / 32)) * nb + b) * 32 + dst % 32] =
+                    vsb[(size_t)j * nb + b];
+            }
+            for (int d = 0; d < D; ++d)
+                orc_code_set(vc + (((size_t)g * ng + (size_t)(dst / 32)) * D + d) * 3, dst % 32,
+                             vcode[(size_t)j * D + d]);
+        }
+    }
+    free(kbuf); free(kbs); free(vcode); free(vsb);
+    return 0;
+}

@@ -1222,13 +1222,14 @@ hipError_t launch_attention(const AttnArgs &a, int D, int NW, bool causal, bool 
 hipError_t launch_merge(const float *part_o, const float *part_lse, int S, int rows, int D,
                         float *out, float *out_lse, hipStream_t stream) {
     if (rows == 0) return hipSuccess;
-    // Vector path: C = D / 4 columns times G split groups, G <= S, at most
-    // 1024 threads.  Scalar path (D % 4 != 0): 256 threads over the columns.
+    // Vector path: C = D / 4 columns times G split groups, about eight
+    // splits per group (so many rows keep blocks small), at most 1024
+    // threads.  Scalar path (D % 4 != 0): 256 threads over the columns.
     int G = 1, threads = 256;
     if ((D & 3) == 0) {
         const int C = D / 4;
-        G = kMergeMaxThreads / C;
-        if (G > S) G = S;
+        G = (S + 7) / 8;
+        if (G > kMergeMaxThreads / C) G = kMergeMaxThreads / C;
         if (G < 1) G = 1;
         threads = ((C * G + 63) / 64) * 64;
     }

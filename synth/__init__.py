@@ -174,3 +174,22 @@ def all_tree_shapes(n_nodes: int):
 def make_new_rows(rng: np.random.Generator, n_tok: int, n_kv_heads: int, head_dim: int) -> np.ndarray:
     """fp32 K or V rows of the new tokens, before they enter the 3-bit cache."""
     return rng.standard_normal((n_tok, n_kv_heads, head_dim), dtype=np.float32)
+
+
+def make_tree_tokens(rng: np.random.Generator, parent: np.ndarray, vocab: int,
+                     p_follow: float = 0.6) -> tuple[np.ndarray, np.ndarray]:
+    """Draft tokens of the tree nodes and the target's greedy token at every
+    tree row, for acceptance tests and benchmarks.
+
+    Draft tokens are uniform over [0, vocab).  The target token of row i is,
+    with probability p_follow, the draft token of one of i's children picked
+    uniformly (so some draft paths are followed for a while), else uniform.
+    """
+    n = len(parent)
+    draft = rng.integers(0, vocab, size=n).astype(np.int32)
+    target = rng.integers(0, vocab, size=n).astype(np.int32)
+    for i in range(n):
+        kids = [c for c in range(n) if parent[c] == i]
+        if kids and rng.random() < p_follow:
+            target[i] = draft[int(rng.choice(kids))]
+    return draft, target
