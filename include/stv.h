@@ -213,6 +213,50 @@ int stv_attention_partials(const float *q, int32_t T, int32_t n_q_heads,
 int stv_split_merge(const float *part_o, const float *part_lse, int32_t S, int32_t rows,
                     int32_t D, float *out, float *out_lse, void *stream);
 
+/*
+ * stv_tree_accept -- greedy acceptance over the draft tree (elpis, "Why
+ * fast": the 8-row token tree, commit the longest matching path plus one
+ * token; elpis-lossless, "Lossless": token ids are compared exactly, nothing
+ * is sampled or thresholded).
+ *   anc_mask    [host] uint64 [T], the verify call's tree masks (same rules)
+ *   T           1 .. 64 tree rows; node 0 is the round's root, already decided
+ *   draft       int32 [T], token id of each tree node
+ *   target      int32 [T], the target's greedy token at each tree row (the
+ *               token that follows the node's path)
+ *   path        int32 [T] out: the committed nodes in increasing order, then
+ *               -1 in the entries past the count
+ *   n_accepted  int32 [1] out: number of committed nodes, >= 1 (the root)
+ *   bonus       int32 [1] out: the extra token, target[last committed node]
+ * Node i > 0 matches when draft[i] == target[parent of i]; a node can end
+ * the path when it lies below node 0 and every node on its path below node 0
+ * matches; the deepest such node wins, the lowest index among equals.
+ * Errors: STV_EINVAL, STV_EMASK, STV_EHIP.
+ */
+int stv_tree_accept(const uint64_t *anc_mask, int32_t T, const int32_t *draft,
+                    const int32_t *target, int32_t *path, int32_t *n_accepted, int32_t *bonus,
+                    void *stream);
+
+/*
+ * stv_kv_commit -- keep only the committed tree tokens in the cache, at
+ * consecutive positions (elpis-lossless, "How": the accepted path's K/V is
+ * what stays; the rejected nodes' rows are free again).
+ *   kv          [host] the layer's cache, written in place through its
+ *               arrays; the tree's K/V sits at ctx_len + i
+ *   ctx_len, T  context before the tree, tree rows (1 .. 64);
+ *               ctx_len + T <= capacity
+ *   path, n_accepted  device outputs of stv_tree_accept (read on the device,
+ *               so the call needs no host synchronisation)
+ * For j < n: the K codes, K scales, V codes and V scales of position
+ * ctx_len + path[j] move to position ctx_len + j in every KV head; all
+ * sources are read before any destination is written.  Every other cache
+ * entry keeps its value.  The next round continues at ctx_len + n.  A count
+ * outside [1, T] or a path entry outside [0, T) found on the device leaves
+ * the cache unchanged.
+ * Errors: STV_EINVAL, STV_ECAPACITY, STV_EHIP.
+ */
+int stv_kv_commit(const stv_kv_layer *kv, int32_t ctx_len, int32_t T, const int32_t *path,
+                  const int32_t *n_accepted, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

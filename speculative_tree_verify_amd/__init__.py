@@ -80,6 +80,10 @@ def load_library():
                                                ctypes.c_float, i32, P, P, P]
         lib.stv_split_merge.restype = ctypes.c_int
         lib.stv_split_merge.argtypes = [P, P, i32, i32, i32, P, P, P]
+        lib.stv_tree_accept.restype = ctypes.c_int
+        lib.stv_tree_accept.argtypes = [P, i32, P, P, P, P, P, P]
+        lib.stv_kv_commit.restype = ctypes.c_int
+        lib.stv_kv_commit.argtypes = [ctypes.POINTER(_KVLayer), i32, i32, P, P, P]
         _lib = lib
     return _lib
 
@@ -314,3 +318,41 @@ def split_merge(part_o, part_lse, out=None, out_lse=None):
         _dev_ptr(out_lse, torch.float32, "out_lse", (rows,)), _stream(part_o.device))
     _check(rc)
     return out
+
+
+def tree_accept(anc_mask, draft, target, path=None, n_accepted=None, bonus=None):
+    """Greedy acceptance over the draft tree (see include/stv.h).
+
+    anc_mask: uint64 [T] host masks; draft, target: int32 [T] GPU tensors.
+    Returns (path int32 [T], n_accepted int32 [1], bonus int32 [1]) GPU
+    tensors; path holds the committed nodes, then -1.
+    """
+    torch = _torch()
+    m = np.ascontiguousarray(np.asarray(anc_mask, dtype=np.uint64))
+    T = m.size
+    dev = draft.device
+    if path is None:
+        path = torch.empty(T, dtype=torch.int32, device=dev)
+    if n_accepted is None:
+        n_accepted = torch.empty(1, dtype=torch.int32, device=dev)
+    if bonus is None:
+        bonus = torch.empty(1, dtype=torch.int32, device=dev)
+    rc = load_library().stv_tree_accept(
+        m.ctypes.data if T else None, T, _dev_ptr(draft, torch.int32, "draft", (T,)),
+        _dev_ptr(target, torch.int32, "target", (T,)), _dev_ptr(path, torch.int32, "path", (T,)),
+        _dev_ptr(n_accepted, torch.int32, "n_accepted", (1,)),
+        _dev_ptr(bonus, torch.int32, "bonus", (1,)), _stream(dev))
+    _check(rc)
+    return path, n_accepted, bonus
+
+
+def kv_commit(kv: KVCache, ctx_len: int, path, n_accepted):
+    """Move the committed tree tokens' K/V to positions ctx_len.. (in place)."""
+    torch = _torch()
+    T = int(path.numel())
+    layer = kv._layer()
+    rc = load_library().stv_kv_commit(ctypes.byref(layer), ctx_len, T,
+                                      _dev_ptr(path, torch.int32, "path", (T,)),
+                                      _dev_ptr(n_accepted, torch.int32, "n_accepted", (1,)),
+                                      _stream(path.device))
+    _check(rc)

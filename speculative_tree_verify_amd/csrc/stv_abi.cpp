@@ -10,6 +10,7 @@
 #include <mutex>
 #include <vector>
 
+#include "stv_accept.h"
 #include "stv_internal.h"
 
 namespace {
@@ -325,6 +326,64 @@ int stv_split_merge(const float *part_o, const float *part_lse, int32_t S, int32
     hipError_t e = stv::launch_merge(part_o, part_lse, S, rows, D, out, out_lse,
                                      static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(STV_EHIP, "merge launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int stv_tree_accept(const uint64_t *anc_mask, int32_t T, const int32_t *draft,
+                    const int32_t *target, int32_t *path, int32_t *n_accepted, int32_t *bonus,
+                    void *stream) {
+    if (T < 1 || T > STV_MAX_TREE_ROWS) return fail(STV_EINVAL, "T must be in 1..64 (got %d)", T);
+    if (!anc_mask) return fail(STV_EINVAL, "anc_mask must not be NULL");
+    if (!draft || !target || !path || !n_accepted || !bonus)
+        return fail(STV_EINVAL, "draft, target, path, n_accepted and bonus must not be NULL");
+    int rc = check_mask(anc_mask, T);
+    if (rc) return rc;
+    stv::AcceptArgs a;
+    memset(&a, 0, sizeof a);
+    for (int i = 0; i < T; ++i) a.mask[i] = anc_mask[i];
+    a.T = T;
+    a.draft = draft;
+    a.target = target;
+    a.path = path;
+    a.n_accepted = n_accepted;
+    a.bonus = bonus;
+    hipError_t e = stv::launch_tree_accept(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(STV_EHIP, "tree_accept launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int stv_kv_commit(const stv_kv_layer *kv, int32_t ctx_len, int32_t T, const int32_t *path,
+                  const int32_t *n_accepted, void *stream) {
+    if (!kv) return fail(STV_EINVAL, "kv is NULL");
+    if (!kv->k_codes || !kv->k_scales || !kv->v_codes || !kv->v_scales)
+        return fail(STV_EINVAL, "kv has a NULL array");
+    if (T < 1 || T > STV_MAX_TREE_ROWS) return fail(STV_EINVAL, "T must be in 1..64 (got %d)", T);
+    if (!path || !n_accepted) return fail(STV_EINVAL, "path and n_accepted must not be NULL");
+    const int D = kv->head_dim;
+    if (D != 64 && D != 128 && D != 256) return fail(STV_EINVAL, "head_dim must be 64, 128 or 256");
+    if (kv->n_kv_heads < 1) return fail(STV_EINVAL, "n_kv_heads must be >= 1");
+    if (kv->capacity <= 0) return fail(STV_EINVAL, "capacity must be positive");
+    if (ctx_len < 0) return fail(STV_EINVAL, "ctx_len must be >= 0");
+    if ((long long)ctx_len + T > kv->capacity)
+        return fail(STV_ECAPACITY, "ctx_len + T = %lld exceeds capacity %d", (long long)ctx_len + T,
+                    kv->capacity);
+    stv::CommitArgs a;
+    // the layer's arrays are the caller's writable device memory; this call
+    // is the one that writes through them
+    a.kc = const_cast<uint32_t *>(kv->k_codes);
+    a.ks = const_cast<uint16_t *>(kv->k_scales);
+    a.vc = const_cast<uint32_t *>(kv->v_codes);
+    a.vs = const_cast<uint16_t *>(kv->v_scales);
+    a.Hkv = kv->n_kv_heads;
+    a.D = D;
+    a.cap = kv->capacity;
+    a.ngroups = (kv->capacity + 31) / 32;
+    a.L = ctx_len;
+    a.T = T;
+    a.path = path;
+    a.n_accepted = n_accepted;
+    hipError_t e = stv::launch_kv_commit(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(STV_EHIP, "kv_commit launch failed: %s", hipGetErrorString(e));
     return ok();
 }
 

@@ -15,6 +15,7 @@
 //          MFMA accumulator over V^T
 //     epilogue: normalise, write the partial (or the output when S = 1)
 //   merge: out = sum_s exp(lse_s - LSE) O_s, splits in fixed order.
+#include "stv_codes.h"
 #include "stv_internal.h"
 
 #include <math.h>
@@ -33,30 +34,6 @@ typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
 
 // Word 3 of a raw buffer descriptor on gfx9: 32-bit data format, no swizzle.
 constexpr int kBufWord3 = 0x00020000;
-
-// ------------------------------------------------------------ 3-bit blocks
-// Byte-plane layout: byte i of word qq' below holds the code of element
-// 4*qq + i.  Words 0..2 of a block give codes qq = 0..7 as follows.
-__device__ __forceinline__ void unpack_bytes(uint32_t w0, uint32_t w1, uint32_t w2,
-                                             uint32_t o[8]) {
-    const uint32_t m3 = 0x07070707u, m2 = 0x03030303u, mh = 0x04040404u;
-    o[0] = w0 & m3;
-    o[1] = (w0 >> 3) & m3;
-    o[2] = w1 & m3;
-    o[3] = (w1 >> 3) & m3;
-    o[4] = w2 & m3;
-    o[5] = (w2 >> 3) & m3;
-    o[6] = ((w0 >> 6) & m2) | ((w2 >> 4) & mh);
-    o[7] = ((w1 >> 6) & m2) | ((w2 >> 5) & mh);
-}
-
-__device__ __forceinline__ void pack_bytes(const uint32_t o[8], uint32_t &w0, uint32_t &w1,
-                                           uint32_t &w2) {
-    const uint32_t m2 = 0x03030303u, mh = 0x04040404u;
-    w0 = o[0] | (o[1] << 3) | ((o[6] & m2) << 6);
-    w1 = o[2] | (o[3] << 3) | ((o[7] & m2) << 6);
-    w2 = o[4] | (o[5] << 3) | ((o[6] & mh) << 4) | ((o[7] & mh) << 5);
-}
 
 // Four codes c in [0, 7] (one per byte) -> four int8 values c - 4, by one
 // v_perm_b32 byte select from the table {-4, -3, -2, -1, 0, 1, 2, 3}.
@@ -106,24 +83,6 @@ __device__ __forceinline__ uint32_t code_of(float x, float s) {
     float r = rintf(x / s);
     r = fminf(fmaxf(r, -4.0f), 3.0f);
     return (uint32_t)((int)r + 4);
-}
-
-// Set element e's code in a three-word block (byte-plane layout).
-__device__ __forceinline__ void set_code(uint32_t &w0, uint32_t &w1, uint32_t &w2, int e,
-                                         uint32_t c) {
-    const int qq = e >> 2, i = e & 3;
-    if (qq < 6) {
-        const int sh = 8 * i + 3 * (qq & 1);
-        const uint32_t m = 7u << sh;
-        uint32_t &w = qq < 2 ? w0 : (qq < 4 ? w1 : w2);
-        w = (w & ~m) | (c << sh);
-    } else {
-        const int sh = 8 * i + 6;
-        uint32_t &w = qq == 6 ? w0 : w1;
-        w = (w & ~(3u << sh)) | ((c & 3u) << sh);
-        const int hb = 8 * i + 6 + (qq - 6);
-        w2 = (w2 & ~(1u << hb)) | ((c >> 2) << hb);
-    }
 }
 
 __device__ __forceinline__ void load32(const float *src, float v[32]) {

@@ -43,7 +43,8 @@ def _declared():
 def test_header_declares_the_four_operations():
     names = _declared()
     for op in ("stv_kv_quant_pack", "stv_verify_attention", "stv_prefill_attention",
-               "stv_split_merge", "stv_attention_plan", "stv_last_error", "stv_abi_version"):
+               "stv_split_merge", "stv_attention_plan", "stv_last_error", "stv_abi_version",
+               "stv_tree_accept", "stv_kv_commit"):
         assert op in names
 
 
@@ -187,6 +188,32 @@ def test_merge_argument_errors(lib, stvmod):
     assert f(FAKE, FAKE, 2, 10, 2000, FAKE, None, None) == E.STV_EINVAL
     assert f(None, FAKE, 2, 10, 256, FAKE, None, None) == E.STV_EINVAL
     assert f(FAKE, FAKE, 2, 0, 256, FAKE, None, None) == E.STV_OK          # no rows: no launch
+
+
+def test_accept_and_commit_argument_errors(lib, stvmod):
+    E = stvmod
+    acc = lib.stv_tree_accept
+    good = synth.ancestor_masks(np.array([-1, 0, 0, 1]))
+    m = np.ascontiguousarray(good)
+    assert acc(m.ctypes.data, 0, FAKE, FAKE, FAKE, FAKE, FAKE, None) == E.STV_EINVAL
+    assert acc(m.ctypes.data, 65, FAKE, FAKE, FAKE, FAKE, FAKE, None) == E.STV_EINVAL
+    assert acc(None, 4, FAKE, FAKE, FAKE, FAKE, FAKE, None) == E.STV_EINVAL
+    assert acc(m.ctypes.data, 4, FAKE, None, FAKE, FAKE, FAKE, None) == E.STV_EINVAL
+    assert acc(m.ctypes.data, 4, FAKE, FAKE, FAKE, FAKE, None, None) == E.STV_EINVAL
+    bad = good.copy()
+    bad[3] = np.uint64(1 << 3)
+    bad[2] |= np.uint64(1 << 3)
+    mb = np.ascontiguousarray(bad)
+    assert acc(mb.ctypes.data, 4, FAKE, FAKE, FAKE, FAKE, FAKE, None) == E.STV_EMASK
+    com = lib.stv_kv_commit
+    layer = _layer(stvmod, cap=100)
+    assert com(ctypes.byref(layer), 90, 11, FAKE, FAKE, None) == E.STV_ECAPACITY
+    assert com(ctypes.byref(layer), -1, 8, FAKE, FAKE, None) == E.STV_EINVAL
+    assert com(ctypes.byref(layer), 0, 0, FAKE, FAKE, None) == E.STV_EINVAL
+    assert com(ctypes.byref(layer), 0, 65, FAKE, FAKE, None) == E.STV_EINVAL
+    assert com(ctypes.byref(layer), 0, 8, None, FAKE, None) == E.STV_EINVAL
+    assert com(ctypes.byref(_layer(stvmod, d=96, cap=100)), 0, 8, FAKE, FAKE, None) == E.STV_EINVAL
+    assert com(None, 0, 8, FAKE, FAKE, None) == E.STV_EINVAL
 
 
 @pytest.mark.parametrize("T,hq,hkv,d,L,causal", [
