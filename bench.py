@@ -49,11 +49,12 @@ def kernel_source_hash() -> str:
     return h.hexdigest()
 
 
-def measured_traffic(workload: str):
+def measured_traffic(kernel: str, workload: str):
     """HBM bytes per launch of the attention kernel from the committed
-    rocprofv3 counter summary for this workload, or None when there is none
-    or the kernel sources changed after the counters were taken."""
-    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.md")
+    rocprofv3 counter summary for this kernel and workload, or None when
+    there is none or the kernel sources changed after the counters were
+    taken."""
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{kernel}_{workload}.md")
     if not os.path.exists(path):
         return None
     fields = {}
@@ -109,6 +110,7 @@ class Workload:
             parents = (synth.chain_parents(geom.n_rows) if geom.kind == "chain"
                        else synth.make_tree_parents(rng, geom.n_rows, geom.max_depth))
             self.mask = synth.ancestor_masks(parents)
+            self.parents = parents
         knew = synth.make_new_rows(rng, geom.n_rows, geom.n_kv_heads, geom.head_dim)
         vnew = synth.make_new_rows(rng, geom.n_rows, geom.n_kv_heads, geom.head_dim)
         dev = "cuda"
@@ -174,6 +176,35 @@ class Workload:
         attn_ms = [e[0].elapsed_time(e[1]) for e in evs]
         merge_ms = [e[1].elapsed_time(e[2]) for e in evs]
         return {"wall_s": wall, "attn_ms": attn_ms, "merge_ms": merge_ms}
+
+
+def accept_commit_bench(wl: Workload, steps: int):
+    """Times the end of a verify round on the workload's tree: greedy
+    acceptance then the accepted-path commit of the 3-bit K/V (one call
+    each, device-side path and count)."""
+    torch, stv, g = wl.torch, wl.stv, wl.g
+    rng = np.random.default_rng(g.seed + 100)
+    draft, target = synth.make_tree_tokens(rng, wl.parents, vocab=2, p_follow=0.9)
+    d = torch.from_numpy(draft).cuda()
+    t = torch.from_numpy(target).cuda()
+    path = torch.empty(g.n_rows, dtype=torch.int32, device="cuda")
+    n = torch.empty(1, dtype=torch.int32, device="cuda")
+    bonus = torch.empty(1, dtype=torch.int32, device="cuda")
+    for i in range(3):
+        stv.tree_accept(wl.mask, d, t, path, n, bonus)
+        stv.kv_commit(wl.caches[i % len(wl.caches)], g.ctx_len, path, n)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    for i in range(steps):
+        stv.tree_accept(wl.mask, d, t, path, n, bonus)
+        stv.kv_commit(wl.caches[i % len(wl.caches)], g.ctx_len, path, n)
+    ev[1].record()
+    torch.cuda.synchronize()
+    n_acc = int(n.item())
+    return {"us_per_call": round(ev[0].elapsed_time(ev[1]) * 1e3 / steps, 2),
+            "n_accepted": n_acc, "tree_nodes": g.n_rows,
+            "moved_bytes": n_acc * g.n_kv_heads * 2 * (g.head_dim // 32) * 14}
 
 
 def summarize(wl: Workload, r, steps):
@@ -249,6 +280,8 @@ def main():
     total_ops = w["qk_ops"] + w["pv_ops"]
     blended_peak = total_ops / (w["qk_ops"] / INT8_PEAK_TOPS + w["pv_ops"] / FP16_PEAK_TFLOPS)
     achieved = total_ops / (s["attn_kernel_us"] * 1e-6) / 1e12
+    rows_per_kv_head = g.n_rows * (g.n_q_heads // g.n_kv_heads)
+    kernel_name = "attn_dec_kernel" if rows_per_kv_head <= 16 else "attn_split_kernel"
     line = {
         "metric": METRIC,
         "value": round(w["step_bytes"] / (s["ms_per_step"] * 1e-3) / 1e9, 2),
@@ -269,19 +302,21 @@ def main():
         "hbm_gbs_per_call": round(s["hbm_gbs"], 1),
         "hbm_frac_per_call": round(s["hbm_frac"], 4),
         "roofline": {
-            "kernel": "attn_split_kernel",
+            "kernel": kernel_name,
             "bound": "mfma",
             "achieved": round(achieved, 2),
             "peak": round(blended_peak, 1),
             "unit": "TFLOP/s",
             "frac": round(achieved / blended_peak, 4),
-            "traffic": measured_traffic(g.name),
+            "traffic": measured_traffic(kernel_name, g.name),
             "kernel_us": round(s["attn_kernel_us"], 2),
             "ideal_mfma_us": round(s["ideal_mfma_us"], 2),
             "ideal_hbm_us": round(s["ideal_hbm_us"], 2),
         },
     }
     extra = {}
+    if wl.mask is not None:
+        extra[f"accept_commit_{g.name}"] = accept_commit_bench(wl, args.extra_steps)
     for name in [n for n in args.extra.split(",") if n]:
         del wl
         torch.cuda.empty_cache()
