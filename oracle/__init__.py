@@ -65,6 +65,8 @@ def _load():
         lib.orc_tree_accept.restype = i32
         lib.orc_kv_commit.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, P, i32]
         lib.orc_kv_commit.restype = i32
+        lib.orc_lookup_draft.argtypes = [P, P, i32, i32, i32, i32, i32, P, P, P, P]
+        lib.orc_lookup_draft.restype = None
         _lib = lib
     return _lib
 
@@ -271,3 +273,20 @@ def kv_commit(kv, ctx_len: int, T: int, path, n: int) -> None:
                                ctx_len, T, _ptr(p), n)
     if rc != 0:
         raise ValueError("bad kv_commit arguments")
+
+
+# ------------------------------------------------------- lookup drafting
+
+def lookup_draft(history, lengths, n_min: int = 6, n_max: int = 12, k: int = 8):
+    """Lookup drafting (see orc_lookup_draft).  history: int32 [B][stride];
+    lengths: int32 [B].  Returns dict(tokens [B][k], count, match, pos)."""
+    h = _c(np.atleast_2d(np.asarray(history, dtype=np.int32)), np.int32)
+    B, stride = h.shape
+    ln = _c(np.asarray(lengths, dtype=np.int32).reshape(B), np.int32)
+    tokens = np.empty((B, k), dtype=np.int32)
+    count = np.empty(B, dtype=np.int32)
+    match = np.empty(B, dtype=np.int32)
+    pos = np.empty(B, dtype=np.int32)
+    _load().orc_lookup_draft(_ptr(h), _ptr(ln), B, stride, n_min, n_max, k, _ptr(tokens),
+                             _ptr(count), _ptr(match), _ptr(pos))
+    return {"tokens": tokens, "count": count, "match": match, "pos": pos}

@@ -517,3 +517,50 @@ ORC_EXPORT int orc_kv_commit(uint32_t *kc, uint16_t *ks, uint32_t *vc, uint16_t 
     free(kbuf); free(kbs); free(vcode); free(vsb);
     return 0;
 }
+
+/* ------------------------------------------------------- lookup drafting */
+
+/* Lookup drafting over a token history (u/iamMess, lookup-augmented
+ * drafting: scan the request's own history for the most recent earlier
+ * occurrence of its last 6-12 tokens and propose the tokens that followed;
+ * elpis, the drafter-free n-gram chains).  Readings:
+ *  (l1) a candidate is an end position e <= N-2 (so at least one token
+ *       follows it); its match length m(e) is the number of tokens, at most
+ *       n_max and at most e+1, for which h[e-i] == h[N-1-i], i = 0, 1, ...;
+ *  (l2) candidates need m(e) >= n_min; the longest match wins, the most
+ *       recent (largest e) among equals;
+ *  (l3) the proposal is h[e+1 .. e+count] with count = min(k, N-1-e);
+ *       without a candidate: count 0, match 0, position -1.
+ * tokens[k] gets the proposal, then -1.  Per sequence b of a batch, history
+ * row b of `stride` tokens holds N = len[b] valid tokens. */
+ORC_EXPORT void orc_lookup_draft(const int32_t *hist, const int32_t *len, int B, int stride,
+                                 int n_min, int n_max, int k, int32_t *tokens, int32_t *count,
+                                 int32_t *match, int32_t *pos)
+{
+    for (int b = 0; b < B; ++b) {
+        const int32_t *h = hist + (size_t)b * stride;
+        int N = len[b] < 0 ? 0 : (len[b] > stride ? stride : len[b]);
+        int best_m = 0, best_e = -1;
+        for (int e = 0; e <= N - 2; ++e) {
+            int cap = n_max < e + 1 ? n_max : e + 1;
+            int m = 0;
+            while (m < cap && h[e - m] == h[N - 1 - m])
+                ++m;
+            if (m >= n_min && (m > best_m || (m == best_m && e > best_e))) {
+                best_m = m;
+                best_e = e;
+            }
+        }
+        int c = 0;
+        if (best_e >= 0) {
+            c = N - 1 - best_e;
+            if (c > k)
+                c = k;
+        }
+        for (int j = 0; j < k; ++j)
+            tokens[(size_t)b * k + j] = j < c ? h[best_e + 1 + j] : -1;
+        count[b] = c;
+        match[b] = best_e >= 0 ? best_m : 0;
+        pos[b] = best_e;
+    }
+}

@@ -193,3 +193,25 @@ def make_tree_tokens(rng: np.random.Generator, parent: np.ndarray, vocab: int,
         if kids and rng.random() < p_follow:
             target[i] = draft[int(rng.choice(kids))]
     return draft, target
+
+
+def make_lookup_history(rng: np.random.Generator, n_tokens: int, vocab: int, copy_len: int,
+                        n_decoys: int = 16) -> np.ndarray:
+    """A token history for lookup-drafting tests and benchmarks.
+
+    Tokens are uniform over [0, vocab).  The last copy_len tokens repeat an
+    earlier span (so the history's tail occurs earlier), and n_decoys shorter
+    copies of the tail's last 1..copy_len-1 tokens are planted at random
+    earlier places.
+    """
+    h = rng.integers(0, vocab, size=n_tokens).astype(np.int32)
+    if copy_len > 0 and n_tokens > 2 * copy_len + 1:
+        p = int(rng.integers(0, n_tokens - 2 * copy_len))
+        h[n_tokens - copy_len:] = h[p:p + copy_len]
+        for _ in range(n_decoys):
+            j = int(rng.integers(1, copy_len))
+            q = int(rng.integers(0, n_tokens - copy_len - j))
+            if q + j > p and q < p + copy_len:
+                continue                      # keep the planted span whole
+            h[q:q + j] = h[n_tokens - j:]
+    return h
