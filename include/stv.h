@@ -257,6 +257,33 @@ int stv_tree_accept(const uint64_t *anc_mask, int32_t T, const int32_t *draft,
 int stv_kv_commit(const stv_kv_layer *kv, int32_t ctx_len, int32_t T, const int32_t *path,
                   const int32_t *n_accepted, void *stream);
 
+/*
+ * stv_lookup_plan / stv_lookup_draft -- lookup drafting: propose draft
+ * tokens by finding the latest earlier occurrence of a request's last
+ * tokens in its own history and copying what followed (u/iamMess,
+ * lookup-augmented drafting, which scans for the last 6-12 tokens; elpis,
+ * the drafter-free n-gram chains).  Batched over B sequences.
+ *   history     int32 [B][stride] token ids; row b holds lengths[b] tokens
+ *   lengths     int32 [B] (device), clamped to [0, stride] on the device
+ *   n_min, n_max  1 <= n_min <= n_max <= 64 (6 and 12 on the pages)
+ *   k           0 .. 4096 proposed tokens per sequence
+ *   tokens      int32 [B][k] out: the proposal, then -1
+ *   count, match, pos  int32 [B] out: proposal length, match length, end
+ *               position e of the matched occurrence (-1 when none)
+ *   workspace   device bytes, at least stv_lookup_plan's figure
+ *               (B * ceil((stride-1)/2048) * 8); contents are scratch
+ * An end position e <= N-2 matches m(e) tokens when h[e-i] == h[N-1-i] for
+ * i < m(e), with m(e) <= min(n_max, e+1); candidates have m(e) >= n_min; the
+ * longest match wins, then the largest e; the proposal is h[e+1 ..], at most
+ * k tokens and never past the history's end.  B <= 65535.
+ * Errors: STV_EINVAL, STV_EWORKSPACE, STV_EHIP.
+ */
+int stv_lookup_plan(int32_t batch, int32_t stride, size_t *workspace_bytes);
+int stv_lookup_draft(const int32_t *history, const int32_t *lengths, int32_t batch,
+                     int32_t stride, int32_t n_min, int32_t n_max, int32_t k, int32_t *tokens,
+                     int32_t *count, int32_t *match, int32_t *pos, void *workspace,
+                     size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -84,6 +84,11 @@ def load_library():
         lib.stv_tree_accept.argtypes = [P, i32, P, P, P, P, P, P]
         lib.stv_kv_commit.restype = ctypes.c_int
         lib.stv_kv_commit.argtypes = [ctypes.POINTER(_KVLayer), i32, i32, P, P, P]
+        lib.stv_lookup_plan.restype = ctypes.c_int
+        lib.stv_lookup_plan.argtypes = [i32, i32, ctypes.POINTER(ctypes.c_size_t)]
+        lib.stv_lookup_draft.restype = ctypes.c_int
+        lib.stv_lookup_draft.argtypes = [P, P, i32, i32, i32, i32, i32, P, P, P, P, P,
+                                         ctypes.c_size_t, P]
         _lib = lib
     return _lib
 
@@ -356,3 +361,33 @@ def kv_commit(kv: KVCache, ctx_len: int, path, n_accepted):
                                       _dev_ptr(n_accepted, torch.int32, "n_accepted", (1,)),
                                       _stream(path.device))
     _check(rc)
+
+
+def lookup_plan(batch: int, stride: int) -> int:
+    """Workspace bytes of a lookup_draft call."""
+    ws = ctypes.c_size_t()
+    _check(load_library().stv_lookup_plan(batch, stride, ctypes.byref(ws)))
+    return int(ws.value)
+
+
+def lookup_draft(history, lengths, n_min: int = 6, n_max: int = 12, k: int = 8, workspace=None):
+    """Lookup drafting (see include/stv.h).  history: int32 [B][stride] GPU
+    tensor; lengths: int32 [B] GPU tensor.  Returns dict(tokens [B][k],
+    count, match, pos) of GPU tensors."""
+    torch = _torch()
+    B, stride = history.shape
+    dev = history.device
+    ws_bytes = lookup_plan(B, stride)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    out = {"tokens": torch.empty((B, k), dtype=torch.int32, device=dev),
+           "count": torch.empty(B, dtype=torch.int32, device=dev),
+           "match": torch.empty(B, dtype=torch.int32, device=dev),
+           "pos": torch.empty(B, dtype=torch.int32, device=dev)}
+    rc = load_library().stv_lookup_draft(
+        _dev_ptr(history, torch.int32, "history"), _dev_ptr(lengths, torch.int32, "lengths", (B,)),
+        B, stride, n_min, n_max, k, out["tokens"].data_ptr() if k else None,
+        out["count"].data_ptr(), out["match"].data_ptr(), out["pos"].data_ptr(),
+        _dev_ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(dev))
+    _check(rc)
+    return out

@@ -8,7 +8,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB_PATH = os.path.join(HERE, "libstv.so")
-SOURCES = [os.path.join(HERE, "csrc", f) for f in ("stv_kernels.hip", "stv_accept.hip", "stv_abi.cpp")]
+SOURCES = [os.path.join(HERE, "csrc", f) for f in ("stv_kernels.hip", "stv_accept.hip", "stv_lookup.hip", "stv_abi.cpp")]
 ARCH = "gfx950"
 
 # Packed fp32 VALU forms stay off: float code is compiled to scalar-lane ops.

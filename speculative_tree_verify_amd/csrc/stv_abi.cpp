@@ -11,6 +11,7 @@
 #include <vector>
 
 #include "stv_accept.h"
+#include "stv_lookup.h"
 #include "stv_internal.h"
 
 namespace {
@@ -384,6 +385,50 @@ int stv_kv_commit(const stv_kv_layer *kv, int32_t ctx_len, int32_t T, const int3
     a.n_accepted = n_accepted;
     hipError_t e = stv::launch_kv_commit(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(STV_EHIP, "kv_commit launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int stv_lookup_plan(int32_t batch, int32_t stride, size_t *workspace_bytes) {
+    if (batch < 0 || batch > 65535) return fail(STV_EINVAL, "batch must be in 0..65535 (got %d)", batch);
+    if (stride < 1) return fail(STV_EINVAL, "stride must be >= 1 (got %d)", stride);
+    if (!workspace_bytes) return fail(STV_EINVAL, "workspace_bytes must not be NULL");
+    *workspace_bytes = (size_t)batch * (size_t)stv::lookup_chunks(stride) * sizeof(uint64_t);
+    return ok();
+}
+
+int stv_lookup_draft(const int32_t *history, const int32_t *lengths, int32_t batch,
+                     int32_t stride, int32_t n_min, int32_t n_max, int32_t k, int32_t *tokens,
+                     int32_t *count, int32_t *match, int32_t *pos, void *workspace,
+                     size_t workspace_bytes, void *stream) {
+    size_t need = 0;
+    int rc = stv_lookup_plan(batch, stride, &need);
+    if (rc) return rc;
+    if (n_min < 1 || n_max < n_min || n_max > stv::kLookupMaxN)
+        return fail(STV_EINVAL, "need 1 <= n_min <= n_max <= %d (got %d, %d)", stv::kLookupMaxN,
+                    n_min, n_max);
+    if (k < 0 || k > 4096) return fail(STV_EINVAL, "k must be in 0..4096 (got %d)", k);
+    if (batch == 0) return ok();
+    if (!history || !lengths || !count || !match || !pos || (k > 0 && !tokens))
+        return fail(STV_EINVAL, "history, lengths, tokens, count, match and pos must not be NULL");
+    if (!workspace || workspace_bytes < need)
+        return fail(STV_EWORKSPACE, "workspace of %zu bytes needed (got %zu)", need,
+                    workspace ? workspace_bytes : (size_t)0);
+    stv::LookupArgs a;
+    a.hist = history;
+    a.len = lengths;
+    a.B = batch;
+    a.stride = stride;
+    a.n_min = n_min;
+    a.n_max = n_max;
+    a.k = k;
+    a.n_chunks = stv::lookup_chunks(stride);
+    a.ws = static_cast<uint64_t *>(workspace);
+    a.tokens = tokens;
+    a.count = count;
+    a.match = match;
+    a.pos = pos;
+    hipError_t e = stv::launch_lookup(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(STV_EHIP, "lookup launch failed: %s", hipGetErrorString(e));
     return ok();
 }
 

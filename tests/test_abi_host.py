@@ -44,7 +44,7 @@ def test_header_declares_the_four_operations():
     names = _declared()
     for op in ("stv_kv_quant_pack", "stv_verify_attention", "stv_prefill_attention",
                "stv_split_merge", "stv_attention_plan", "stv_last_error", "stv_abi_version",
-               "stv_tree_accept", "stv_kv_commit"):
+               "stv_tree_accept", "stv_kv_commit", "stv_lookup_plan", "stv_lookup_draft"):
         assert op in names
 
 
@@ -214,6 +214,28 @@ def test_accept_and_commit_argument_errors(lib, stvmod):
     assert com(ctypes.byref(layer), 0, 8, None, FAKE, None) == E.STV_EINVAL
     assert com(ctypes.byref(_layer(stvmod, d=96, cap=100)), 0, 8, FAKE, FAKE, None) == E.STV_EINVAL
     assert com(None, 0, 8, FAKE, FAKE, None) == E.STV_EINVAL
+
+
+def test_lookup_argument_errors(lib, stvmod):
+    E = stvmod
+    ws = ctypes.c_size_t()
+    assert lib.stv_lookup_plan(3, 5000, ctypes.byref(ws)) == E.STV_OK
+    assert ws.value == 3 * 3 * 8                     # ceil(4999 / 2048) = 3 chunks
+    assert lib.stv_lookup_plan(-1, 10, ctypes.byref(ws)) == E.STV_EINVAL
+    assert lib.stv_lookup_plan(1, 0, ctypes.byref(ws)) == E.STV_EINVAL
+    f = lib.stv_lookup_draft
+
+    def call(B=2, stride=100, n_min=6, n_max=12, k=8, ws_bytes=64, hist=FAKE, tokens=FAKE):
+        return f(hist, FAKE, B, stride, n_min, n_max, k, tokens, FAKE, FAKE, FAKE, FAKE,
+                 ws_bytes, None)
+    assert call(n_min=0) == E.STV_EINVAL
+    assert call(n_min=7, n_max=6) == E.STV_EINVAL
+    assert call(n_max=65) == E.STV_EINVAL
+    assert call(k=-1) == E.STV_EINVAL
+    assert call(hist=None) == E.STV_EINVAL
+    assert call(tokens=None) == E.STV_EINVAL
+    assert call(ws_bytes=15) == E.STV_EWORKSPACE
+    assert call(B=0) == E.STV_OK
 
 
 @pytest.mark.parametrize("T,hq,hkv,d,L,causal", [
