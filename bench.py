@@ -207,6 +207,41 @@ def accept_commit_bench(wl: Workload, steps: int):
             "moved_bytes": n_acc * g.n_kv_heads * 2 * (g.head_dim // 32) * 14}
 
 
+def lookup_bench(torch, stv, batch: int, n_tokens: int, steps: int, n_buffers: int = 1):
+    """Lookup drafting over `batch` histories of n_tokens tokens each (vocab
+    151,936, the tail copied from earlier in the history), rotating n_buffers
+    distinct batches; the scan reads every token once, so its algorithmic
+    bytes are batch * n_tokens * 4 per call."""
+    rng = np.random.default_rng(7)
+    bufs = []
+    for _ in range(n_buffers):
+        hist = np.stack([synth.make_lookup_history(rng, n_tokens, 151936, 12)
+                         for _ in range(batch)])
+        bufs.append(torch.from_numpy(hist).cuda())
+    ln = torch.full((batch,), n_tokens, dtype=torch.int32, device="cuda")
+    ws = torch.empty(max(stv.lookup_plan(batch, n_tokens), 1), dtype=torch.uint8, device="cuda")
+    out = {"tokens": torch.empty((batch, 8), dtype=torch.int32, device="cuda"),
+           "count": torch.empty(batch, dtype=torch.int32, device="cuda"),
+           "match": torch.empty(batch, dtype=torch.int32, device="cuda"),
+           "pos": torch.empty(batch, dtype=torch.int32, device="cuda")}
+    for i in range(3):
+        stv.lookup_draft(bufs[i % n_buffers], ln, 6, 12, 8, workspace=ws, out=out)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    for i in range(steps):
+        stv.lookup_draft(bufs[i % n_buffers], ln, 6, 12, 8, workspace=ws, out=out)
+    ev[1].record()
+    torch.cuda.synchronize()
+    us = ev[0].elapsed_time(ev[1]) * 1e3 / steps
+    nbytes = batch * n_tokens * 4
+    return {"us_per_call": round(us, 2), "batch": batch, "tokens_per_history": n_tokens,
+            "buffers_rotated": n_buffers,
+            "hbm_gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "match_len": int(out["match"][0].item())}
+
+
 def summarize(wl: Workload, r, steps):
     w = wl.work
     ms_step = r["wall_s"] * 1e3 / steps
@@ -256,6 +291,8 @@ def main():
     ap.add_argument("--extra", default="prefill_4k_32k,tree8_262k,decode_262k,decode_8k,tree64_32k",
                     help="comma-separated extra workloads ('' for none)")
     ap.add_argument("--extra-steps", type=int, default=10)
+    ap.add_argument("--no-lookup", dest="lookup", action="store_false",
+                    help="skip the lookup-drafting lines under extra")
     ap.add_argument("--cpu-rows", type=int, default=128, help="oracle sample size (0: skip)")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="after the run, launch an elementwise copy (torch.neg) of this many MiB "
@@ -324,6 +361,10 @@ def main():
         rr = wl.run(args.extra_steps, 2)
         se = summarize(wl, rr, args.extra_steps)
         extra[name] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in se.items()}
+    if args.lookup:
+        extra["lookup_1x262k"] = lookup_bench(torch, stv, 1, 262144, args.extra_steps)
+        extra["lookup_256x262k"] = lookup_bench(torch, stv, 256, 262144, args.extra_steps,
+                                                n_buffers=2)
     if extra:
         line["extra"] = extra
     if args.calib_copy_mb > 0:

@@ -271,7 +271,7 @@ int stv_kv_commit(const stv_kv_layer *kv, int32_t ctx_len, int32_t T, const int3
  *   count, match, pos  int32 [B] out: proposal length, match length, end
  *               position e of the matched occurrence (-1 when none)
  *   workspace   device bytes, at least stv_lookup_plan's figure
- *               (B * ceil((stride-1)/2048) * 8); contents are scratch
+ *               (B * ceil((stride-1)/4096) * 8); contents are scratch
  * An end position e <= N-2 matches m(e) tokens when h[e-i] == h[N-1-i] for
  * i < m(e), with m(e) <= min(n_max, e+1); candidates have m(e) >= n_min; the
  * longest match wins, then the largest e; the proposal is h[e+1 ..], at most

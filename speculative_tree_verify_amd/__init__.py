@@ -370,24 +370,28 @@ def lookup_plan(batch: int, stride: int) -> int:
     return int(ws.value)
 
 
-def lookup_draft(history, lengths, n_min: int = 6, n_max: int = 12, k: int = 8, workspace=None):
+def lookup_draft(history, lengths, n_min: int = 6, n_max: int = 12, k: int = 8, workspace=None,
+                 out=None):
     """Lookup drafting (see include/stv.h).  history: int32 [B][stride] GPU
     tensor; lengths: int32 [B] GPU tensor.  Returns dict(tokens [B][k],
-    count, match, pos) of GPU tensors."""
+    count, match, pos) of GPU tensors (`out`, when given, is filled)."""
     torch = _torch()
     B, stride = history.shape
     dev = history.device
     ws_bytes = lookup_plan(B, stride)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
-    out = {"tokens": torch.empty((B, k), dtype=torch.int32, device=dev),
-           "count": torch.empty(B, dtype=torch.int32, device=dev),
-           "match": torch.empty(B, dtype=torch.int32, device=dev),
-           "pos": torch.empty(B, dtype=torch.int32, device=dev)}
+    if out is None:
+        out = {"tokens": torch.empty((B, k), dtype=torch.int32, device=dev),
+               "count": torch.empty(B, dtype=torch.int32, device=dev),
+               "match": torch.empty(B, dtype=torch.int32, device=dev),
+               "pos": torch.empty(B, dtype=torch.int32, device=dev)}
     rc = load_library().stv_lookup_draft(
         _dev_ptr(history, torch.int32, "history"), _dev_ptr(lengths, torch.int32, "lengths", (B,)),
-        B, stride, n_min, n_max, k, out["tokens"].data_ptr() if k else None,
-        out["count"].data_ptr(), out["match"].data_ptr(), out["pos"].data_ptr(),
+        B, stride, n_min, n_max, k, _dev_ptr(out["tokens"], torch.int32, "tokens", (B, k)) if k else None,
+        _dev_ptr(out["count"], torch.int32, "count", (B,)),
+        _dev_ptr(out["match"], torch.int32, "match", (B,)),
+        _dev_ptr(out["pos"], torch.int32, "pos", (B,)),
         _dev_ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(dev))
     _check(rc)
     return out

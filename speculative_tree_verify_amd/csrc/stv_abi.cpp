@@ -422,6 +422,7 @@ int stv_lookup_draft(const int32_t *history, const int32_t *lengths, int32_t bat
     a.n_max = n_max;
     a.k = k;
     a.n_chunks = stv::lookup_chunks(stride);
+    a.vec16 = (stride % 4) == 0 && (reinterpret_cast<uintptr_t>(history) & 15u) == 0;
     a.ws = static_cast<uint64_t *>(workspace);
     a.tokens = tokens;
     a.count = count;

@@ -8,13 +8,14 @@
 
 namespace stv {
 
-constexpr int kLookupChunk = 2048;      // end positions per scan work-group
+constexpr int kLookupChunk = 4096;      // end positions per scan work-group
 constexpr int kLookupMaxN = 64;         // largest n_max
 
 struct LookupArgs {
     const int32_t *hist;    // [B][stride]
     const int32_t *len;     // [B], clamped to [0, stride] on the device
     int B, stride, n_min, n_max, k, n_chunks;
+    bool vec16;             // every row starts on a 16-byte boundary
     uint64_t *ws;           // [B][n_chunks] best (match << 32 | end) per chunk
     int32_t *tokens;        // [B][k]
     int32_t *count, *match, *pos;   // [B]

@@ -3,7 +3,7 @@
 // the tokens that followed (u/iamMess, lookup-augmented drafting; elpis, the
 // drafter-free n-gram chains).
 //
-// lookup_scan_kernel: one work-group per (2,048 end positions, sequence).
+// lookup_scan_kernel: one work-group per (4,096 end positions, sequence).
 //   Coalesced loads of h[e]; only positions whose token equals the last
 //   token extend the comparison backwards (a rare, divergent path), so the
 //   scan streams the history at HBM speed.  The candidate key
@@ -40,23 +40,47 @@ __global__ __launch_bounds__(kScanThreads) void lookup_scan_kernel(const LookupA
     const int tid = threadIdx.x;
     const int32_t *h = a.hist + (size_t)b * a.stride;
     const int N = clamp_len(a.len[b], a.stride);
+    // Thread tid covers positions c0 + 4*(tid + 256 j) + [0, 4): one 16-byte
+    // load per four positions when every row starts 16-byte aligned (checked
+    // on the host), else four 4-byte loads.  All of them are issued before
+    // the tail is read, so the chunk's loads overlap the tail's latency.
+    // Positions past N - 2 hold a token that cannot match (fixed below).
+    constexpr int J = kScanPer / 4;
+    const int c0 = chunk * kLookupChunk;
+    int v[J][4];
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        const int e4 = c0 + 4 * (tid + j * kScanThreads);
+        if (a.vec16 && e4 + 3 <= N - 2) {
+            const int4 q = *reinterpret_cast<const int4 *>(h + e4);
+            v[j][0] = q.x;
+            v[j][1] = q.y;
+            v[j][2] = q.z;
+            v[j][3] = q.w;
+        } else {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) v[j][u] = e4 + u <= N - 2 ? h[e4 + u] : 0;
+        }
+    }
     // tail[i] = h[N-1-i]; only i <= N-2 is ever compared
     if (tid < a.n_max && tid < N) tail[tid] = h[N - 1 - tid];
     __syncthreads();
     uint64_t best = 0;
     if (N >= 2) {
         const int last = tail[0];
-        const int e0 = chunk * kLookupChunk + tid;
 #pragma unroll
-        for (int j = 0; j < kScanPer; ++j) {
-            const int e = e0 + j * kScanThreads;
-            if (e <= N - 2 && h[e] == last) {
-                const int cap = min(a.n_max, e + 1);
-                int m = 1;
-                while (m < cap && h[e - m] == tail[m]) ++m;
-                if (m >= a.n_min) {
-                    const uint64_t key = ((uint64_t)m << 32) | (uint32_t)e;
-                    best = key > best ? key : best;
+        for (int j = 0; j < J; ++j) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int e = c0 + 4 * (tid + j * kScanThreads) + u;
+                if (v[j][u] == last && e <= N - 2) {
+                    const int cap = min(a.n_max, e + 1);
+                    int m = 1;
+                    while (m < cap && h[e - m] == tail[m]) ++m;
+                    if (m >= a.n_min) {
+                        const uint64_t key = ((uint64_t)m << 32) | (uint32_t)e;
+                        best = key > best ? key : best;
+                    }
                 }
             }
         }
@@ -65,9 +89,9 @@ __global__ __launch_bounds__(kScanThreads) void lookup_scan_kernel(const LookupA
     if ((tid & 63) == 0) red[tid >> 6] = best;
     __syncthreads();
     if (tid == 0) {
-        uint64_t v = red[0];
-        for (int w = 1; w < kScanThreads / 64; ++w) v = red[w] > v ? red[w] : v;
-        a.ws[(size_t)b * a.n_chunks + chunk] = v;
+        uint64_t w = red[0];
+        for (int i = 1; i < kScanThreads / 64; ++i) w = red[i] > w ? red[i] : w;
+        a.ws[(size_t)b * a.n_chunks + chunk] = w;
     }
 }
 

@@ -219,8 +219,8 @@ def test_accept_and_commit_argument_errors(lib, stvmod):
 def test_lookup_argument_errors(lib, stvmod):
     E = stvmod
     ws = ctypes.c_size_t()
-    assert lib.stv_lookup_plan(3, 5000, ctypes.byref(ws)) == E.STV_OK
-    assert ws.value == 3 * 3 * 8                     # ceil(4999 / 2048) = 3 chunks
+    assert lib.stv_lookup_plan(3, 9000, ctypes.byref(ws)) == E.STV_OK
+    assert ws.value == 3 * 3 * 8                     # ceil(8999 / 4096) = 3 chunks
     assert lib.stv_lookup_plan(-1, 10, ctypes.byref(ws)) == E.STV_EINVAL
     assert lib.stv_lookup_plan(1, 0, ctypes.byref(ws)) == E.STV_EINVAL
     f = lib.stv_lookup_draft

@@ -49,11 +49,11 @@ def test_long_histories_with_planted_copies(gpu, orc):
 
 
 def test_chunk_boundaries(gpu, orc):
-    """Matches that straddle the 2,048-position chunks of the scan."""
+    """Matches that straddle the 4,096-position chunks of the scan."""
     rng = np.random.default_rng(63)
-    for stride in (2047, 2048, 2049, 4097, 6145):
+    for stride in (4095, 4096, 4097, 8193, 12289):
         for shift in (0, 1, 5, 11):
             h = rng.integers(0, 1000, size=stride).astype(np.int32)
-            e = min(2047 + shift, stride - 20)
+            e = min(4095 + shift, stride - 20)
             h[stride - 12:] = h[e - 11:e + 1]
             _check(gpu, orc, h[None], [stride], 6, 12, 8)
