@@ -67,6 +67,13 @@ def _load():
         lib.orc_kv_commit.restype = i32
         lib.orc_lookup_draft.argtypes = [P, P, i32, i32, i32, i32, i32, P, P, P, P]
         lib.orc_lookup_draft.restype = None
+        lib.orc_quantize_kv4_row.argtypes = [P, i32, P]
+        lib.orc_quantize_kv4_row.restype = ctypes.c_uint16
+        for fn in (lib.orc_k4_quant_pack, lib.orc_v4_quant_pack):
+            fn.argtypes = [P, i32, i32, P, P, i32, i32, i32]
+            fn.restype = None
+        lib.orc_attention_i4.argtypes = lib.orc_attention.argtypes
+        lib.orc_attention_i4.restype = i32
         _lib = lib
     return _lib
 
@@ -191,12 +198,23 @@ def v_values(kv, head: int, key: int) -> np.ndarray:
 def attention(q, kv, ctx_len: int, mask=None, scale: float | None = None,
               k_begin: int = 0, k_end: int | None = None, rows=None,
               want_logits: bool = False):
+    """See attention_fmt; kv is the 3-bit cache, or the 4-bit per-token-head
+    cache when it has `fmt == "i4"`."""
+    return attention_fmt(q, kv, ctx_len, mask, scale, k_begin, k_end, rows, want_logits,
+                         getattr(kv, "fmt", "b3"))
+
+
+def attention_fmt(q, kv, ctx_len: int, mask=None, scale: float | None = None,
+                  k_begin: int = 0, k_end: int | None = None, rows=None,
+                  want_logits: bool = False, fmt: str = "b3"):
     """The oracle's attention for the rows listed (flattened t*Hq + h).
 
     kv: an object with k_codes, k_scales, v_codes, v_scales, n_kv_heads,
     head_dim, capacity (K token-major, V key-transposed; see stv_oracle.c).  mask: uint64 [T] ancestor masks, or None for the
     causal chunk rule.  Returns dict(out fp64 [n][D], lse fp64 [n],
-    qi8 int8 [n][D], sq fp32 [n], logits int64 [n][L+T][NB] or None).
+    qi8 int8 [n][D], sq fp32 [n], logits int64 [n][L+T][NB] (3-bit) or
+    [n][L+T] (4-bit), or None).  fmt: "b3" (3-bit, per-block scales) or "i4"
+    (4-bit, per token-head scales).
     """
     q = _c(q, np.float32)
     T, hq, d = q.shape
@@ -216,12 +234,14 @@ def attention(q, kv, ctx_len: int, mask=None, scale: float | None = None,
     lse = np.empty(n, dtype=np.float64)
     qi8 = np.empty((n, d), dtype=np.int8)
     sq = np.empty(n, dtype=np.float32)
-    logits = np.empty((n, n_keys, d // 32), dtype=np.int64) if want_logits else None
+    lshape = (n, n_keys, d // 32) if fmt == "b3" else (n, n_keys)
+    logits = np.empty(lshape, dtype=np.int64) if want_logits else None
     kc = _c(kv.k_codes, np.uint32)
     ks = _c(kv.k_scales, np.uint16)
     vc = _c(kv.v_codes, np.uint32)
     vs = _c(kv.v_scales, np.uint16)
-    rc = _load().orc_attention(_ptr(q), T, hq, _ptr(kc), _ptr(ks), _ptr(vc), _ptr(vs),
+    fn = _load().orc_attention if fmt == "b3" else _load().orc_attention_i4
+    rc = fn(_ptr(q), T, hq, _ptr(kc), _ptr(ks), _ptr(vc), _ptr(vs),
                                kv.n_kv_heads, d, kv.capacity, ctx_len, _ptr(m),
                                float(scale), k_begin, k_end, _ptr(rows_arr),
                                n if rows is not None else 0, _ptr(out), _ptr(lse),
@@ -290,3 +310,25 @@ def lookup_draft(history, lengths, n_min: int = 6, n_max: int = 12, k: int = 8):
     _load().orc_lookup_draft(_ptr(h), _ptr(ln), B, stride, n_min, n_max, k, _ptr(tokens),
                              _ptr(count), _ptr(match), _ptr(pos))
     return {"tokens": tokens, "count": count, "match": match, "pos": pos}
+
+
+# ------------------------------------------- 4-bit per-token-head format
+
+def quantize_kv4_row(x) -> tuple[np.ndarray, int]:
+    """(D/8 code words, fp16 scale bits) of one row (see orc_quantize_kv4_row)."""
+    x = _c(x, np.float32)
+    w = np.empty(x.size // 8, dtype=np.uint32)
+    s = _load().orc_quantize_kv4_row(_ptr(x), x.size, _ptr(w))
+    return w, int(s)
+
+
+def kv4_quant_pack(x, pos0: int, codes: np.ndarray, scales: np.ndarray, which: str) -> None:
+    """In-place 4-bit pack of x [n_tok][Hkv][D] at positions pos0.. into the
+    K (which="k") or V (which="v") arrays of the 4-bit cache."""
+    x = _c(x, np.float32)
+    n_tok, hkv, d = x.shape
+    assert codes.dtype == np.uint32 and scales.dtype == np.uint16
+    assert codes.flags["C_CONTIGUOUS"] and scales.flags["C_CONTIGUOUS"]
+    cap = scales.shape[1]
+    fn = _load().orc_k4_quant_pack if which == "k" else _load().orc_v4_quant_pack
+    fn(_ptr(x), n_tok, pos0, _ptr(codes), _ptr(scales), hkv, d, cap)

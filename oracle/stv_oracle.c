@@ -564,3 +564,170 @@ ORC_EXPORT void orc_lookup_draft(const int32_t *hist, const int32_t *len, int B,
         pos[b] = best_e;
     }
 }
+
+/* ------------------------------------- second KV format: 4-bit per token-head */
+
+/* The 4-bit per-token-head cache ("Qwen3.8-27B on one RTX 3090", the int4 KV
+ * section: 4-bit codes with one scale per token and KV head).  The pages give
+ * the granularity only; readings:
+ *  (i1) codes c in [0, 15] stand for s * (c - 8);
+ *  (i2) per (token, KV head) row of D elements: s16 = fp16_rne(amax / 7)
+ *       saturated to the largest finite fp16, code = clamp(rint(x / s), -8,
+ *       7) + 8, all codes 8 when s16 is zero (the 3-bit rule with 7 = 2^3 - 1);
+ *  (i3) K token-major: codes uint32 [Hkv][cap][D/8], element 8w + i in bits
+ *       [4i, 4i+4) of word w; scales fp16 [Hkv][cap].  V key-transposed in
+ *       32-key groups: codes uint32 [Hkv][ng][D][4], key 32*grp + e of
+ *       element d in word e/8 bits [4(e%8), +4) of row (grp, d); scales fp16
+ *       [Hkv][cap];
+ *  (i4) Q.K^T is one int64 sum over the whole row, x = scale * sq * sk * S. */
+static int nib_get(const uint32_t *w, int e) { return (int)((w[e / 8] >> (4 * (e % 8))) & 15u); }
+
+static void nib_set(uint32_t *w, int e, int c)
+{
+    w[e / 8] &= ~(15u << (4 * (e % 8)));
+    w[e / 8] |= (uint32_t)(c & 15) << (4 * (e % 8));
+}
+
+ORC_EXPORT uint16_t orc_quantize_kv4_row(const float *x, int D, uint32_t *w)
+{
+    float amax = 0.0f;
+    for (int e = 0; e < D; ++e) {
+        float a = fabsf(x[e]);
+        if (a > amax)
+            amax = a;
+    }
+    uint16_t s16 = orc_f32_to_f16(amax / 7.0f);
+    if ((s16 & 0x7FFFu) == 0x7C00u)
+        s16 = (uint16_t)((s16 & 0x8000u) | 0x7BFFu);
+    float s = (float)orc_f16_to_f64(s16);
+    for (int i = 0; i < D / 8; ++i)
+        w[i] = 0;
+    for (int e = 0; e < D; ++e) {
+        int c = 8;
+        if (s != 0.0f) {
+            float r = rintf(x[e] / s);
+            if (r < -8.0f)
+                r = -8.0f;
+            if (r > 7.0f)
+                r = 7.0f;
+            c = (int)r + 8;
+        }
+        nib_set(w, e, c);
+    }
+    return s16;
+}
+
+ORC_EXPORT void orc_k4_quant_pack(const float *x, int n_tok, int pos0, uint32_t *codes,
+                                  uint16_t *scales, int Hkv, int D, int cap)
+{
+    for (int t = 0; t < n_tok; ++t)
+        for (int g = 0; g < Hkv; ++g) {
+            size_t pos = (size_t)g * cap + (size_t)(pos0 + t);
+            scales[pos] = orc_quantize_kv4_row(x + ((size_t)t * Hkv + g) * D, D,
+                                               codes + pos * (size_t)(D / 8));
+        }
+}
+
+ORC_EXPORT void orc_v4_quant_pack(const float *x, int n_tok, int pos0, uint32_t *codes,
+                                  uint16_t *scales, int Hkv, int D, int cap)
+{
+    size_t ng = n_groups(cap);
+    uint32_t *w = malloc((size_t)(D / 8) * sizeof(uint32_t) + 1);
+    if (!w)
+        return;
+    for (int t = 0; t < n_tok; ++t)
+        for (int g = 0; g < Hkv; ++g) {
+            int pos = pos0 + t, grp = pos / 32, e = pos % 32;
+            scales[(size_t)g * cap + pos] = orc_quantize_kv4_row(x + ((size_t)t * Hkv + g) * D, D, w);
+            for (int d = 0; d < D; ++d)
+                nib_set(codes + (((size_t)g * ng + grp) * D + d) * 4, e, nib_get(w, d));
+        }
+    free(w);
+}
+
+/* As orc_attention, for the 4-bit per-token-head cache; logits [n][L+T]
+ * (one int64 sum per key). */
+ORC_EXPORT int orc_attention_i4(const float *q, int T, int Hq,
+                                const uint32_t *kc, const uint16_t *ks,
+                                const uint32_t *vc, const uint16_t *vs,
+                                int Hkv, int D, int cap, int L,
+                                const uint64_t *mask, double scale,
+                                int k_begin, int k_end,
+                                const int32_t *rows, int n_rows,
+                                double *out, double *lse, int64_t *logits,
+                                int8_t *qi8_out, float *sq_out)
+{
+    if (T < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || D <= 0 || D % 32 || L < 0 ||
+        L + T > cap || (mask && T > 64))
+        return -1;
+    int G = Hq / Hkv, N = L + T;
+    size_t ng = n_groups(cap);
+    if (!rows)
+        n_rows = T * Hq;
+    int bad = 0;
+
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int r = 0; r < n_rows; ++r) {
+        int flat = rows ? rows[r] : r;
+        if (flat < 0 || flat >= T * Hq) {
+            bad = 1;
+            continue;
+        }
+        int t = flat / Hq, h = flat % Hq, g = h / G;
+        int8_t *qi = (int8_t *)malloc((size_t)D);
+        double *x = (double *)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
+        char *vis = (char *)malloc((size_t)(N > 0 ? N : 1));
+        float sq;
+        orc_quantize_q_row(q + ((size_t)t * Hq + h) * D, D, qi, &sq);
+        if (qi8_out)
+            memcpy(qi8_out + (size_t)r * D, qi, (size_t)D);
+        if (sq_out)
+            sq_out[r] = sq;
+
+        double m = -INFINITY;
+        for (int j = 0; j < N; ++j) {
+            const uint32_t *kw = kc + ((size_t)g * cap + j) * (size_t)(D / 8);
+            int64_t s = 0;
+            for (int d = 0; d < D; ++d)
+                s += (int64_t)qi[d] * (int64_t)(nib_get(kw, d) - 8);
+            if (logits)
+                logits[(size_t)r * N + j] = s;
+            x[j] = scale * (double)sq * orc_f16_to_f64(ks[(size_t)g * cap + j]) * (double)s;
+            int v = (j >= k_begin && j < k_end);
+            if (v && j >= L) {
+                int a = j - L;
+                v = mask ? (int)((mask[t] >> a) & 1u) : (a <= t);
+            }
+            vis[j] = (char)v;
+            if (v && x[j] > m)
+                m = x[j];
+        }
+
+        double *o = out + (size_t)r * D;
+        for (int d = 0; d < D; ++d)
+            o[d] = 0.0;
+        if (m == -INFINITY) {
+            lse[r] = -INFINITY;
+        } else {
+            double l = 0.0;
+            for (int j = 0; j < N; ++j) {
+                if (!vis[j])
+                    continue;
+                double p = exp(x[j] - m);
+                l += p;
+                double sv = orc_f16_to_f64(vs[(size_t)g * cap + j]);
+                for (int d = 0; d < D; ++d) {
+                    const uint32_t *vw = vc + (((size_t)g * ng + (size_t)(j / 32)) * D + d) * 4;
+                    o[d] += p * (sv * (double)(nib_get(vw, j % 32) - 8));
+                }
+            }
+            for (int d = 0; d < D; ++d)
+                o[d] /= l;
+            lse[r] = m + log(l);
+        }
+        free(qi);
+        free(x);
+        free(vis);
+    }
+    return bad ? -1 : 0;
+}

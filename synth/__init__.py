@@ -88,6 +88,7 @@ class KVCache:
     head_dim: int
     capacity: int
     n_filled: int
+    fmt: str = "b3"
 
 
 def _scales(rng: np.random.Generator, shape) -> np.ndarray:
@@ -215,3 +216,32 @@ def make_lookup_history(rng: np.random.Generator, n_tokens: int, vocab: int, cop
                 continue                      # keep the planted span whole
             h[q:q + j] = h[n_tokens - j:]
     return h
+
+
+def make_kv4(rng: np.random.Generator, n_kv_heads: int, head_dim: int,
+             n_filled: int, capacity: int | None = None) -> KVCache:
+    """A 4-bit per-token-head cache (fmt "i4"):
+
+    K, token-major:    k_codes uint32 [Hkv][capacity][D/8] (8 codes per word),
+                       k_scales uint16 (fp16 bits) [Hkv][capacity]
+    V, key-transposed: v_codes uint32 [Hkv][ng][D][4] (32 keys per row),
+                       v_scales uint16 (fp16 bits) [Hkv][capacity]
+    Codes uniform in [0, 15], scales U(0.01, 0.1); positions past n_filled
+    (K) and groups past the last filled key (V) are zero.
+    """
+    if capacity is None:
+        capacity = n_filled
+    assert head_dim % 32 == 0 and 0 <= n_filled <= capacity
+    ng = (capacity + 31) // 32
+    kc = np.zeros((n_kv_heads, capacity, head_dim // 8), dtype=np.uint32)
+    ks = np.zeros((n_kv_heads, capacity), dtype=np.uint16)
+    vc = np.zeros((n_kv_heads, ng, head_dim, 4), dtype=np.uint32)
+    vs = np.zeros((n_kv_heads, capacity), dtype=np.uint16)
+    kc[:, :n_filled] = rng.integers(0, 2**32, size=(n_kv_heads, n_filled, head_dim // 8),
+                                    dtype=np.uint32)
+    ks[:, :n_filled] = _scales(rng, (n_kv_heads, n_filled))
+    g_used = (n_filled + 31) // 32
+    vc[:, :g_used] = rng.integers(0, 2**32, size=(n_kv_heads, g_used, head_dim, 4),
+                                  dtype=np.uint32)
+    vs[:, :n_filled] = _scales(rng, (n_kv_heads, n_filled))
+    return KVCache(kc, ks, vc, vs, n_kv_heads, head_dim, capacity, n_filled, "i4")
