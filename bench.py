@@ -72,15 +72,17 @@ def measured_traffic(kernel: str, workload: str):
         return None
 
 
-def work_of(geom: synth.Geometry, masks):
+def work_of(geom: synth.Geometry, masks, fmt: str = "b3"):
     """Algorithmic bytes and operations of one step (see the design notes)."""
     T, hq, hkv, d, L = geom.n_rows, geom.n_q_heads, geom.n_kv_heads, geom.head_dim, geom.ctx_len
     nb = d // 32
     n_keys = L + T
-    kv_bytes = n_keys * hkv * 2 * nb * (12 + 2)          # codes + fp16 scales, K and V
+    # codes + fp16 scales per (key, KV head), K and V
+    per_key_head = 2 * nb * (12 + 2) if fmt == "b3" else 2 * (d // 2 + 2)
+    kv_bytes = n_keys * hkv * per_key_head
     q_bytes = T * hq * d * 4
     out_bytes = T * hq * d * 4
-    append_bytes = 2 * T * hkv * d * 4 + 2 * T * hkv * nb * 14
+    append_bytes = 2 * T * hkv * d * 4 + T * hkv * per_key_head
     if masks is None:
         visible = sum(L + t + 1 for t in range(T)) * hq
     else:
@@ -96,12 +98,14 @@ def work_of(geom: synth.Geometry, masks):
 
 
 class Workload:
-    def __init__(self, geom: synth.Geometry, torch, stv, n_buffers=N_BUFFERS):
+    def __init__(self, geom: synth.Geometry, torch, stv, n_buffers=N_BUFFERS, fmt="b3"):
         self.g = geom
         self.torch = torch
         self.stv = stv
+        self.fmt = fmt
         rng = np.random.default_rng(geom.seed)
-        host = synth.make_kv(rng, geom.n_kv_heads, geom.head_dim, geom.n_keys)
+        make = synth.make_kv if fmt == "b3" else synth.make_kv4
+        host = make(rng, geom.n_kv_heads, geom.head_dim, geom.n_keys)
         self.host = host
         self.q_host = synth.make_q(rng, geom.n_rows, geom.n_q_heads, geom.head_dim)
         self.causal = geom.kind == "prefill"
@@ -116,14 +120,15 @@ class Workload:
         dev = "cuda"
         base = stv.KVCache.from_host(host, device=dev)
         self.caches = [base] + [stv.KVCache(base.k_codes.clone(), base.k_scales.clone(),
-                                            base.v_codes.clone(), base.v_scales.clone())
+                                            base.v_codes.clone(), base.v_scales.clone(), fmt)
                                 for _ in range(n_buffers - 1)]
         self.q = torch.from_numpy(self.q_host).to(dev)
         self.knew = torch.from_numpy(knew).to(dev)
         self.vnew = torch.from_numpy(vnew).to(dev)
         self.scale = 1.0 / math.sqrt(geom.head_dim)
         self.S, self.ws_bytes = stv.attention_plan(geom.n_rows, geom.n_q_heads, geom.n_kv_heads,
-                                                   geom.head_dim, geom.ctx_len, self.causal, 0)
+                                                   geom.head_dim, geom.ctx_len, self.causal, 0,
+                                                   fmt)
         T, hq, d = geom.n_rows, geom.n_q_heads, geom.head_dim
         self.part_o = self.part_lse = None
         if self.S > 1:
@@ -131,7 +136,7 @@ class Workload:
             self.part_lse = torch.empty((self.S, T, hq), dtype=torch.float32, device=dev)
         self.out = torch.empty((T, hq, d), dtype=torch.float32, device=dev)
         self.out_lse = torch.empty((T, hq), dtype=torch.float32, device=dev)
-        self.work = work_of(geom, self.mask)
+        self.work = work_of(geom, self.mask, fmt)
 
     def step(self, i, ev=None):
         stv, g = self.stv, self.g
@@ -288,7 +293,8 @@ def main():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="tree64_262k")
-    ap.add_argument("--extra", default="prefill_4k_32k,tree8_262k,decode_262k,decode_8k,tree64_32k",
+    ap.add_argument("--extra", default="prefill_4k_32k,tree8_262k,decode_262k,decode_8k,tree64_32k,"
+                                       "tree64_262k_i4,prefill_4k_32k_i4,tree8_262k_i4,decode_262k_i4",
                     help="comma-separated extra workloads ('' for none)")
     ap.add_argument("--extra-steps", type=int, default=10)
     ap.add_argument("--no-lookup", dest="lookup", action="store_false",
@@ -357,7 +363,8 @@ def main():
     for name in [n for n in args.extra.split(",") if n]:
         del wl
         torch.cuda.empty_cache()
-        wl = Workload(geoms[name], torch, stv)
+        base, fmt = (name[:-3], "i4") if name.endswith("_i4") else (name, "b3")
+        wl = Workload(geoms[base], torch, stv, fmt=fmt)
         rr = wl.run(args.extra_steps, 2)
         se = summarize(wl, rr, args.extra_steps)
         extra[name] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in se.items()}

@@ -66,10 +66,32 @@ extern "C" {
 
 #define STV_MAX_TREE_ROWS 64
 
-#define STV_K 0              /* stv_kv_quant_pack: the K layout */
-#define STV_V 1              /* stv_kv_quant_pack: the V layout */
+#define STV_K 0              /* stv_kv_quant_pack: K, 3-bit format */
+#define STV_V 1              /* stv_kv_quant_pack: V, 3-bit format */
+#define STV_K4 2             /* stv_kv_quant_pack: K, 4-bit per-token-head format */
+#define STV_V4 3             /* stv_kv_quant_pack: V, 4-bit per-token-head format */
 
-/* One layer's quantized cache (layout above).  Passed by [host] pointer. */
+/*
+ * Cache formats.
+ *  STV_KV_3BIT (the layout above): 3-bit codes, one fp16 scale per 32
+ *    elements of a (token, KV head) row.
+ *  STV_KV_4BIT_TOKEN: 4-bit codes c in [0, 15] standing for s * (c - 8), one
+ *    fp16 scale per (token, KV head) (the int4 per-token-head cache of the
+ *    "Qwen3.8-27B on one RTX 3090" page, int4 KV section):
+ *      k_codes  uint32 [Hkv][capacity][D/8]   element 8w + i in bits [4i, 4i+4)
+ *                                             of word w
+ *      k_scales uint16 [Hkv][capacity]        fp16 bits, one per (key, head)
+ *      v_codes  uint32 [Hkv][ng][D][4]        row (group, d): element d of the
+ *                                             group's 32 keys, key e in word
+ *                                             e/8 bits [4(e%8), +4)
+ *      v_scales uint16 [Hkv][capacity]        fp16 bits, one per (key, head)
+ *    k_codes and v_codes must be 16-byte aligned.  Q.K^T is one exact int32
+ *    sum per (row, key) over the whole head dimension.
+ */
+#define STV_KV_3BIT 0
+#define STV_KV_4BIT_TOKEN 1
+
+/* One layer's quantized cache (layouts above).  Passed by [host] pointer. */
 typedef struct stv_kv_layer {
     const uint32_t *k_codes;
     const uint16_t *k_scales;
@@ -78,12 +100,13 @@ typedef struct stv_kv_layer {
     int32_t n_kv_heads;
     int32_t head_dim;
     int32_t capacity;
+    int32_t kv_format;      /* STV_KV_3BIT or STV_KV_4BIT_TOKEN */
 } stv_kv_layer;
 
 /* Description of the last failure on the calling thread ("" after success). */
 const char *stv_last_error(void);
 
-/* ABI version; bumped on any incompatible change.  Currently 1. */
+/* ABI version; bumped on any incompatible change.  Currently 2. */
 int32_t stv_abi_version(void);
 
 /*
@@ -98,8 +121,12 @@ int32_t stv_abi_version(void);
  * Rule per 32-element block: s = fp16_rne(amax / 3) (the largest finite fp16
  * if that overflows), code = clamp(rint(x / s), -4, 3) + 4, all codes 4 when
  * s is zero; the division is correctly rounded and rint rounds half to even.
+ * which = STV_K4 / STV_V4 write the 4-bit per-token-head format instead:
+ * one scale per (token, head) row of head_dim elements, s = fp16_rne(amax /
+ * 7) (saturated likewise), code = clamp(rint(x / s), -8, 7) + 8, all codes 8
+ * when s is zero; scales are [n_kv_heads][capacity] for K and V alike.
  * Calls for the same tensor that touch the same 32-key group of V must not
- * run concurrently (they rewrite shared words).
+ * run concurrently (they rewrite shared words).  x must be 16-byte aligned.
  * Errors: STV_EINVAL (null pointer, n_tok < 0, bad head_dim, heads or
  * which), STV_ECAPACITY (pos0 < 0 or pos0 + n_tok > capacity), STV_EHIP.
  */
@@ -109,7 +136,8 @@ int stv_kv_quant_pack(const float *x, int32_t n_tok, int32_t pos0, int32_t which
 
 /*
  * stv_attention_plan -- the split plan a verify (causal = 0) or prefill
- * (causal = 1) call with these sizes will use, and the workspace it needs.
+ * (causal = 1) call with these sizes and cache format (STV_KV_3BIT or
+ * STV_KV_4BIT_TOKEN) will use, and the workspace it needs.
  *   n_splits_req  0 lets the library choose; otherwise the requested number
  *                 of context splits (the effective count may be lower: each
  *                 split covers a whole number of 32-key tiles)
@@ -118,7 +146,7 @@ int stv_kv_quant_pack(const float *x, int32_t n_tok, int32_t pos0, int32_t which
  * Errors: STV_EINVAL, STV_ECAPACITY is not checked here (no capacity given).
  */
 int stv_attention_plan(int32_t T, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
-                       int32_t ctx_len, int32_t causal, int32_t n_splits_req,
+                       int32_t ctx_len, int32_t causal, int32_t kv_format, int32_t n_splits_req,
                        int32_t *n_splits_out, size_t *workspace_bytes_out);
 
 /*
@@ -144,8 +172,9 @@ int stv_attention_plan(int32_t T, int32_t n_q_heads, int32_t n_kv_heads, int32_t
  *               (may be NULL when the plan has S = 1)
  *   n_splits    0 = automatic, else requested split count (see the plan)
  *   dbg_logits  nullable int32 [T][n_q_heads][ctx_len+T][head_dim/32]: the
- *               exact per-block integer Q.K^T sums; entries of keys a row
- *               cannot see are unspecified
+ *               exact per-block integer Q.K^T sums (3-bit format), or
+ *               [T][n_q_heads][ctx_len+T]: the exact whole-row sums (4-bit
+ *               format); entries of keys a row cannot see are unspecified
  *   dbg_q       nullable int8 [T][n_q_heads][head_dim]: the quantized Q
  *   dbg_qscale  nullable fp32 [T][n_q_heads]: the Q scales
  * Per-row Q quantizer: amax = max|q|; inv = 127 / amax (correctly rounded);

@@ -43,7 +43,12 @@ class _KVLayer(ctypes.Structure):
     _fields_ = [("k_codes", ctypes.c_void_p), ("k_scales", ctypes.c_void_p),
                 ("v_codes", ctypes.c_void_p), ("v_scales", ctypes.c_void_p),
                 ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
-                ("capacity", ctypes.c_int32)]
+                ("capacity", ctypes.c_int32), ("kv_format", ctypes.c_int32)]
+
+
+STV_KV_3BIT = 0
+STV_KV_4BIT_TOKEN = 1
+_FORMATS = {"b3": STV_KV_3BIT, "i4": STV_KV_4BIT_TOKEN}
 
 
 _lib = None
@@ -65,7 +70,7 @@ def load_library():
         lib.stv_kv_quant_pack.restype = ctypes.c_int
         lib.stv_kv_quant_pack.argtypes = [P, i32, i32, i32, P, P, i32, i32, i32, P]
         lib.stv_attention_plan.restype = ctypes.c_int
-        lib.stv_attention_plan.argtypes = [i32, i32, i32, i32, i32, i32, i32,
+        lib.stv_attention_plan.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32,
                                            ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_size_t)]
         lib.stv_verify_attention.restype = ctypes.c_int
         lib.stv_verify_attention.argtypes = [P, i32, i32, ctypes.POINTER(_KVLayer), i32, P,
@@ -125,21 +130,26 @@ def _stream(device):
 
 STV_K = 0
 STV_V = 1
+STV_K4 = 2
+STV_V4 = 3
 
 
 @dataclass
 class KVCache:
-    """One layer's 3-bit cache on the GPU (layouts as in include/stv.h).
+    """One layer's quantized cache on the GPU (layouts as in include/stv.h).
 
-    k_codes: int32 [Hkv][capacity][D/32][3] (32-bit words), k_scales: float16
-    [Hkv][capacity][D/32]; v_codes: int32 [Hkv][ng][D][3], v_scales: float16
-    [Hkv][ng][D/32][32] with ng = ceil(capacity / 32).  The capacity is that
-    of the K arrays.
+    fmt "b3" (3-bit, per-32-element scales): k_codes int32 [Hkv][cap][D/32][3],
+    k_scales float16 [Hkv][cap][D/32], v_codes int32 [Hkv][ng][D][3],
+    v_scales float16 [Hkv][ng][D/32][32].  fmt "i4" (4-bit, per-token-head
+    scales): k_codes int32 [Hkv][cap][D/8], k_scales float16 [Hkv][cap],
+    v_codes int32 [Hkv][ng][D][4], v_scales float16 [Hkv][cap].
+    ng = ceil(cap / 32); the capacity is that of the K arrays.
     """
     k_codes: "object"
     k_scales: "object"
     v_codes: "object"
     v_scales: "object"
+    fmt: str = "b3"
 
     @property
     def n_kv_heads(self) -> int:
@@ -151,14 +161,19 @@ class KVCache:
 
     @property
     def head_dim(self) -> int:
-        return int(self.k_codes.shape[2]) * 32
+        return int(self.k_codes.shape[2]) * (32 if self.fmt == "b3" else 8)
 
     @classmethod
-    def empty(cls, n_kv_heads: int, head_dim: int, capacity: int, device="cuda"):
+    def empty(cls, n_kv_heads: int, head_dim: int, capacity: int, device="cuda", fmt="b3"):
         torch = _torch()
         nb = head_dim // 32
         ng = (capacity + 31) // 32
         z = lambda shape, dt: torch.zeros(shape, dtype=dt, device=device)  # noqa: E731
+        if fmt == "i4":
+            return cls(z((n_kv_heads, capacity, head_dim // 8), torch.int32),
+                       z((n_kv_heads, capacity), torch.float16),
+                       z((n_kv_heads, ng, head_dim, 4), torch.int32),
+                       z((n_kv_heads, capacity), torch.float16), "i4")
         return cls(z((n_kv_heads, capacity, nb, 3), torch.int32),
                    z((n_kv_heads, capacity, nb), torch.float16),
                    z((n_kv_heads, ng, head_dim, 3), torch.int32),
@@ -166,23 +181,29 @@ class KVCache:
 
     @classmethod
     def from_host(cls, host, device="cuda"):
-        """Copy host arrays (uint32 codes, uint16 fp16-bit scales) to the GPU."""
+        """Copy host arrays (uint32 codes, uint16 fp16-bit scales) to the GPU;
+        the format is host.fmt when present, else "b3"."""
         torch = _torch()
 
         def up(a, view):
             return torch.from_numpy(np.ascontiguousarray(a).view(view)).to(device)
         return cls(up(host.k_codes, np.int32), up(host.k_scales, np.float16),
-                   up(host.v_codes, np.int32), up(host.v_scales, np.float16))
+                   up(host.v_codes, np.int32), up(host.v_scales, np.float16),
+                   getattr(host, "fmt", "b3"))
 
     def _layer(self) -> _KVLayer:
         torch = _torch()
         hkv, cap, d = self.n_kv_heads, self.capacity, self.head_dim
         nb, ng = d // 32, (cap + 31) // 32
-        return _KVLayer(_dev_ptr(self.k_codes, torch.int32, "k_codes", (hkv, cap, nb, 3)),
-                        _dev_ptr(self.k_scales, torch.float16, "k_scales", (hkv, cap, nb)),
-                        _dev_ptr(self.v_codes, torch.int32, "v_codes", (hkv, ng, d, 3)),
-                        _dev_ptr(self.v_scales, torch.float16, "v_scales", (hkv, ng, nb, 32)),
-                        hkv, d, cap)
+        if self.fmt == "i4":
+            shapes = ((hkv, cap, d // 8), (hkv, cap), (hkv, ng, d, 4), (hkv, cap))
+        else:
+            shapes = ((hkv, cap, nb, 3), (hkv, cap, nb), (hkv, ng, d, 3), (hkv, ng, nb, 32))
+        return _KVLayer(_dev_ptr(self.k_codes, torch.int32, "k_codes", shapes[0]),
+                        _dev_ptr(self.k_scales, torch.float16, "k_scales", shapes[1]),
+                        _dev_ptr(self.v_codes, torch.int32, "v_codes", shapes[2]),
+                        _dev_ptr(self.v_scales, torch.float16, "v_scales", shapes[3]),
+                        hkv, d, cap, _FORMATS[self.fmt])
 
 
 def kv_quant_pack(x, pos0: int, cache: KVCache, which: str):
@@ -196,21 +217,23 @@ def kv_quant_pack(x, pos0: int, cache: KVCache, which: str):
     if hkv != cache.n_kv_heads or d != cache.head_dim:
         raise ValueError("x does not match the cache's heads or head_dim")
     codes, scales = (cache.k_codes, cache.k_scales) if which == "k" else (cache.v_codes, cache.v_scales)
+    code = {("k", "b3"): STV_K, ("v", "b3"): STV_V, ("k", "i4"): STV_K4,
+            ("v", "i4"): STV_V4}[(which, cache.fmt)]
     rc = load_library().stv_kv_quant_pack(
-        _dev_ptr(x, torch.float32, "x"), n_tok, pos0, STV_K if which == "k" else STV_V,
+        _dev_ptr(x, torch.float32, "x"), n_tok, pos0, code,
         codes.data_ptr(), scales.data_ptr(), hkv, d, cache.capacity, _stream(x.device))
     _check(rc)
     del layer
 
 
 def attention_plan(T: int, n_q_heads: int, n_kv_heads: int, head_dim: int, ctx_len: int,
-                   causal: bool, n_splits: int = 0) -> tuple[int, int]:
+                   causal: bool, n_splits: int = 0, fmt: str = "b3") -> tuple[int, int]:
     """(effective split count, workspace bytes) of a call with these sizes."""
     s = ctypes.c_int32()
     ws = ctypes.c_size_t()
     _check(load_library().stv_attention_plan(T, n_q_heads, n_kv_heads, head_dim, ctx_len,
-                                             int(bool(causal)), n_splits, ctypes.byref(s),
-                                             ctypes.byref(ws)))
+                                             int(bool(causal)), _FORMATS[fmt], n_splits,
+                                             ctypes.byref(s), ctypes.byref(ws)))
     return int(s.value), int(ws.value)
 
 
@@ -222,7 +245,7 @@ def _attention(q, kv: KVCache, ctx_len: int, mask, softmax_scale, out, out_lse, 
         softmax_scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty((T, hq, d), dtype=torch.float32, device=q.device)
-    S, ws_bytes = attention_plan(T, hq, kv.n_kv_heads, d, ctx_len, causal, n_splits)
+    S, ws_bytes = attention_plan(T, hq, kv.n_kv_heads, d, ctx_len, causal, n_splits, kv.fmt)
     if ws_bytes and workspace is None:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
     ws_ptr = None
@@ -234,7 +257,8 @@ def _attention(q, kv: KVCache, ctx_len: int, mask, softmax_scale, out, out_lse, 
     dbg_ptrs = (None, None, None)
     if debug:
         names = ("logits", "q8", "qscale") if debug is True else tuple(debug)
-        shapes = {"logits": ((T, hq, ctx_len + T, d // 32), torch.int32),
+        lshape = (T, hq, ctx_len + T, d // 32) if kv.fmt == "b3" else (T, hq, ctx_len + T)
+        shapes = {"logits": (lshape, torch.int32),
                   "q8": ((T, hq, d), torch.int8), "qscale": ((T, hq), torch.float32)}
         dbg = {k: torch.zeros(shapes[k][0], dtype=shapes[k][1], device=q.device) for k in names}
         dbg_ptrs = tuple(dbg[k].data_ptr() if k in dbg else None
@@ -290,7 +314,7 @@ def attention_partials(q, kv: KVCache, ctx_len: int, anc_mask=None, softmax_scal
     T, hq, d = q.shape
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(d)
-    S, _ = attention_plan(T, hq, kv.n_kv_heads, d, ctx_len, anc_mask is None, n_splits)
+    S, _ = attention_plan(T, hq, kv.n_kv_heads, d, ctx_len, anc_mask is None, n_splits, kv.fmt)
     if part_o is None:
         part_o = torch.empty((S, T, hq, d), dtype=torch.float32, device=q.device)
     if part_lse is None:

@@ -65,6 +65,11 @@ int check_kv(const stv_kv_layer *kv, int Hq, int L, int T) {
     int rc = check_heads(Hq, kv->n_kv_heads, kv->head_dim);
     if (rc) return rc;
     if (kv->capacity <= 0) return fail(STV_EINVAL, "capacity must be positive");
+    if (kv->kv_format != STV_KV_3BIT && kv->kv_format != STV_KV_4BIT_TOKEN)
+        return fail(STV_EINVAL, "kv_format %d unknown", kv->kv_format);
+    if (kv->kv_format == STV_KV_4BIT_TOKEN &&
+        ((reinterpret_cast<uintptr_t>(kv->k_codes) | reinterpret_cast<uintptr_t>(kv->v_codes)) & 15u))
+        return fail(STV_EINVAL, "4-bit k_codes and v_codes must be 16-byte aligned");
     if (L < 0) return fail(STV_EINVAL, "ctx_len must be >= 0");
     if ((long long)L + T > kv->capacity)
         return fail(STV_ECAPACITY, "ctx_len + T = %lld exceeds capacity %d", (long long)L + T, kv->capacity);
@@ -96,7 +101,8 @@ int attention_common(const float *q, int T, int Hq, const stv_kv_layer *kv, int 
     const int D = kv->head_dim, Hkv = kv->n_kv_heads;
     if (dbg_logits && (long long)T * Hq * (L + T) * (D / 32) >= (1ll << 40))
         return fail(STV_EINVAL, "dbg_logits would be too large");
-    const stv::Plan plan = stv::make_plan(T, Hq, Hkv, D, L, causal, n_splits);
+    const int fmt = kv->kv_format;
+    const stv::Plan plan = stv::make_plan(T, Hq, Hkv, D, L, causal, n_splits, fmt);
     if (!partials_only && plan.S > 1 && (!ws || ws_bytes < plan.ws_bytes))
         return fail(STV_EWORKSPACE, "workspace of %zu bytes needed for %d splits (got %zu)",
                     plan.ws_bytes, plan.S, ws ? ws_bytes : (size_t)0);
@@ -141,7 +147,7 @@ int attention_common(const float *q, int T, int Hq, const stv_kv_layer *kv, int 
     hipStream_t st = static_cast<hipStream_t>(stream);
     const bool debug = dbg_logits || dbg_q || dbg_qscale;
     hipError_t e = plan.dec ? stv::launch_attention_dec(a, D, causal, debug, st)
-                            : stv::launch_attention(a, D, plan.NW, causal, debug, st);
+                            : stv::launch_attention(a, D, plan.NW, causal, debug, fmt, st);
     if (e != hipSuccess) return fail(STV_EHIP, "attention launch failed: %s", hipGetErrorString(e));
     if (!partials_only && plan.S > 1) {
         e = stv::launch_merge(a.part_o, a.part_lse, plan.S, (int)rows, D, out, out_lse, st);
@@ -154,12 +160,13 @@ int attention_common(const float *q, int T, int Hq, const stv_kv_layer *kv, int 
 
 namespace stv {
 
-long long attention_slots(int D, int NW, bool causal, bool dec) {
+long long attention_slots(int D, int NW, bool causal, bool dec, int fmt) {
     // MI355X: 256 CUs; the D = 256 four-wave kernels hold two work-groups per CU.
     constexpr long long kFallback = 256LL * 2;
     struct Entry {
         int dev, D, NW;
         bool causal, dec;
+        int fmt;
         long long slots;
     };
     static std::mutex mu;
@@ -171,7 +178,8 @@ long long attention_slots(int D, int NW, bool causal, bool dec) {
     }
     std::lock_guard<std::mutex> lock(mu);
     for (const Entry &e : cache)
-        if (e.dev == dev && e.D == D && e.NW == NW && e.causal == causal && e.dec == dec)
+        if (e.dev == dev && e.D == D && e.NW == NW && e.causal == causal && e.dec == dec &&
+            e.fmt == fmt)
             return e.slots;
     int cus = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
@@ -179,17 +187,19 @@ long long attention_slots(int D, int NW, bool causal, bool dec) {
         (void)hipGetLastError();
         return kFallback;
     }
-    const int per_cu = dec ? attention_dec_wgs_per_cu(D, causal) : attention_wgs_per_cu(D, NW, causal);
+    const int per_cu =
+        dec ? attention_dec_wgs_per_cu(D, causal) : attention_wgs_per_cu(D, NW, causal, fmt);
     const long long slots = per_cu > 0 ? (long long)cus * per_cu : kFallback;
-    cache.push_back({dev, D, NW, causal, dec, slots});
+    cache.push_back({dev, D, NW, causal, dec, fmt, slots});
     return slots;
 }
 
-Plan make_plan(int T, int Hq, int Hkv, int D, int L, bool causal, int n_splits_req) {
+Plan make_plan(int T, int Hq, int Hkv, int D, int L, bool causal, int n_splits_req, int fmt) {
     Plan p;
     const int G = Hq / Hkv;
     const long long R = (long long)T * G;
-    p.dec = R <= kDecMaxRows;
+    // the few-row kernel reads the 3-bit format only
+    p.dec = R <= kDecMaxRows && fmt == 0;
     if (p.dec) {
         p.NW = 4;
         p.NRG = 1;
@@ -207,7 +217,7 @@ Plan make_plan(int T, int Hq, int Hkv, int D, int L, bool causal, int n_splits_r
         // Fill the device's resident work-group slots exactly once: one
         // round of equal work-groups, no straggling partial round.  Splits
         // keep at least four tiles.
-        const long long slots = attention_slots(D, p.NW, causal, p.dec);
+        const long long slots = attention_slots(D, p.NW, causal, p.dec, fmt);
         const long long groups = (long long)Hkv * p.NRG;
         if (groups < slots) {
             S = slots / groups;
@@ -250,12 +260,13 @@ extern "C" {
 
 const char *stv_last_error(void) { return g_err; }
 
-int32_t stv_abi_version(void) { return 1; }
+int32_t stv_abi_version(void) { return 2; }
 
 int stv_kv_quant_pack(const float *x, int32_t n_tok, int32_t pos0, int32_t which,
                       uint32_t *codes, uint16_t *scales, int32_t n_kv_heads, int32_t head_dim,
                       int32_t capacity, void *stream) {
-    if (which != STV_K && which != STV_V) return fail(STV_EINVAL, "which must be STV_K or STV_V");
+    if (which != STV_K && which != STV_V && which != STV_K4 && which != STV_V4)
+        return fail(STV_EINVAL, "which must be STV_K, STV_V, STV_K4 or STV_V4");
     if (n_tok < 0) return fail(STV_EINVAL, "n_tok must be >= 0");
     if (n_kv_heads <= 0) return fail(STV_EINVAL, "n_kv_heads must be positive");
     if (!head_dim_ok(head_dim)) return fail(STV_EINVAL, "head_dim %d unsupported (64, 128 or 256)", head_dim);
@@ -265,15 +276,22 @@ int stv_kv_quant_pack(const float *x, int32_t n_tok, int32_t pos0, int32_t which
                     (long long)pos0 + n_tok - 1, capacity);
     if (n_tok == 0) return ok();
     if (!x || !codes || !scales) return fail(STV_EINVAL, "x, codes and scales must not be NULL");
-    hipError_t e = stv::launch_kv_pack(x, n_tok, pos0, codes, scales, n_kv_heads, head_dim,
-                                       capacity, which == STV_V, static_cast<hipStream_t>(stream));
+    if ((reinterpret_cast<uintptr_t>(x) & 15u) != 0) return fail(STV_EINVAL, "x must be 16-byte aligned");
+    const bool four = which == STV_K4 || which == STV_V4;
+    const bool is_v = which == STV_V || which == STV_V4;
+    hipError_t e = four ? stv::launch_kv_pack4(x, n_tok, pos0, codes, scales, n_kv_heads, head_dim,
+                                               capacity, is_v, static_cast<hipStream_t>(stream))
+                        : stv::launch_kv_pack(x, n_tok, pos0, codes, scales, n_kv_heads, head_dim,
+                                              capacity, is_v, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(STV_EHIP, "kv pack launch failed: %s", hipGetErrorString(e));
     return ok();
 }
 
 int stv_attention_plan(int32_t T, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
-                       int32_t ctx_len, int32_t causal, int32_t n_splits_req,
+                       int32_t ctx_len, int32_t causal, int32_t kv_format, int32_t n_splits_req,
                        int32_t *n_splits_out, size_t *workspace_bytes_out) {
+    if (kv_format != STV_KV_3BIT && kv_format != STV_KV_4BIT_TOKEN)
+        return fail(STV_EINVAL, "kv_format %d unknown", kv_format);
     if (T < 1) return fail(STV_EINVAL, "T must be >= 1");
     if (!causal && T > STV_MAX_TREE_ROWS) return fail(STV_EINVAL, "verify supports at most 64 tree rows");
     int rc = check_heads(n_q_heads, n_kv_heads, head_dim);
@@ -282,7 +300,7 @@ int stv_attention_plan(int32_t T, int32_t n_q_heads, int32_t n_kv_heads, int32_t
     if (n_splits_req < 0) return fail(STV_EINVAL, "n_splits must be >= 0");
     if ((long long)T * n_q_heads >= (1ll << 31)) return fail(STV_EINVAL, "T * n_q_heads too large");
     const stv::Plan p = stv::make_plan(T, n_q_heads, n_kv_heads, head_dim, ctx_len, causal != 0,
-                                       n_splits_req);
+                                       n_splits_req, kv_format);
     if (n_splits_out) *n_splits_out = p.S;
     if (workspace_bytes_out) *workspace_bytes_out = p.ws_bytes;
     return ok();
@@ -364,6 +382,7 @@ int stv_kv_commit(const stv_kv_layer *kv, int32_t ctx_len, int32_t T, const int3
     if (D != 64 && D != 128 && D != 256) return fail(STV_EINVAL, "head_dim must be 64, 128 or 256");
     if (kv->n_kv_heads < 1) return fail(STV_EINVAL, "n_kv_heads must be >= 1");
     if (kv->capacity <= 0) return fail(STV_EINVAL, "capacity must be positive");
+    if (kv->kv_format != STV_KV_3BIT) return fail(STV_EINVAL, "kv_commit moves the 3-bit format only");
     if (ctx_len < 0) return fail(STV_EINVAL, "ctx_len must be >= 0");
     if ((long long)ctx_len + T > kv->capacity)
         return fail(STV_ECAPACITY, "ctx_len + T = %lld exceeds capacity %d", (long long)ctx_len + T,

@@ -48,17 +48,19 @@ struct Plan {
 
 // Work-groups of the attention kernels that fit on one CU at once, from the
 // runtime's occupancy calculator; 0 when no device answers.
-int attention_wgs_per_cu(int D, int NW, bool causal);
+// fmt: 0 = 3-bit codes with per-32-element scales, 1 = 4-bit codes with
+// per-token-head scales.
+int attention_wgs_per_cu(int D, int NW, bool causal, int fmt);
 int attention_dec_wgs_per_cu(int D, bool causal);
 
 // Resident work-group slots of the current device for a kernel variant
 // (CUs x work-groups per CU); a fixed MI355X figure when no device answers.
-long long attention_slots(int D, int NW, bool causal, bool dec);
+long long attention_slots(int D, int NW, bool causal, bool dec, int fmt);
 
-Plan make_plan(int T, int Hq, int Hkv, int D, int L, bool causal, int n_splits_req);
+Plan make_plan(int T, int Hq, int Hkv, int D, int L, bool causal, int n_splits_req, int fmt);
 
 // Launchers return the hipError_t of the launch.
-hipError_t launch_attention(const AttnArgs &a, int D, int NW, bool causal, bool debug,
+hipError_t launch_attention(const AttnArgs &a, int D, int NW, bool causal, bool debug, int fmt,
                             hipStream_t stream);
 hipError_t launch_attention_dec(const AttnArgs &a, int D, bool causal, bool debug,
                                 hipStream_t stream);
@@ -67,5 +69,8 @@ hipError_t launch_merge(const float *part_o, const float *part_lse, int S, int r
 hipError_t launch_kv_pack(const float *x, int n_tok, int pos0, uint32_t *codes,
                           uint16_t *scales, int Hkv, int D, int cap, bool is_v,
                           hipStream_t stream);
+hipError_t launch_kv_pack4(const float *x, int n_tok, int pos0, uint32_t *codes,
+                           uint16_t *scales, int Hkv, int D, int cap, bool is_v,
+                           hipStream_t stream);
 
 }  // namespace stv

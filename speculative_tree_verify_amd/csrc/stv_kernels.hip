@@ -20,6 +20,8 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 namespace stv {
 namespace {
 
@@ -176,6 +178,85 @@ __global__ void v_code_kernel(const float *__restrict__ x, int n_tok, int pos0,
     w[2] = w2;
 }
 
+// ---- 4-bit per-token-head pack.  One wave per (token, head): lane l holds
+// elements 8l .. 8l+7 (l < D/8); scale fp16(amax / 7) saturated, code
+// clamp(rint(x / s), -8, 7) + 8, all 8 when the scale is zero.  K writes its
+// word directly; V writes the scales here and the codes in v4_code_kernel.
+__device__ __forceinline__ uint16_t row_scale4(float amax) {
+    _Float16 sh = (_Float16)(amax / 7.0f);              // RNE to binary16
+    uint16_t s16 = __builtin_bit_cast(uint16_t, sh);
+    if ((s16 & 0x7FFFu) == 0x7C00u) s16 = 0x7BFFu;
+    return s16;
+}
+
+__device__ __forceinline__ uint32_t code4_of(float x, float s) {
+    if (s == 0.0f) return 8u;
+    float r = rintf(x / s);
+    r = fminf(fmaxf(r, -8.0f), 7.0f);
+    return (uint32_t)((int)r + 8);
+}
+
+template <bool IS_V>
+__global__ __launch_bounds__(64) void kv4_pack_kernel(const float *__restrict__ x, int n_tok,
+                                                      int pos0, uint32_t *__restrict__ codes,
+                                                      uint16_t *__restrict__ scales, int Hkv,
+                                                      int D, int cap) {
+    const int t = blockIdx.x / Hkv, g = blockIdx.x - (blockIdx.x / Hkv) * Hkv;
+    const int l = threadIdx.x;
+    const bool act = l < D / 8;
+    const float *xr = x + ((size_t)t * Hkv + g) * D + 8 * l;
+    float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    float amax = 0.0f;
+    if (act) {
+        const f32x4 a0 = *reinterpret_cast<const f32x4 *>(xr);
+        const f32x4 a1 = *reinterpret_cast<const f32x4 *>(xr + 4);
+        v[0] = a0.x; v[1] = a0.y; v[2] = a0.z; v[3] = a0.w;
+        v[4] = a1.x; v[5] = a1.y; v[6] = a1.z; v[7] = a1.w;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[e]));
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+    const uint16_t s16 = row_scale4(amax);
+    const size_t pos = (size_t)g * cap + (size_t)(pos0 + t);
+    if (l == 0) scales[pos] = s16;
+    if (!IS_V && act) {
+        const float s = half_bits_to_float(s16);
+        uint32_t w = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) w |= code4_of(v[e], s) << (4 * e);
+        codes[pos * (size_t)(D / 8) + l] = w;
+    }
+}
+
+// V codes: one thread per (group, head, d) row of four words, over the new
+// keys of that group; scales come from kv4_pack_kernel<true>.
+__global__ void v4_code_kernel(const float *__restrict__ x, int n_tok, int pos0,
+                               uint32_t *__restrict__ codes, const uint16_t *__restrict__ scales,
+                               int Hkv, int D, int cap, int ng, int grp0, int n_grp) {
+    const long long total = (long long)n_grp * Hkv * D;
+    const long long id = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (id >= total) return;
+    const int d = (int)(id % D);
+    const int g = (int)((id / D) % Hkv);
+    const int grp = grp0 + (int)(id / ((long long)D * Hkv));
+    uint32_t *w = codes + (((size_t)g * ng + grp) * D + d) * 4;
+    uint32_t ww[4] = {w[0], w[1], w[2], w[3]};
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+        const int pos = grp * 32 + e;
+        if (pos >= pos0 && pos < pos0 + n_tok) {
+            const float xv = x[((size_t)(pos - pos0) * Hkv + g) * D + d];
+            const uint32_t c = code4_of(xv, half_bits_to_float(scales[(size_t)g * cap + pos]));
+            ww[e / 8] = (ww[e / 8] & ~(15u << (4 * (e % 8)))) | (c << (4 * (e % 8)));
+        }
+    }
+    w[0] = ww[0];
+    w[1] = ww[1];
+    w[2] = ww[2];
+    w[3] = ww[3];
+}
+
 // ------------------------------------------------------------ attention
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -198,7 +279,9 @@ struct TileLds {
     int8_t kq[kKeyTile * KQS];
     _Float16 vt[D * VTS + NB * VBPAD];
     float skf[NB * kKeyTile];
-    alignas(16) uint16_t svs[D];   // the tile's V scales, [D/32][32 keys]
+    // the tile's V scales: [D/32][32 keys] (3-bit), or per wave [NW][32 keys]
+    // (4-bit per-token-head)
+    alignas(16) uint16_t svs[D > 128 ? D : 128];
 };
 
 // One (key, block) item of the K side: 3 code words and the fp16 scale.
@@ -325,7 +408,126 @@ struct TileIo {
     }
 };
 
-template <int D, int NW, bool CAUSAL, bool DEBUG>
+// ---- the 4-bit per-token-head format: 8 codes per word (element 8w + i in
+// bits 4i), one fp16 scale per (token, KV head) for K and for V.
+struct KItem4 {
+    uint32_t w[4];      // elements 32b .. 32b+31 of one key
+    uint16_t s;         // the key's scale (items with b == 0), else 0
+};
+struct VItem4 {
+    uint32_t w[4];      // element d of the tile's 32 keys
+};
+
+// K codes become int8 (c - 8) * 16 = (c ^ 8) << 4, with the even elements
+// of each 8-element group first: bytes e0 e2 e4 e6 | e1 e3 e5 e7.  The Q
+// operand uses the same order, so the int32 sums are those of the natural
+// order times 16 (exact; the 1/16 goes into the key's scale).
+template <int D, int NT>
+struct TileIo4 {
+    static constexpr int NB = D / 32;
+    static constexpr int KI = kKeyTile * NB;
+    static constexpr int VI = D;
+    static constexpr int KPT = (KI + NT - 1) / NT;
+    static constexpr int VPT = (VI + NT - 1) / NT;
+    KItem4 k[KPT];
+    VItem4 v[VPT];
+    uint16_t vs;        // V scale of key (lane % 32) of the tile, lanes 0..31 of each wave
+
+    __device__ __forceinline__ void load(const AttnArgs &a, int head, int kb, int k1, int tid) {
+        const size_t head_base = (size_t)head * a.cap;
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) {
+            const int item = tid + i * NT;
+            const int kk = item / NB, b = item % NB;
+            const int key = kb + kk;
+            k[i].w[0] = k[i].w[1] = k[i].w[2] = k[i].w[3] = 0u;
+            k[i].s = 0;
+            if (item < KI && key < k1) {
+                const u32x4 w = *reinterpret_cast<const u32x4 *>(
+                    a.kc + (head_base + key) * (D / 8) + 4 * b);
+                k[i].w[0] = w[0];
+                k[i].w[1] = w[1];
+                k[i].w[2] = w[2];
+                k[i].w[3] = w[3];
+                if (b == 0) k[i].s = a.ks[head_base + key];
+            }
+        }
+        const size_t grp_base = (size_t)head * a.ngroups + (size_t)(kb / kKeyTile);
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) {
+            const int d = tid + i * NT;
+            v[i].w[0] = v[i].w[1] = v[i].w[2] = v[i].w[3] = 0u;
+            if (d < VI) {
+                const u32x4 w = *reinterpret_cast<const u32x4 *>(a.vc + (grp_base * D + d) * 4);
+                v[i].w[0] = w[0];
+                v[i].w[1] = w[1];
+                v[i].w[2] = w[2];
+                v[i].w[3] = w[3];
+            }
+        }
+        const int lane = tid & 63;
+        // keys past the range get scale 0, so their V^ is exactly 0
+        vs = (lane < kKeyTile && kb + lane < k1) ? a.vs[head_base + kb + lane] : (uint16_t)0;
+    }
+
+    __device__ __forceinline__ void store(TileLds<D> &t, int tid) const {
+        using L = TileLds<D>;
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) {
+            const int item = tid + i * NT;
+            if (item < KI) {
+                const int kk = item / NB, b = item % NB;
+                uint32_t o[8];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    o[2 * j] = ((k[i].w[j] << 4) & 0xF0F0F0F0u) ^ 0x80808080u;
+                    o[2 * j + 1] = (k[i].w[j] & 0xF0F0F0F0u) ^ 0x80808080u;
+                }
+                *reinterpret_cast<u32x4 *>(t.kq + kk * L::KQS + 32 * b) = u32x4{o[0], o[1], o[2], o[3]};
+                *reinterpret_cast<u32x4 *>(t.kq + kk * L::KQS + 32 * b + 16) = u32x4{o[4], o[5], o[6], o[7]};
+                if (b == 0) t.skf[kk] = half_bits_to_float(k[i].s) * 0.0625f;
+            }
+        }
+        // V scales: every wave stages the tile's 32 key scales for its rows.
+        const int wave = tid >> 6, lane = tid & 63;
+        if (lane < kKeyTile) t.svs[wave * kKeyTile + lane] = vs;
+        wave_lds_sync();
+        const uint32_t *sv32 = reinterpret_cast<const uint32_t *>(t.svs + wave * kKeyTile);
+        const f16x2 off = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) {
+            const int d = tid + i * NT;
+            if (d < VI) {
+                uint32_t row[16];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    // keys 8j + 2m (low nibbles) and 8j + 2m + 1 (high nibbles)
+                    const uint32_t lo = v[i].w[j] & 0x0F0F0F0Fu;
+                    const uint32_t hi = (v[i].w[j] >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        // binary16 bits 0x6400 | c = 1024 + c; minus 1032 is c - 8, exactly
+                        const uint32_t sel = (uint32_t)m | 0x0C00u | ((uint32_t)(4 + m) << 16) | 0x0C000000u;
+                        const uint32_t pr = __builtin_amdgcn_perm(hi, lo, sel) | 0x64006400u;
+                        const uint32_t sw = sv32[4 * j + m];
+                        const f16x2 val = (__builtin_bit_cast(f16x2, pr) + off) *
+                                          __builtin_bit_cast(f16x2, sw);
+                        row[4 * j + m] = __builtin_bit_cast(uint32_t, val);
+                    }
+                }
+                u32x4 *dst = reinterpret_cast<u32x4 *>(t.vt + d * L::VTS + (d / 32) * L::VBPAD);
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    dst[j] = u32x4{row[4 * j], row[4 * j + 1], row[4 * j + 2], row[4 * j + 3]};
+            }
+        }
+    }
+};
+
+template <int D, int NT, int FMT>
+using TileIoOf = typename std::conditional<FMT == 0, TileIo<D, NT>, TileIo4<D, NT>>::type;
+
+template <int D, int NW, bool CAUSAL, bool DEBUG, int FMT>
 __global__ __launch_bounds__(NW * 64) void attn_split_kernel(const AttnArgs a) {
     constexpr int NB = D / 32;
     constexpr int KT = kKeyTile;
@@ -411,7 +613,19 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(const AttnArgs a) {
             }
         }
 #pragma unroll
-        for (int b = 0; b < NB; ++b) *reinterpret_cast<i32x4 *>(q_lane + 32 * b) = qreg[b];
+        for (int b = 0; b < NB; ++b) {
+            i32x4 w = qreg[b];
+            if constexpr (FMT == 1) {
+                // even elements of each 8-element group first, as the K codes
+                const uint32_t q0 = (uint32_t)w[0], q1 = (uint32_t)w[1];
+                const uint32_t q2 = (uint32_t)w[2], q3 = (uint32_t)w[3];
+                w[0] = (int32_t)__builtin_amdgcn_perm(q1, q0, 0x06040200u);
+                w[1] = (int32_t)__builtin_amdgcn_perm(q1, q0, 0x07050301u);
+                w[2] = (int32_t)__builtin_amdgcn_perm(q3, q2, 0x06040200u);
+                w[3] = (int32_t)__builtin_amdgcn_perm(q3, q2, 0x07050301u);
+            }
+            *reinterpret_cast<i32x4 *>(q_lane + 32 * b) = w;
+        }
         if (DEBUG && split == 0 && row_ok) {
             if (a.dbg_q) {
 #pragma unroll
@@ -448,7 +662,7 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(const AttnArgs a) {
     float m_run = -INFINITY;
     float l_run = 0.0f;
 
-    TileIo<D, NT> io;
+    TileIoOf<D, NT, FMT> io;
     if (k0 < k1) io.load(a, head, k0, k1, tid);
 
     for (int kb = k0; kb < k1; kb += KT) {
@@ -457,37 +671,63 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(const AttnArgs a) {
         if (kb + KT < k1) io.load(a, head, kb + KT, k1, tid);
 
         if (wave_active) {
-            // ---- Q.K^T: one int8 MFMA per 32-element block, fp32 epilogue.
-            // The MFMA of block b + 1 is issued before the epilogue of block b
-            // reads its results, so the matrix unit and the VALU overlap.
             f32x16 acc = f32x16{};
-            i32x16 s_cur = __builtin_amdgcn_mfma_i32_32x32x32_i8(
-                *reinterpret_cast<const i32x4 *>(kq_lane),
-                *reinterpret_cast<const i32x4 *>(q_lane), i32x16{}, 0, 0, 0);
+            if constexpr (FMT == 0) {
+                // ---- Q.K^T: one int8 MFMA per 32-element block, fp32 epilogue.
+                // The MFMA of block b + 1 is issued before the epilogue of block b
+                // reads its results, so the matrix unit and the VALU overlap.
+                i32x16 s_cur = __builtin_amdgcn_mfma_i32_32x32x32_i8(
+                    *reinterpret_cast<const i32x4 *>(kq_lane),
+                    *reinterpret_cast<const i32x4 *>(q_lane), i32x16{}, 0, 0, 0);
 #pragma unroll
-            for (int b = 0; b < NB; ++b) {
-                i32x16 s_next;
-                if (b + 1 < NB)
-                    s_next = __builtin_amdgcn_mfma_i32_32x32x32_i8(
-                        *reinterpret_cast<const i32x4 *>(kq_lane + 32 * (b + 1)),
-                        *reinterpret_cast<const i32x4 *>(q_lane + 32 * (b + 1)), i32x16{}, 0, 0, 0);
-                const f32x4 s0 = *reinterpret_cast<const f32x4 *>(lds.skf + b * KT + 8 * hl);
-                const f32x4 s1 = *reinterpret_cast<const f32x4 *>(lds.skf + b * KT + 8 * hl + 4);
-                const f32x4 s2 = *reinterpret_cast<const f32x4 *>(lds.skf + b * KT + 16 + 8 * hl);
-                const f32x4 s3 = *reinterpret_cast<const f32x4 *>(lds.skf + b * KT + 16 + 8 * hl + 4);
+                for (int b = 0; b < NB; ++b) {
+                    i32x16 s_next;
+                    if (b + 1 < NB)
+                        s_next = __builtin_amdgcn_mfma_i32_32x32x32_i8(
+                            *reinterpret_cast<const i32x4 *>(kq_lane + 32 * (b + 1)),
+                            *reinterpret_cast<const i32x4 *>(q_lane + 32 * (b + 1)), i32x16{}, 0, 0, 0);
+                    const f32x4 s0 = *reinterpret_cast<const f32x4 *>(lds.skf + b * KT + 8 * hl);
+                    const f32x4 s1 = *reinterpret_cast<const f32x4 *>(lds.skf + b * KT + 8 * hl + 4);
+                    const f32x4 s2 = *reinterpret_cast<const f32x4 *>(lds.skf + b * KT + 16 + 8 * hl);
+                    const f32x4 s3 = *reinterpret_cast<const f32x4 *>(lds.skf + b * KT + 16 + 8 * hl + 4);
+                    const float skr[16] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w,
+                                           s2.x, s2.y, s2.z, s2.w, s3.x, s3.y, s3.z, s3.w};
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[r] = fmaf(skr[r], (float)s_cur[r], acc[r]);
+                    if (DEBUG && a.dbg_logits && row_ok) {
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int key = kb + (r < 8 ? 8 * hl + r : 16 + 8 * hl + (r - 8));
+                            if (key < k1)
+                                a.dbg_logits[((size_t)flat * a.N + key) * NB + b] = s_cur[r];
+                        }
+                    }
+                    if (b + 1 < NB) s_cur = s_next;
+                }
+            } else {
+                // ---- 4-bit per-token-head: the int8 MFMAs of all blocks
+                // accumulate one int32 sum per (row, key), scaled once.
+                i32x16 s_acc = i32x16{};
+#pragma unroll
+                for (int b = 0; b < NB; ++b)
+                    s_acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(
+                        *reinterpret_cast<const i32x4 *>(kq_lane + 32 * b),
+                        *reinterpret_cast<const i32x4 *>(q_lane + 32 * b), s_acc, 0, 0, 0);
+                const f32x4 s0 = *reinterpret_cast<const f32x4 *>(lds.skf + 8 * hl);
+                const f32x4 s1 = *reinterpret_cast<const f32x4 *>(lds.skf + 8 * hl + 4);
+                const f32x4 s2 = *reinterpret_cast<const f32x4 *>(lds.skf + 16 + 8 * hl);
+                const f32x4 s3 = *reinterpret_cast<const f32x4 *>(lds.skf + 16 + 8 * hl + 4);
                 const float skr[16] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w,
                                        s2.x, s2.y, s2.z, s2.w, s3.x, s3.y, s3.z, s3.w};
 #pragma unroll
-                for (int r = 0; r < 16; ++r) acc[r] = fmaf(skr[r], (float)s_cur[r], acc[r]);
+                for (int r = 0; r < 16; ++r) acc[r] = skr[r] * (float)s_acc[r];
                 if (DEBUG && a.dbg_logits && row_ok) {
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const int key = kb + (r < 8 ? 8 * hl + r : 16 + 8 * hl + (r - 8));
-                        if (key < k1)
-                            a.dbg_logits[((size_t)flat * a.N + key) * NB + b] = s_cur[r];
+                        if (key < k1) a.dbg_logits[(size_t)flat * a.N + key] = s_acc[r] >> 4;
                     }
                 }
-                if (b + 1 < NB) s_cur = s_next;
             }
 
             // ---- mask, online softmax in base 2.  c_row >= 0, so the row max
@@ -1071,46 +1311,47 @@ __global__ __launch_bounds__(kMergeMaxThreads) void merge_kernel(
     }
 }
 
-template <int D, int NW, bool CAUSAL, bool DEBUG>
+template <int D, int NW, bool CAUSAL, bool DEBUG, int FMT>
 hipError_t launch_t(const AttnArgs &a, hipStream_t stream) {
     const int grid = a.n_hs_pad * a.NRG;
-    hipLaunchKernelGGL((attn_split_kernel<D, NW, CAUSAL, DEBUG>), dim3(grid), dim3(NW * 64), 0,
-                       stream, a);
+    hipLaunchKernelGGL((attn_split_kernel<D, NW, CAUSAL, DEBUG, FMT>), dim3(grid), dim3(NW * 64),
+                       0, stream, a);
     return hipGetLastError();
 }
 
-template <int D, int NW>
+template <int D, int NW, int FMT>
 hipError_t launch_d(const AttnArgs &a, bool causal, bool debug, hipStream_t s) {
-    if (causal) return debug ? launch_t<D, NW, true, true>(a, s) : launch_t<D, NW, true, false>(a, s);
-    return debug ? launch_t<D, NW, false, true>(a, s) : launch_t<D, NW, false, false>(a, s);
+    if (causal)
+        return debug ? launch_t<D, NW, true, true, FMT>(a, s) : launch_t<D, NW, true, false, FMT>(a, s);
+    return debug ? launch_t<D, NW, false, true, FMT>(a, s) : launch_t<D, NW, false, false, FMT>(a, s);
 }
 
-template <int D>
+template <int D, int FMT>
 hipError_t launch_nw(const AttnArgs &a, int NW, bool causal, bool debug, hipStream_t s) {
     switch (NW) {
-        case 1: return launch_d<D, 1>(a, causal, debug, s);
-        case 2: return launch_d<D, 2>(a, causal, debug, s);
-        case 4: return launch_d<D, 4>(a, causal, debug, s);
+        case 1: return launch_d<D, 1, FMT>(a, causal, debug, s);
+        case 2: return launch_d<D, 2, FMT>(a, causal, debug, s);
+        case 4: return launch_d<D, 4, FMT>(a, causal, debug, s);
         default: return hipErrorInvalidValue;
     }
 }
 
-template <int D, int NW, bool CAUSAL>
+template <int D, int NW, bool CAUSAL, int FMT>
 int occupancy_t() {
     int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &n, reinterpret_cast<const void *>(&attn_split_kernel<D, NW, CAUSAL, false>), NW * 64,
-            0) != hipSuccess)
+            &n, reinterpret_cast<const void *>(&attn_split_kernel<D, NW, CAUSAL, false, FMT>),
+            NW * 64, 0) != hipSuccess)
         return 0;
     return n;
 }
 
-template <int D>
+template <int D, int FMT>
 int occupancy_d(int NW, bool causal) {
     switch (NW) {
-        case 1: return causal ? occupancy_t<D, 1, true>() : occupancy_t<D, 1, false>();
-        case 2: return causal ? occupancy_t<D, 2, true>() : occupancy_t<D, 2, false>();
-        case 4: return causal ? occupancy_t<D, 4, true>() : occupancy_t<D, 4, false>();
+        case 1: return causal ? occupancy_t<D, 1, true, FMT>() : occupancy_t<D, 1, false, FMT>();
+        case 2: return causal ? occupancy_t<D, 2, true, FMT>() : occupancy_t<D, 2, false, FMT>();
+        case 4: return causal ? occupancy_t<D, 4, true, FMT>() : occupancy_t<D, 4, false, FMT>();
         default: return 0;
     }
 }
@@ -1159,21 +1400,37 @@ hipError_t launch_attention_dec(const AttnArgs &a, int D, bool causal, bool debu
     }
 }
 
-int attention_wgs_per_cu(int D, int NW, bool causal) {
+int attention_wgs_per_cu(int D, int NW, bool causal, int fmt) {
+    if (fmt == 1) {
+        switch (D) {
+            case 64: return occupancy_d<64, 1>(NW, causal);
+            case 128: return occupancy_d<128, 1>(NW, causal);
+            case 256: return occupancy_d<256, 1>(NW, causal);
+            default: return 0;
+        }
+    }
     switch (D) {
-        case 64: return occupancy_d<64>(NW, causal);
-        case 128: return occupancy_d<128>(NW, causal);
-        case 256: return occupancy_d<256>(NW, causal);
+        case 64: return occupancy_d<64, 0>(NW, causal);
+        case 128: return occupancy_d<128, 0>(NW, causal);
+        case 256: return occupancy_d<256, 0>(NW, causal);
         default: return 0;
     }
 }
 
-hipError_t launch_attention(const AttnArgs &a, int D, int NW, bool causal, bool debug,
+hipError_t launch_attention(const AttnArgs &a, int D, int NW, bool causal, bool debug, int fmt,
                             hipStream_t stream) {
+    if (fmt == 1) {
+        switch (D) {
+            case 64: return launch_nw<64, 1>(a, NW, causal, debug, stream);
+            case 128: return launch_nw<128, 1>(a, NW, causal, debug, stream);
+            case 256: return launch_nw<256, 1>(a, NW, causal, debug, stream);
+            default: return hipErrorInvalidValue;
+        }
+    }
     switch (D) {
-        case 64: return launch_nw<64>(a, NW, causal, debug, stream);
-        case 128: return launch_nw<128>(a, NW, causal, debug, stream);
-        case 256: return launch_nw<256>(a, NW, causal, debug, stream);
+        case 64: return launch_nw<64, 0>(a, NW, causal, debug, stream);
+        case 128: return launch_nw<128, 0>(a, NW, causal, debug, stream);
+        case 256: return launch_nw<256, 0>(a, NW, causal, debug, stream);
         default: return hipErrorInvalidValue;
     }
 }
@@ -1217,6 +1474,29 @@ hipError_t launch_kv_pack(const float *x, int n_tok, int pos0, uint32_t *codes, 
     hipLaunchKernelGGL(v_code_kernel, dim3((unsigned)((rows + threads - 1) / threads)),
                        dim3(threads), 0, stream, x, n_tok, pos0, codes, scales, Hkv, D, ng, grp0,
                        n_grp);
+    return hipGetLastError();
+}
+
+hipError_t launch_kv_pack4(const float *x, int n_tok, int pos0, uint32_t *codes, uint16_t *scales,
+                           int Hkv, int D, int cap, bool is_v, hipStream_t stream) {
+    if (n_tok == 0) return hipSuccess;
+    const int rows = n_tok * Hkv;
+    if (!is_v) {
+        hipLaunchKernelGGL(kv4_pack_kernel<false>, dim3(rows), dim3(64), 0, stream, x, n_tok, pos0,
+                           codes, scales, Hkv, D, cap);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL(kv4_pack_kernel<true>, dim3(rows), dim3(64), 0, stream, x, n_tok, pos0,
+                       codes, scales, Hkv, D, cap);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int ng = (cap + 31) / 32;
+    const int grp0 = pos0 / 32, n_grp = (pos0 + n_tok - 1) / 32 - grp0 + 1;
+    const long long items = (long long)n_grp * Hkv * D;
+    const int threads = 256;
+    hipLaunchKernelGGL(v4_code_kernel, dim3((unsigned)((items + threads - 1) / threads)),
+                       dim3(threads), 0, stream, x, n_tok, pos0, codes, scales, Hkv, D, cap, ng,
+                       grp0, n_grp);
     return hipGetLastError();
 }
 

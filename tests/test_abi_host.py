@@ -55,7 +55,7 @@ def test_library_exports_every_declared_symbol(lib, stvmod):
     for name in _declared():
         assert name in exported, name
         assert hasattr(lib, name)
-    assert lib.stv_abi_version() == 1
+    assert lib.stv_abi_version() == 2
 
 
 def _layer(stvmod, hkv=4, d=256, cap=1000):
@@ -99,6 +99,25 @@ def test_verify_argument_errors(lib, stvmod):
     assert _verify(lib, stvmod, layer=layer) == E.STV_EINVAL
 
 
+def test_format_errors(lib, stvmod):
+    E = stvmod
+    layer = stvmod._KVLayer(FAKE, FAKE, FAKE, FAKE, 4, 256, 1000, 7)
+    assert _verify(lib, stvmod, layer=layer) == E.STV_EINVAL
+    assert "kv_format" in _err(lib)
+    unaligned = stvmod._KVLayer(FAKE + 4, FAKE, FAKE, FAKE, 4, 256, 1000, 1)
+    assert _verify(lib, stvmod, layer=unaligned) == E.STV_EINVAL
+    assert "aligned" in _err(lib)
+    s, ws = ctypes.c_int32(), ctypes.c_size_t()
+    assert lib.stv_attention_plan(8, 24, 4, 256, 100, 0, 2, 0, ctypes.byref(s),
+                                  ctypes.byref(ws)) == E.STV_EINVAL
+    f = lib.stv_kv_quant_pack
+    assert f(FAKE, 10, 0, 4, FAKE, FAKE, 4, 256, 100, None) == E.STV_EINVAL
+    assert f(FAKE + 4, 10, 0, 2, FAKE, FAKE, 4, 256, 100, None) == E.STV_EINVAL   # x alignment
+    i4 = stvmod._KVLayer(FAKE, FAKE, FAKE, FAKE, 4, 256, 1000, 1)
+    assert lib.stv_kv_commit(ctypes.byref(i4), 0, 8, FAKE, FAKE, None) == E.STV_EINVAL
+    assert "3-bit" in _err(lib)
+
+
 def test_verify_mask_errors(lib, stvmod):
     E = stvmod
     good = synth.ancestor_masks(np.array([-1, 0, 0, 1, 1, 2, 3, 6]))
@@ -122,7 +141,7 @@ def _big_plan_args(stvmod, lib, T):
     L = 60000
     s = ctypes.c_int32()
     ws = ctypes.c_size_t()
-    assert lib.stv_attention_plan(T, 24, 4, 256, L, 0, 0, ctypes.byref(s), ctypes.byref(ws)) == 0
+    assert lib.stv_attention_plan(T, 24, 4, 256, L, 0, 0, 0, ctypes.byref(s), ctypes.byref(ws)) == 0
     assert s.value > 1 and ws.value > 0
     return L, ws.value
 
@@ -175,7 +194,7 @@ def test_kv_pack_argument_errors(lib, stvmod):
         assert f(None, 10, 0, which, FAKE, FAKE, 4, 256, 100, None) == E.STV_EINVAL
         assert f(FAKE, 0, 100, which, FAKE, FAKE, 4, 256, 100, None) == E.STV_OK   # nothing to do
         assert _err(lib) == ""
-    assert f(FAKE, 10, 0, 2, FAKE, FAKE, 4, 256, 100, None) == E.STV_EINVAL
+    assert f(FAKE, 10, 0, 4, FAKE, FAKE, 4, 256, 100, None) == E.STV_EINVAL
     assert "which" in _err(lib)
 
 
@@ -242,9 +261,10 @@ def test_lookup_argument_errors(lib, stvmod):
     (1, 24, 4, 256, 8192, 0), (64, 24, 4, 256, 32768, 0), (64, 24, 4, 256, 262144, 0),
     (8, 24, 4, 256, 262144, 0), (4096, 24, 4, 256, 32768, 1), (8, 4, 1, 64, 512, 0),
 ])
-def test_plan_is_consistent(stvmod, T, hq, hkv, d, L, causal):
+@pytest.mark.parametrize("fmt", ["b3", "i4"])
+def test_plan_is_consistent(stvmod, T, hq, hkv, d, L, causal, fmt):
     for req in (0, 1, 3, 17, 100000):
-        S, ws = stvmod.attention_plan(T, hq, hkv, d, L, bool(causal), req)
+        S, ws = stvmod.attention_plan(T, hq, hkv, d, L, bool(causal), req, fmt)
         n_tiles = -(-(L + T) // 32)
         assert 1 <= S <= n_tiles
         if req:

@@ -1,0 +1,126 @@
+"""GPU parity for the second KV format (4-bit codes, one scale per token-head)
+against the oracle: int8 Q and the whole-row int32 Q.K^T sums bit-exact,
+outputs within 2e-3 per row (max_d |o - o_ref| / max_d |o_ref|), lse within
+2e-3; the 4-bit pack bit-exact."""
+import math
+
+import numpy as np
+import pytest
+
+import synth
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-3
+
+
+@pytest.fixture(scope="module")
+def gpu():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import speculative_tree_verify_amd as stv
+    stv.load_library()
+    return stv, torch
+
+
+def _row_err(got, ref):
+    den = np.max(np.abs(ref), axis=-1)
+    return np.max(np.abs(got - ref), axis=-1) / np.where(den > 0, den, 1.0)
+
+
+def _visible(T, L, mask, n):
+    vis = np.zeros((T, n), dtype=bool)
+    vis[:, :L] = True
+    for t in range(T):
+        for a in range(T):
+            vis[t, L + a] = (a <= t) if mask is None else bool((int(mask[t]) >> a) & 1)
+    return vis
+
+
+def run4(gpu, orc, hq, hkv, d, L, T, kind, seed, n_splits=0, rows=None, check_logits=True):
+    stv, torch = gpu
+    rng = np.random.default_rng(seed)
+    host = synth.make_kv4(rng, hkv, d, L + T, L + T + 3)
+    q = synth.make_q(rng, T, hq, d)
+    mask = None
+    if kind == "chain":
+        mask = synth.ancestor_masks(synth.chain_parents(T))
+    elif kind == "tree":
+        mask = synth.ancestor_masks(synth.make_tree_parents(rng, T, 8))
+    scale = 1.0 / math.sqrt(d)
+    ref = orc.attention(q, host, L, mask, scale, rows=rows, want_logits=check_logits)
+    kv = stv.KVCache.from_host(host)
+    qd = torch.from_numpy(q).cuda()
+    lse = torch.empty((T, hq), dtype=torch.float32, device="cuda")
+
+    def call(debug):
+        if kind == "prefill":
+            return stv.prefill_attention(qd, kv, L, scale, out_lse=lse, n_splits=n_splits,
+                                         debug=debug)
+        return stv.verify_attention(qd, kv, L, mask, scale, out_lse=lse, n_splits=n_splits,
+                                    debug=debug)
+
+    flat = np.arange(T * hq) if rows is None else np.asarray(rows)
+    out = call(False)
+    torch.cuda.synchronize()
+    o = out.reshape(T * hq, d).cpu().numpy()[flat]
+    assert np.all(np.isfinite(o))
+    err = _row_err(o, ref["out"])
+    assert err.max() <= TOL, f"max row error {err.max():.3g}"
+    assert np.max(np.abs(lse.reshape(-1).cpu().numpy()[flat] - ref["lse"])) <= TOL
+    names = ("logits", "q8", "qscale") if check_logits else ("q8", "qscale")
+    _, dbg = call(names)
+    torch.cuda.synchronize()
+    assert np.array_equal(dbg["q8"].reshape(T * hq, d).cpu().numpy()[flat], ref["qi8"])
+    assert np.array_equal(dbg["qscale"].reshape(-1).cpu().numpy()[flat].view(np.uint32),
+                          ref["sq"].view(np.uint32))
+    if check_logits:
+        lg = dbg["logits"].reshape(T * hq, L + T).cpu().numpy()[flat]
+        vis = _visible(T, L, mask, L + T)
+        for i, r in enumerate(flat):
+            v = vis[r // hq]
+            assert np.array_equal(lg[i][v], ref["logits"][i][v]), f"logits differ, row {r}"
+    return err.max()
+
+
+CASES = [
+    ("tiny_chain", 4, 1, 64, 512, 8, "chain", 0, 0),
+    ("tiny_3split", 4, 1, 64, 512, 8, "chain", 0, 3),
+    ("tree64_ragged", 24, 4, 256, 1000, 64, "tree", 201, 0),
+    ("tree8_d128", 8, 2, 128, 777, 8, "tree", 202, 0),
+    ("tree17_d128", 8, 2, 128, 333, 17, "tree", 203, 5),
+    ("decode_t1", 24, 4, 256, 2049, 1, "tree", 204, 0),
+    ("tree_L0", 4, 2, 64, 0, 5, "tree", 205, 0),
+    ("prefill_small", 12, 2, 128, 100, 70, "prefill", 206, 0),
+    ("prefill_splits", 8, 1, 64, 300, 40, "prefill", 207, 4),
+]
+
+
+@pytest.mark.parametrize("name,hq,hkv,d,L,T,kind,seed,ns", CASES, ids=[c[0] for c in CASES])
+def test_parity_int4(gpu, orc, name, hq, hkv, d, L, T, kind, seed, ns):
+    run4(gpu, orc, hq, hkv, d, L, T, kind, seed, n_splits=ns)
+
+
+def test_full_size_tree_sampled_rows(gpu, orc):
+    rows = np.linspace(0, 64 * 24 - 1, 24).round().astype(np.int32)
+    run4(gpu, orc, 24, 4, 256, 65536, 64, "tree", 208, rows=rows, check_logits=False)
+
+
+@pytest.mark.parametrize("d,pos0,n_tok", [(64, 0, 1), (128, 29, 8), (256, 61, 64), (256, 0, 100)])
+def test_pack4_matches_oracle(gpu, orc, d, pos0, n_tok):
+    stv, torch = gpu
+    rng = np.random.default_rng(pos0 + d)
+    hkv, cap = 3, pos0 + n_tok + 40
+    x = (rng.standard_normal((n_tok, hkv, d)) * 10.0 ** rng.uniform(-2, 2)).astype(np.float32)
+    x[0, 0, :] = 0.0                                   # a zero row: scale 0, codes 8
+    host = synth.make_kv4(rng, hkv, d, cap, cap)
+    kv = stv.KVCache.from_host(host)
+    xd = torch.from_numpy(x).cuda()
+    stv.kv_quant_pack(xd, pos0, kv, "k")
+    stv.kv_quant_pack(xd, pos0, kv, "v")
+    torch.cuda.synchronize()
+    orc.kv4_quant_pack(x, pos0, host.k_codes, host.k_scales, "k")
+    orc.kv4_quant_pack(x, pos0, host.v_codes, host.v_scales, "v")
+    assert np.array_equal(kv.k_codes.cpu().numpy().view(np.uint32), host.k_codes)
+    assert np.array_equal(kv.k_scales.cpu().numpy().view(np.uint16), host.k_scales)
+    assert np.array_equal(kv.v_codes.cpu().numpy().view(np.uint32), host.v_codes)
+    assert np.array_equal(kv.v_scales.cpu().numpy().view(np.uint16), host.v_scales)
