@@ -315,7 +315,9 @@ def main():
     import speculative_tree_verify_amd as stv
     stv.load_library()
     geoms = {g.name: g for g in synth.CONFIGS + synth.EXTRA_CONFIGS}
-    wl = Workload(geoms[args.workload], torch, stv)
+    wbase, wfmt = ((args.workload[:-3], "i4") if args.workload.endswith("_i4")
+                   else (args.workload, "b3"))
+    wl = Workload(geoms[wbase], torch, stv, fmt=wfmt)
     r = wl.run(args.steps, args.warmup)
     s = summarize(wl, r, args.steps)
     g = wl.g
@@ -358,7 +360,7 @@ def main():
         },
     }
     extra = {}
-    if wl.mask is not None:
+    if wl.mask is not None and wl.fmt == "b3":
         extra[f"accept_commit_{g.name}"] = accept_commit_bench(wl, args.extra_steps)
     for name in [n for n in args.extra.split(",") if n]:
         del wl
@@ -391,7 +393,7 @@ def main():
     if args.cpu_rows > 0:
         del wl
         torch.cuda.empty_cache()
-        wl = Workload(geoms[args.workload], torch, stv, n_buffers=1)
+        wl = Workload(geoms[wbase], torch, stv, n_buffers=1, fmt=wfmt)
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_rows)
     print(json.dumps(line), flush=True)
 

@@ -163,16 +163,25 @@ __global__ void v_code_kernel(const float *__restrict__ x, int n_tok, int pos0,
     const int g = (int)((id / D) % Hkv);
     const int grp = grp0 + (int)(id / ((long long)D * Hkv));
     uint32_t *w = codes + (((size_t)g * ng + grp) * D + d) * 3;
-    uint32_t w0 = w[0], w1 = w[1], w2 = w[2];
     const uint16_t *srow = scales + (((size_t)g * ng + grp) * NB + d / 32) * 32;
+    // All loads first (the new keys of this group are a contiguous run), so
+    // they are in flight together; then the read-modify-write of the row.
+    const int e0 = max(0, pos0 - grp * 32), e1 = min(32, pos0 + n_tok - grp * 32);
+    float xv[32];
+    uint16_t sv[32];
 #pragma unroll
     for (int e = 0; e < 32; ++e) {
-        const int pos = grp * 32 + e;
-        if (pos >= pos0 && pos < pos0 + n_tok) {
-            const float xv = x[((size_t)(pos - pos0) * Hkv + g) * D + d];
-            set_code(w0, w1, w2, e, code_of(xv, half_bits_to_float(srow[e])));
+        xv[e] = 0.0f;
+        sv[e] = 0;
+        if (e >= e0 && e < e1) {
+            xv[e] = x[((size_t)(grp * 32 + e - pos0) * Hkv + g) * D + d];
+            sv[e] = srow[e];
         }
     }
+    uint32_t w0 = w[0], w1 = w[1], w2 = w[2];
+#pragma unroll
+    for (int e = 0; e < 32; ++e)
+        if (e >= e0 && e < e1) set_code(w0, w1, w2, e, code_of(xv[e], half_bits_to_float(sv[e])));
     w[0] = w0;
     w[1] = w1;
     w[2] = w2;
@@ -241,13 +250,23 @@ __global__ void v4_code_kernel(const float *__restrict__ x, int n_tok, int pos0,
     const int g = (int)((id / D) % Hkv);
     const int grp = grp0 + (int)(id / ((long long)D * Hkv));
     uint32_t *w = codes + (((size_t)g * ng + grp) * D + d) * 4;
+    const int e0 = max(0, pos0 - grp * 32), e1 = min(32, pos0 + n_tok - grp * 32);
+    float xv[32];
+    uint16_t sv[32];
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+        xv[e] = 0.0f;
+        sv[e] = 0;
+        if (e >= e0 && e < e1) {
+            xv[e] = x[((size_t)(grp * 32 + e - pos0) * Hkv + g) * D + d];
+            sv[e] = scales[(size_t)g * cap + grp * 32 + e];
+        }
+    }
     uint32_t ww[4] = {w[0], w[1], w[2], w[3]};
 #pragma unroll
     for (int e = 0; e < 32; ++e) {
-        const int pos = grp * 32 + e;
-        if (pos >= pos0 && pos < pos0 + n_tok) {
-            const float xv = x[((size_t)(pos - pos0) * Hkv + g) * D + d];
-            const uint32_t c = code4_of(xv, half_bits_to_float(scales[(size_t)g * cap + pos]));
+        if (e >= e0 && e < e1) {
+            const uint32_t c = code4_of(xv[e], half_bits_to_float(sv[e]));
             ww[e / 8] = (ww[e / 8] & ~(15u << (4 * (e % 8)))) | (c << (4 * (e % 8)));
         }
     }
@@ -268,7 +287,8 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 //        VTS = 40 keeps the B128 operand reads conflict-free; the per-block
 //        pad of 16 dwords spreads the four blocks written by one wave over
 //        all 64 banks.
-//   skf: fp32 K scales, [D/32][32 keys]
+//   skh: fp16 K scales, [D/32][32 keys] (3-bit format); skf: fp32 K scale
+//        per key (4-bit per-token-head format)
 //   svs: fp16 V scales as stored, [D/32][32 keys]
 template <int D>
 struct TileLds {
@@ -278,7 +298,8 @@ struct TileLds {
     static constexpr int VBPAD = 32;
     int8_t kq[kKeyTile * KQS];
     _Float16 vt[D * VTS + NB * VBPAD];
-    float skf[NB * kKeyTile];
+    float skf[kKeyTile];                  // fp32 K scales per key (4-bit format)
+    alignas(16) _Float16 skh[NB * kKeyTile];  // fp16 K scales [D/32][32 keys] (3-bit format)
     // the tile's V scales: [D/32][32 keys] (3-bit), or per wave [NW][32 keys]
     // (4-bit per-token-head)
     alignas(16) uint16_t svs[D > 128 ? D : 128];
@@ -315,43 +336,48 @@ struct TileIo {
     KItem k[KPT];
     VItem v[VPT];
 
-    __device__ __forceinline__ void load(const AttnArgs &a, int head, int kb, int k1, int tid) {
+    // Loads go through buffer descriptors based at the tile and sized to the
+    // keys below k1 (zero size for a tile at or past k1, based at k0), so
+    // entries past the range read as zero and every lane issues the same
+    // loads: the waits for one register set never wait for another.  The V
+    // scales past the range are zeroed by store().
+    __device__ __forceinline__ void load(const AttnArgs &a, int head, int kb, int k0, int k1,
+                                         int tid) {
+        const bool valid = kb < k1;
+        const int kt = valid ? kb : k0;
+        const int nk = valid ? min(kKeyTile, k1 - kb) : 0;
         const size_t head_base = (size_t)head * a.cap;
+        const size_t grp = (size_t)head * a.ngroups + (size_t)(kt / kKeyTile);
+        const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint32_t *>(a.kc + (head_base + kt) * NB * 3), (short)0, nk * NB * 12, kBufWord3);
+        const __amdgpu_buffer_rsrc_t rks = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t *>(a.ks + (head_base + kt) * NB), (short)0, nk * NB * 2, kBufWord3);
+        const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint32_t *>(a.vc + grp * D * 3), (short)0, valid ? D * 12 : 0, kBufWord3);
+        const __amdgpu_buffer_rsrc_t rvs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t *>(a.vs + grp * D), (short)0, valid ? D * 2 : 0, kBufWord3);
 #pragma unroll
         for (int i = 0; i < KPT; ++i) {
-            const int item = tid + i * NT;
-            const int kk = item / NB, b = item % NB;
-            const int key = kb + kk;
-            k[i].w[0] = k[i].w[1] = k[i].w[2] = 0u;
-            k[i].s = 0;
-            if (item < KI && key < k1) {
-                const size_t blk = (head_base + key) * NB + b;
-                const uint32_t *src = a.kc + blk * 3;
-                k[i].w[0] = src[0];
-                k[i].w[1] = src[1];
-                k[i].w[2] = src[2];
-                k[i].s = a.ks[blk];
-            }
+            const int item = tid + i * NT;      // (key item / NB, block item % NB)
+            const u32x3 w = __builtin_amdgcn_raw_buffer_load_b96(rk, item * 12, 0, 0);
+            k[i].w[0] = w[0];
+            k[i].w[1] = w[1];
+            k[i].w[2] = w[2];
+            k[i].s = __builtin_amdgcn_raw_buffer_load_b16(rks, item * 2, 0, 0);
         }
-        const size_t grp_base = (size_t)head * a.ngroups + (size_t)(kb / kKeyTile);
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
             const int d = tid + i * NT;
-            VItem &it = v[i];
-            it.w[0] = it.w[1] = it.w[2] = 0u;
-            it.s = 0;
-            if (d < VI) {
-                const uint32_t *src = a.vc + (grp_base * D + d) * 3;
-                it.w[0] = src[0];
-                it.w[1] = src[1];
-                it.w[2] = src[2];
-                // keys past the range get scale 0, so their V^ is exactly 0
-                if (kb + (d & 31) < k1) it.s = a.vs[grp_base * D + d];
-            }
+            const u32x3 w = __builtin_amdgcn_raw_buffer_load_b96(rv, d * 12, 0, 0);
+            v[i].w[0] = w[0];
+            v[i].w[1] = w[1];
+            v[i].w[2] = w[2];
+            v[i].s = __builtin_amdgcn_raw_buffer_load_b16(rvs, d * 2, 0, 0);
         }
     }
 
-    __device__ __forceinline__ void store(TileLds<D> &t, int tid) const {
+    // nk: keys of the tile below k1 (V scales of later keys become 0)
+    __device__ __forceinline__ void store(TileLds<D> &t, int tid, int nk) const {
         using L = TileLds<D>;
 #pragma unroll
         for (int i = 0; i < KPT; ++i) {
@@ -366,14 +392,15 @@ struct TileIo {
                                   codes_to_i8(o[7])};
                 *reinterpret_cast<u32x4 *>(t.kq + kk * L::KQS + 32 * b) = lo;
                 *reinterpret_cast<u32x4 *>(t.kq + kk * L::KQS + 32 * b + 16) = hi;
-                t.skf[b * kKeyTile + kk] = half_bits_to_float(k[i].s);
+                t.skh[b * kKeyTile + kk] = __builtin_bit_cast(_Float16, k[i].s);
             }
         }
-        // V scales: every wave stages the entries its own rows need.
+        // V scales: every wave stages the entries its own rows need; keys
+        // past the range get scale 0, so their V^ is exactly 0.
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
             const int d = tid + i * NT;
-            if (d < VI) t.svs[d] = v[i].s;
+            if (d < VI) t.svs[d] = (d & 31) < nk ? v[i].s : (uint16_t)0;
         }
         wave_lds_sync();
 #pragma unroll
@@ -431,46 +458,50 @@ struct TileIo4 {
     static constexpr int VPT = (VI + NT - 1) / NT;
     KItem4 k[KPT];
     VItem4 v[VPT];
-    uint16_t vs;        // V scale of key (lane % 32) of the tile, lanes 0..31 of each wave
+    uint16_t vs;        // V scale of key (lane % 32) of the tile (lanes 0..31 of each wave use it)
 
-    __device__ __forceinline__ void load(const AttnArgs &a, int head, int kb, int k1, int tid) {
+    // Buffer-descriptor loads as in TileIo: zeros past k1, the same loads
+    // on every lane.
+    __device__ __forceinline__ void load(const AttnArgs &a, int head, int kb, int k0, int k1,
+                                         int tid) {
+        const bool valid = kb < k1;
+        const int kt = valid ? kb : k0;
+        const int nk = valid ? min(kKeyTile, k1 - kb) : 0;
         const size_t head_base = (size_t)head * a.cap;
+        const size_t grp = (size_t)head * a.ngroups + (size_t)(kt / kKeyTile);
+        const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint32_t *>(a.kc + (head_base + kt) * (D / 8)), (short)0, nk * (D / 2), kBufWord3);
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t *>(a.ks + head_base + kt), (short)0, nk * 2, kBufWord3);
+        const __amdgpu_buffer_rsrc_t rvs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t *>(a.vs + head_base + kt), (short)0, nk * 2, kBufWord3);
+        const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint32_t *>(a.vc + grp * D * 4), (short)0, valid ? D * 16 : 0, kBufWord3);
 #pragma unroll
         for (int i = 0; i < KPT; ++i) {
             const int item = tid + i * NT;
             const int kk = item / NB, b = item % NB;
-            const int key = kb + kk;
-            k[i].w[0] = k[i].w[1] = k[i].w[2] = k[i].w[3] = 0u;
-            k[i].s = 0;
-            if (item < KI && key < k1) {
-                const u32x4 w = *reinterpret_cast<const u32x4 *>(
-                    a.kc + (head_base + key) * (D / 8) + 4 * b);
-                k[i].w[0] = w[0];
-                k[i].w[1] = w[1];
-                k[i].w[2] = w[2];
-                k[i].w[3] = w[3];
-                if (b == 0) k[i].s = a.ks[head_base + key];
-            }
+            const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(rk, (kk * (D / 8) + 4 * b) * 4, 0, 0);
+            k[i].w[0] = w[0];
+            k[i].w[1] = w[1];
+            k[i].w[2] = w[2];
+            k[i].w[3] = w[3];
+            k[i].s = __builtin_amdgcn_raw_buffer_load_b16(rs, kk * 2, 0, 0);
         }
-        const size_t grp_base = (size_t)head * a.ngroups + (size_t)(kb / kKeyTile);
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
             const int d = tid + i * NT;
-            v[i].w[0] = v[i].w[1] = v[i].w[2] = v[i].w[3] = 0u;
-            if (d < VI) {
-                const u32x4 w = *reinterpret_cast<const u32x4 *>(a.vc + (grp_base * D + d) * 4);
-                v[i].w[0] = w[0];
-                v[i].w[1] = w[1];
-                v[i].w[2] = w[2];
-                v[i].w[3] = w[3];
-            }
+            const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(rv, d * 16, 0, 0);
+            v[i].w[0] = w[0];
+            v[i].w[1] = w[1];
+            v[i].w[2] = w[2];
+            v[i].w[3] = w[3];
         }
-        const int lane = tid & 63;
-        // keys past the range get scale 0, so their V^ is exactly 0
-        vs = (lane < kKeyTile && kb + lane < k1) ? a.vs[head_base + kb + lane] : (uint16_t)0;
+        // key (lane % 32)'s V scale; zero past the range
+        vs = __builtin_amdgcn_raw_buffer_load_b16(rvs, (tid & 31) * 2, 0, 0);
     }
 
-    __device__ __forceinline__ void store(TileLds<D> &t, int tid) const {
+    __device__ __forceinline__ void store(TileLds<D> &t, int tid, int) const {
         using L = TileLds<D>;
 #pragma unroll
         for (int i = 0; i < KPT; ++i) {
@@ -662,13 +693,22 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(const AttnArgs a) {
     float m_run = -INFINITY;
     float l_run = 0.0f;
 
-    TileIoOf<D, NT, FMT> io;
-    if (k0 < k1) io.load(a, head, k0, k1, tid);
+    // Tile data is prefetched into registers AHEAD tiles ahead: with two
+    // register sets, tile i is stored to LDS from one while the other's loads
+    // (tile i + 1) are outstanding, and the freed set is refilled with tile
+    // i + 2 right after the store.  The 4-bit format, with fewer VALU
+    // operations per tile, gains from the deeper prefetch; the 3-bit format
+    // keeps one set (measured no faster with two, and its causal variant
+    // needs the registers).
+    constexpr int AHEAD = FMT == 1 ? 2 : 1;
+    TileIoOf<D, NT, FMT> io0, io1;
+    io0.load(a, head, k0, k0, k1, tid);
+    if constexpr (AHEAD == 2) io1.load(a, head, k0 + KT, k0, k1, tid);
 
-    for (int kb = k0; kb < k1; kb += KT) {
-        io.store(lds, tid);
+    auto tile = [&](TileIoOf<D, NT, FMT> &io, int kb) {
+        io.store(lds, tid, min(KT, k1 - kb));
         __syncthreads();
-        if (kb + KT < k1) io.load(a, head, kb + KT, k1, tid);
+        io.load(a, head, kb + AHEAD * KT, k0, k1, tid);
 
         if (wave_active) {
             f32x16 acc = f32x16{};
@@ -686,14 +726,15 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(const AttnArgs a) {
                         s_next = __builtin_amdgcn_mfma_i32_32x32x32_i8(
                             *reinterpret_cast<const i32x4 *>(kq_lane + 32 * (b + 1)),
                             *reinterpret_cast<const i32x4 *>(q_lane + 32 * (b + 1)), i32x16{}, 0, 0, 0);
-                    const f32x4 s0 = *reinterpret_cast<const f32x4 *>(lds.skf + b * KT + 8 * hl);
-                    const f32x4 s1 = *reinterpret_cast<const f32x4 *>(lds.skf + b * KT + 8 * hl + 4);
-                    const f32x4 s2 = *reinterpret_cast<const f32x4 *>(lds.skf + b * KT + 16 + 8 * hl);
-                    const f32x4 s3 = *reinterpret_cast<const f32x4 *>(lds.skf + b * KT + 16 + 8 * hl + 4);
-                    const float skr[16] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w,
-                                           s2.x, s2.y, s2.z, s2.w, s3.x, s3.y, s3.z, s3.w};
+                    // fp16 scales of keys 8hl + [0, 8) and 16 + 8hl + [0, 8); the FMA
+                    // widens them in the instruction (v_fma_mix_f32)
+                    const f16x8 h0 = *reinterpret_cast<const f16x8 *>(lds.skh + b * KT + 8 * hl);
+                    const f16x8 h1 = *reinterpret_cast<const f16x8 *>(lds.skh + b * KT + 16 + 8 * hl);
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) acc[r] = fmaf(skr[r], (float)s_cur[r], acc[r]);
+                    for (int r = 0; r < 8; ++r) {
+                        acc[r] = fmaf((float)h0[r], (float)s_cur[r], acc[r]);
+                        acc[8 + r] = fmaf((float)h1[r], (float)s_cur[8 + r], acc[8 + r]);
+                    }
                     if (DEBUG && a.dbg_logits && row_ok) {
 #pragma unroll
                         for (int r = 0; r < 16; ++r) {
@@ -799,6 +840,15 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(const AttnArgs a) {
             __builtin_amdgcn_s_setprio(0);
         }
         __syncthreads();
+    };
+    if constexpr (AHEAD == 2) {
+        for (int kb = k0; kb < k1; kb += 2 * KT) {
+            tile(io0, kb);
+            if (kb + KT >= k1) break;
+            tile(io1, kb + KT);
+        }
+    } else {
+        for (int kb = k0; kb < k1; kb += KT) tile(io0, kb);
     }
 
     // ---- epilogue
