@@ -74,6 +74,8 @@ def _load():
             fn.restype = None
         lib.orc_attention_i4.argtypes = lib.orc_attention.argtypes
         lib.orc_attention_i4.restype = i32
+        lib.orc_kv4_commit.argtypes = lib.orc_kv_commit.argtypes
+        lib.orc_kv4_commit.restype = i32
         _lib = lib
     return _lib
 
@@ -288,7 +290,8 @@ def kv_commit(kv, ctx_len: int, T: int, path, n: int) -> None:
         a = getattr(kv, name)
         assert a.flags["C_CONTIGUOUS"], name
     p = _c(np.asarray(path, dtype=np.int32), np.int32)
-    rc = _load().orc_kv_commit(_ptr(kv.k_codes), _ptr(kv.k_scales), _ptr(kv.v_codes),
+    fn = _load().orc_kv_commit if getattr(kv, "fmt", "b3") == "b3" else _load().orc_kv4_commit
+    rc = fn(_ptr(kv.k_codes), _ptr(kv.k_scales), _ptr(kv.v_codes),
                                _ptr(kv.v_scales), kv.n_kv_heads, kv.head_dim, kv.capacity,
                                ctx_len, T, _ptr(p), n)
     if rc != 0:

@@ -731,3 +731,47 @@ ORC_EXPORT int orc_attention_i4(const float *q, int T, int Hq,
     }
     return bad ? -1 : 0;
 }
+
+/* Accepted-path commit for the 4-bit per-token-head cache (as
+ * orc_kv_commit; layouts as in (i3)). */
+ORC_EXPORT int orc_kv4_commit(uint32_t *kc, uint16_t *ks, uint32_t *vc, uint16_t *vs, int Hkv,
+                              int D, int cap, int L, int T, const int32_t *path, int n)
+{
+    size_t ng = n_groups(cap);
+    int kw = D / 8;
+    if (n < 1 || n > T || L < 0 || L + T > cap)
+        return -1;
+    for (int j = 0; j < n; ++j)
+        if (path[j] < 0 || path[j] >= T)
+            return -1;
+    uint32_t *kbuf = malloc((size_t)n * kw * sizeof(uint32_t) + 1);
+    uint16_t *ksb = malloc((size_t)n * sizeof(uint16_t) + 1);
+    uint16_t *vsb = malloc((size_t)n * sizeof(uint16_t) + 1);
+    int *vcode = malloc((size_t)n * D * sizeof(int) + 1);
+    if (!kbuf || !ksb || !vsb || !vcode) {
+        free(kbuf); free(ksb); free(vsb); free(vcode);
+        return -1;
+    }
+    for (int g = 0; g < Hkv; ++g) {
+        for (int j = 0; j < n; ++j) {
+            int src = L + path[j];
+            memcpy(kbuf + (size_t)j * kw, kc + ((size_t)g * cap + src) * kw, (size_t)kw * 4);
+            ksb[j] = ks[(size_t)g * cap + src];
+            vsb[j] = vs[(size_t)g * cap + src];
+            for (int d = 0; d < D; ++d)
+                vcode[(size_t)j * D + d] =
+                    nib_get(vc + (((size_t)g * ng + (size_t)(src / 32)) * D + d) * 4, src % 32);
+        }
+        for (int j = 0; j < n; ++j) {
+            int dst = L + j;
+            memcpy(kc + ((size_t)g * cap + dst) * kw, kbuf + (size_t)j * kw, (size_t)kw * 4);
+            ks[(size_t)g * cap + dst] = ksb[j];
+            vs[(size_t)g * cap + dst] = vsb[j];
+            for (int d = 0; d < D; ++d)
+                nib_set(vc + (((size_t)g * ng + (size_t)(dst / 32)) * D + d) * 4, dst % 32,
+                        vcode[(size_t)j * D + d]);
+        }
+    }
+    free(kbuf); free(ksb); free(vsb); free(vcode);
+    return 0;
+}

@@ -382,7 +382,8 @@ int stv_kv_commit(const stv_kv_layer *kv, int32_t ctx_len, int32_t T, const int3
     if (D != 64 && D != 128 && D != 256) return fail(STV_EINVAL, "head_dim must be 64, 128 or 256");
     if (kv->n_kv_heads < 1) return fail(STV_EINVAL, "n_kv_heads must be >= 1");
     if (kv->capacity <= 0) return fail(STV_EINVAL, "capacity must be positive");
-    if (kv->kv_format != STV_KV_3BIT) return fail(STV_EINVAL, "kv_commit moves the 3-bit format only");
+    if (kv->kv_format != STV_KV_3BIT && kv->kv_format != STV_KV_4BIT_TOKEN)
+        return fail(STV_EINVAL, "kv_format %d unknown", kv->kv_format);
     if (ctx_len < 0) return fail(STV_EINVAL, "ctx_len must be >= 0");
     if ((long long)ctx_len + T > kv->capacity)
         return fail(STV_ECAPACITY, "ctx_len + T = %lld exceeds capacity %d", (long long)ctx_len + T,
@@ -398,6 +399,7 @@ int stv_kv_commit(const stv_kv_layer *kv, int32_t ctx_len, int32_t T, const int3
     a.D = D;
     a.cap = kv->capacity;
     a.ngroups = (kv->capacity + 31) / 32;
+    a.fmt = kv->kv_format;
     a.L = ctx_len;
     a.T = T;
     a.path = path;

@@ -23,6 +23,7 @@ struct CommitArgs {
     uint32_t *vc;
     uint16_t *vs;
     int Hkv, D, cap, ngroups;
+    int fmt;                    // 0 = 3-bit blocks, 1 = 4-bit per-token-head
     int L, T;
     const int32_t *path;        // [T] device
     const int32_t *n_accepted;  // [1] device

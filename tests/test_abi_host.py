@@ -113,9 +113,9 @@ def test_format_errors(lib, stvmod):
     f = lib.stv_kv_quant_pack
     assert f(FAKE, 10, 0, 4, FAKE, FAKE, 4, 256, 100, None) == E.STV_EINVAL
     assert f(FAKE + 4, 10, 0, 2, FAKE, FAKE, 4, 256, 100, None) == E.STV_EINVAL   # x alignment
-    i4 = stvmod._KVLayer(FAKE, FAKE, FAKE, FAKE, 4, 256, 1000, 1)
-    assert lib.stv_kv_commit(ctypes.byref(i4), 0, 8, FAKE, FAKE, None) == E.STV_EINVAL
-    assert "3-bit" in _err(lib)
+    unknown = stvmod._KVLayer(FAKE, FAKE, FAKE, FAKE, 4, 256, 1000, 3)
+    assert lib.stv_kv_commit(ctypes.byref(unknown), 0, 8, FAKE, FAKE, None) == E.STV_EINVAL
+    assert "kv_format" in _err(lib)
 
 
 def test_verify_mask_errors(lib, stvmod):

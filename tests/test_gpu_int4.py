@@ -124,3 +124,26 @@ def test_pack4_matches_oracle(gpu, orc, d, pos0, n_tok):
     assert np.array_equal(kv.k_scales.cpu().numpy().view(np.uint16), host.k_scales)
     assert np.array_equal(kv.v_codes.cpu().numpy().view(np.uint32), host.v_codes)
     assert np.array_equal(kv.v_scales.cpu().numpy().view(np.uint16), host.v_scales)
+
+
+@pytest.mark.parametrize("hkv,d,L,T,seed", [(2, 64, 29, 8, 1), (4, 256, 1000, 64, 2),
+                                            (3, 128, 31, 33, 3)])
+def test_commit4_matches_oracle(gpu, orc, hkv, d, L, T, seed):
+    stv, torch = gpu
+    rng = np.random.default_rng(seed + 90)
+    cap = L + T + 7
+    host = synth.make_kv4(rng, hkv, d, L + T, cap)
+    parents = synth.make_tree_parents(rng, T, 8)
+    draft, target = synth.make_tree_tokens(rng, parents, vocab=2, p_follow=0.9)
+    mask = synth.ancestor_masks(parents)
+    kv = stv.KVCache.from_host(host)
+    path, n, _ = stv.tree_accept(mask, torch.from_numpy(draft).cuda(),
+                                 torch.from_numpy(target).cuda())
+    stv.kv_commit(kv, L, path, n)
+    torch.cuda.synchronize()
+    wn, wpath, _ = orc.tree_accept(mask, draft, target)
+    orc.kv_commit(host, L, T, wpath, wn)
+    assert np.array_equal(kv.k_codes.cpu().numpy().view(np.uint32), host.k_codes)
+    assert np.array_equal(kv.k_scales.cpu().numpy().view(np.uint16), host.k_scales)
+    assert np.array_equal(kv.v_codes.cpu().numpy().view(np.uint32), host.v_codes)
+    assert np.array_equal(kv.v_scales.cpu().numpy().view(np.uint16), host.v_scales)

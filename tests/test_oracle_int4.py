@@ -149,3 +149,24 @@ def test_tree_rows_equal_their_chains_and_chain_is_causal(orc):
             causal = orc.attention(qc, ch, L, None, 0.125)
             for h in range(hq):
                 assert np.array_equal(tree["out"][i * hq + h], causal["out"][(n - 1) * hq + h])
+
+
+@pytest.mark.parametrize("L,T,seed", [(0, 8, 1), (29, 8, 2), (61, 17, 3), (100, 64, 4)])
+def test_commit4_moves_exactly_the_committed_tokens(orc, L, T, seed):
+    rng = np.random.default_rng(seed + 80)
+    hkv, d = 2, 64
+    cap = L + T + 5
+    kv = synth.make_kv4(rng, hkv, d, L + T, cap)
+    old = synth.KVCache(kv.k_codes.copy(), kv.k_scales.copy(), kv.v_codes.copy(),
+                        kv.v_scales.copy(), hkv, d, cap, kv.n_filled, "i4")
+    parents = synth.make_tree_parents(rng, T, 8)
+    draft, target = synth.make_tree_tokens(rng, parents, vocab=2, p_follow=0.9)
+    n, path, _ = orc.tree_accept(synth.ancestor_masks(parents), draft, target)
+    orc.kv_commit(kv, L, T, path, n)
+    for g in range(hkv):
+        for pos in range(cap):
+            src = L + int(path[pos - L]) if L <= pos < L + n else pos
+            assert [_k_val(kv, g, pos, e) for e in range(d)] == [_k_val(old, g, src, e) for e in range(d)]
+            assert [_v_val(kv, g, pos, e) for e in range(d)] == [_v_val(old, g, src, e) for e in range(d)]
+            assert kv.k_scales[g, pos] == old.k_scales[g, src]
+            assert kv.v_scales[g, pos] == old.v_scales[g, src]
