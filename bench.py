@@ -37,7 +37,7 @@ INT8_PEAK_TOPS = 5000.0          # dense int8 MFMA
 FP16_PEAK_TFLOPS = 2500.0        # dense fp16 MFMA
 N_BUFFERS = 4                    # 4 x 235 MB > 256 MB Infinity Cache
 KERNEL_SOURCES = [os.path.join(ROOT, "speculative_tree_verify_amd", "csrc", f)
-                  for f in ("stv_kernels.hip", "stv_internal.h")]
+                  for f in ("stv_kernels.hip", "stv_internal.h", "stv_codes.h")]
 
 
 def kernel_source_hash() -> str:
@@ -98,11 +98,14 @@ def work_of(geom: synth.Geometry, masks, fmt: str = "b3"):
 
 
 class Workload:
-    def __init__(self, geom: synth.Geometry, torch, stv, n_buffers=N_BUFFERS, fmt="b3"):
+    def __init__(self, geom: synth.Geometry, torch, stv, n_buffers=N_BUFFERS, fmt="b3",
+                 pv16=False):
         self.g = geom
         self.torch = torch
         self.stv = stv
         self.fmt = fmt
+        # pv16: the fp16-accumulated P.V variant, one call (its merge included)
+        self.pv16 = pv16
         rng = np.random.default_rng(geom.seed)
         make = synth.make_kv if fmt == "b3" else synth.make_kv4
         host = make(rng, geom.n_kv_heads, geom.head_dim, geom.n_keys)
@@ -137,32 +140,73 @@ class Workload:
         self.out = torch.empty((T, hq, d), dtype=torch.float32, device=dev)
         self.out_lse = torch.empty((T, hq), dtype=torch.float32, device=dev)
         self.work = work_of(geom, self.mask, fmt)
+        self._prepare_calls()
+
+    def _prepare_calls(self):
+        """Marshals every C-ABI call of a step once per cache, so that a step
+        costs the host a few microseconds and the launches queue up ahead of
+        the GPU (the events then time the kernels, not host gaps).  The calls
+        are the ones the package's Python functions make."""
+        import ctypes
+        stv, g, torch = self.stv, self.g, self.torch
+        lib = stv.load_library()
+        stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        T, hq, d = g.n_rows, g.n_q_heads, g.head_dim
+        codes = {"b3": (stv.STV_K, stv.STV_V), "i4": (stv.STV_K4, stv.STV_V4)}[self.fmt]
+        self._mask_arr = (None if self.mask is None
+                          else np.ascontiguousarray(np.asarray(self.mask, dtype=np.uint64)))
+        mask_ptr = None if self._mask_arr is None else self._mask_arr.ctypes.data
+        self._layers = [kv._layer() for kv in self.caches]
+        self._calls = []
+        for kv, layer in zip(self.caches, self._layers):
+            pack = [(lib.stv_kv_quant_pack, (x.data_ptr(), T, g.ctx_len, code, c.data_ptr(),
+                                            sc.data_ptr(), g.n_kv_heads, d, kv.capacity, stream))
+                    for x, code, c, sc in ((self.knew, codes[0], kv.k_codes, kv.k_scales),
+                                           (self.vnew, codes[1], kv.v_codes, kv.v_scales))]
+            lref = ctypes.byref(layer)
+            if self.pv16:
+                if not hasattr(self, "_ws"):
+                    self._ws = torch.empty(max(self.ws_bytes, 1), dtype=torch.uint8,
+                                           device="cuda")
+                attn = (lib.stv_verify_attention_fp16acc,
+                        (self.q.data_ptr(), T, hq, lref, g.ctx_len, mask_ptr, self.scale,
+                         self.out.data_ptr(), self.out_lse.data_ptr(), self._ws.data_ptr(),
+                         self.ws_bytes, 0, stream))
+                merge = None
+            elif self.S == 1:
+                # one split: the attention kernel writes the output itself
+                if self.causal:
+                    attn = (lib.stv_prefill_attention,
+                            (self.q.data_ptr(), T, hq, lref, g.ctx_len, self.scale,
+                             self.out.data_ptr(), self.out_lse.data_ptr(), None, 0, 0, None,
+                             None, None, stream))
+                else:
+                    attn = (lib.stv_verify_attention,
+                            (self.q.data_ptr(), T, hq, lref, g.ctx_len, mask_ptr, self.scale,
+                             self.out.data_ptr(), self.out_lse.data_ptr(), None, 0, 0, None,
+                             None, None, stream))
+                merge = None
+            else:
+                attn = (lib.stv_attention_partials,
+                        (self.q.data_ptr(), T, hq, lref, g.ctx_len, mask_ptr, self.scale, 0,
+                         self.part_o.data_ptr(), self.part_lse.data_ptr(), stream))
+                merge = (lib.stv_split_merge,
+                         (self.part_o.data_ptr(), self.part_lse.data_ptr(), self.S, T * hq, d,
+                          self.out.data_ptr(), self.out_lse.data_ptr(), stream))
+            self._calls.append((pack, attn, merge))
 
     def step(self, i, ev=None):
-        stv, g = self.stv, self.g
-        kv = self.caches[i % len(self.caches)]
-        stv.kv_quant_pack(self.knew, g.ctx_len, kv, "k")
-        stv.kv_quant_pack(self.vnew, g.ctx_len, kv, "v")
+        check = self.stv._check
+        pack, attn, merge = self._calls[i % len(self._calls)]
+        for fn, args in pack:
+            check(fn(*args))
         if ev is not None:
             ev[0].record()
-        if self.S == 1:
-            # one split: the attention kernel writes the output itself
-            if self.causal:
-                stv.prefill_attention(self.q, kv, g.ctx_len, self.scale, self.out, self.out_lse)
-            else:
-                stv.verify_attention(self.q, kv, g.ctx_len, self.mask, self.scale, self.out,
-                                     self.out_lse)
-            if ev is not None:
-                ev[1].record()
-                ev[2].record()
-            return
-        stv.attention_partials(self.q, kv, g.ctx_len, self.mask, self.scale, 0,
-                               self.part_o, self.part_lse)
+        check(attn[0](*attn[1]))
         if ev is not None:
             ev[1].record()
-        stv.split_merge(self.part_o.reshape(self.S, -1, g.head_dim),
-                        self.part_lse.reshape(self.S, -1), self.out.reshape(-1, g.head_dim),
-                        self.out_lse.reshape(-1))
+        if merge is not None:
+            check(merge[0](*merge[1]))
         if ev is not None:
             ev[2].record()
 
@@ -199,11 +243,20 @@ def accept_commit_bench(wl: Workload, steps: int):
         stv.tree_accept(wl.mask, d, t, path, n, bonus)
         stv.kv_commit(wl.caches[i % len(wl.caches)], g.ctx_len, path, n)
     torch.cuda.synchronize()
+    # the same C-ABI calls, marshalled once (see Workload._prepare_calls)
+    import ctypes
+    lib = stv.load_library()
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    T = g.n_rows
+    accept = (wl._mask_arr.ctypes.data, T, d.data_ptr(), t.data_ptr(), path.data_ptr(),
+              n.data_ptr(), bonus.data_ptr(), stream)
+    commits = [(ctypes.byref(layer), g.ctx_len, T, path.data_ptr(), n.data_ptr(), stream)
+               for layer in wl._layers]
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     ev[0].record()
     for i in range(steps):
-        stv.tree_accept(wl.mask, d, t, path, n, bonus)
-        stv.kv_commit(wl.caches[i % len(wl.caches)], g.ctx_len, path, n)
+        stv._check(lib.stv_tree_accept(*accept))
+        stv._check(lib.stv_kv_commit(*commits[i % len(commits)]))
     ev[1].record()
     torch.cuda.synchronize()
     n_acc = int(n.item())
@@ -232,10 +285,17 @@ def lookup_bench(torch, stv, batch: int, n_tokens: int, steps: int, n_buffers: i
     for i in range(3):
         stv.lookup_draft(bufs[i % n_buffers], ln, 6, 12, 8, workspace=ws, out=out)
     torch.cuda.synchronize()
+    # the same C-ABI call, marshalled once (see Workload._prepare_calls)
+    import ctypes
+    lib = stv.load_library()
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    calls = [(b.data_ptr(), ln.data_ptr(), batch, n_tokens, 6, 12, 8, out["tokens"].data_ptr(),
+              out["count"].data_ptr(), out["match"].data_ptr(), out["pos"].data_ptr(),
+              ws.data_ptr(), ws.numel(), stream) for b in bufs]
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     ev[0].record()
     for i in range(steps):
-        stv.lookup_draft(bufs[i % n_buffers], ln, 6, 12, 8, workspace=ws, out=out)
+        stv._check(lib.stv_lookup_draft(*calls[i % n_buffers]))
     ev[1].record()
     torch.cuda.synchronize()
     us = ev[0].elapsed_time(ev[1]) * 1e3 / steps
@@ -287,6 +347,15 @@ def cpu_baseline(wl: Workload, n_rows: int):
                       f"scaled to the whole call: {full_s * 1e6:.0f} us"}
 
 
+def parse_workload(name: str):
+    """'tree8_262k_i4' -> ('tree8_262k', 'i4', False); '_pv16' -> fp16-accumulated P.V."""
+    if name.endswith("_i4"):
+        return name[:-3], "i4", False
+    if name.endswith("_pv16"):
+        return name[:-5], "b3", True
+    return name, "b3", False
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -294,8 +363,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="tree64_262k")
     ap.add_argument("--extra", default="prefill_4k_32k,tree8_262k,decode_262k,decode_8k,tree64_32k,"
-                                       "tree64_262k_i4,prefill_4k_32k_i4,tree8_262k_i4,decode_262k_i4",
-                    help="comma-separated extra workloads ('' for none)")
+                                       "tree64_262k_i4,prefill_4k_32k_i4,tree8_262k_i4,decode_262k_i4,"
+                                       "tree8_262k_pv16,decode_262k_pv16",
+                    help="comma-separated extra workloads ('' for none); suffix _i4: the 4-bit "
+                         "per-token-head cache; _pv16: fp16-accumulated P.V (whole call)")
     ap.add_argument("--extra-steps", type=int, default=10)
     ap.add_argument("--no-lookup", dest="lookup", action="store_false",
                     help="skip the lookup-drafting lines under extra")
@@ -315,9 +386,8 @@ def main():
     import speculative_tree_verify_amd as stv
     stv.load_library()
     geoms = {g.name: g for g in synth.CONFIGS + synth.EXTRA_CONFIGS}
-    wbase, wfmt = ((args.workload[:-3], "i4") if args.workload.endswith("_i4")
-                   else (args.workload, "b3"))
-    wl = Workload(geoms[wbase], torch, stv, fmt=wfmt)
+    wbase, wfmt, wpv16 = parse_workload(args.workload)
+    wl = Workload(geoms[wbase], torch, stv, fmt=wfmt, pv16=wpv16)
     r = wl.run(args.steps, args.warmup)
     s = summarize(wl, r, args.steps)
     g = wl.g
@@ -326,7 +396,8 @@ def main():
     blended_peak = total_ops / (w["qk_ops"] / INT8_PEAK_TOPS + w["pv_ops"] / FP16_PEAK_TFLOPS)
     achieved = total_ops / (s["attn_kernel_us"] * 1e-6) / 1e12
     rows_per_kv_head = g.n_rows * (g.n_q_heads // g.n_kv_heads)
-    kernel_name = "attn_dec_kernel" if rows_per_kv_head <= 16 else "attn_split_kernel"
+    kernel_name = ("attn_dec_kernel" if rows_per_kv_head <= 16 and wl.fmt == "b3"
+                   else "attn_split_kernel")
     line = {
         "metric": METRIC,
         "value": round(w["step_bytes"] / (s["ms_per_step"] * 1e-3) / 1e9, 2),
@@ -365,8 +436,8 @@ def main():
     for name in [n for n in args.extra.split(",") if n]:
         del wl
         torch.cuda.empty_cache()
-        base, fmt = (name[:-3], "i4") if name.endswith("_i4") else (name, "b3")
-        wl = Workload(geoms[base], torch, stv, fmt=fmt)
+        base, fmt, pv16 = parse_workload(name)
+        wl = Workload(geoms[base], torch, stv, fmt=fmt, pv16=pv16)
         rr = wl.run(args.extra_steps, 2)
         se = summarize(wl, rr, args.extra_steps)
         extra[name] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in se.items()}
@@ -393,7 +464,7 @@ def main():
     if args.cpu_rows > 0:
         del wl
         torch.cuda.empty_cache()
-        wl = Workload(geoms[wbase], torch, stv, n_buffers=1, fmt=wfmt)
+        wl = Workload(geoms[wbase], torch, stv, n_buffers=1, fmt=wfmt, pv16=wpv16)
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_rows)
     print(json.dumps(line), flush=True)
 

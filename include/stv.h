@@ -106,7 +106,7 @@ typedef struct stv_kv_layer {
 /* Description of the last failure on the calling thread ("" after success). */
 const char *stv_last_error(void);
 
-/* ABI version; bumped on any incompatible change.  Currently 2. */
+/* ABI version; bumped on any change of the interface.  Currently 3. */
 int32_t stv_abi_version(void);
 
 /*
@@ -188,6 +188,23 @@ int stv_verify_attention(const float *q, int32_t T, int32_t n_q_heads,
                          float softmax_scale, float *out, float *out_lse, void *workspace,
                          size_t workspace_bytes, int32_t n_splits, int32_t *dbg_logits,
                          int8_t *dbg_q, float *dbg_qscale, void *stream);
+
+/*
+ * stv_verify_attention_fp16acc -- stv_verify_attention with P.V accumulated
+ * in fp16 (elpis, "What fast means": the fp16-accumulated P.V decode kernel,
+ * left unresolved there and not shipped).  Each 32-key tile's P.V product
+ * is computed in fp32, rounded to fp16 and added into fp16 accumulators; the
+ * running max follows every increase, so P <= 1.  An accumulator overflows
+ * to inf when a split's sum of P * |V| passes 65504 (all keys of a split
+ * about equally likely and |V| large); the result is then undefined.
+ * Arguments, workspace (same plan) and errors as for stv_verify_attention,
+ * without the debug outputs; the 3-bit format only (STV_EINVAL otherwise).
+ */
+int stv_verify_attention_fp16acc(const float *q, int32_t T, int32_t n_q_heads,
+                                 const stv_kv_layer *kv, int32_t ctx_len,
+                                 const uint64_t *anc_mask, float softmax_scale, float *out,
+                                 float *out_lse, void *workspace, size_t workspace_bytes,
+                                 int32_t n_splits, void *stream);
 
 /*
  * stv_prefill_attention -- the chunked-prefill variant (elpis, "Why fast":

@@ -76,6 +76,10 @@ def load_library():
         lib.stv_verify_attention.argtypes = [P, i32, i32, ctypes.POINTER(_KVLayer), i32, P,
                                              ctypes.c_float, P, P, P, ctypes.c_size_t, i32,
                                              P, P, P, P]
+        lib.stv_verify_attention_fp16acc.restype = ctypes.c_int
+        lib.stv_verify_attention_fp16acc.argtypes = [P, i32, i32, ctypes.POINTER(_KVLayer), i32,
+                                                     P, ctypes.c_float, P, P, P, ctypes.c_size_t,
+                                                     i32, P]
         lib.stv_prefill_attention.restype = ctypes.c_int
         lib.stv_prefill_attention.argtypes = [P, i32, i32, ctypes.POINTER(_KVLayer), i32,
                                               ctypes.c_float, P, P, P, ctypes.c_size_t, i32,
@@ -238,7 +242,7 @@ def attention_plan(T: int, n_q_heads: int, n_kv_heads: int, head_dim: int, ctx_l
 
 
 def _attention(q, kv: KVCache, ctx_len: int, mask, softmax_scale, out, out_lse, workspace,
-               n_splits, debug, causal):
+               n_splits, debug, causal, fp16acc=False):
     torch = _torch()
     T, hq, d = q.shape
     if softmax_scale is None:
@@ -276,10 +280,16 @@ def _attention(q, kv: KVCache, ctx_len: int, mask, softmax_scale, out, out_lse, 
         m = np.ascontiguousarray(np.asarray(mask, dtype=np.uint64))
         if m.shape != (T,):
             raise ValueError(f"anc_mask must have shape ({T},)")
-        rc = lib.stv_verify_attention(
-            _dev_ptr(q, torch.float32, "q"), T, hq, ctypes.byref(layer), ctx_len,
-            m.ctypes.data, float(softmax_scale), *common, ws_ptr, ws_len, n_splits,
-            *dbg_ptrs, _stream(q.device))
+        if fp16acc:
+            rc = lib.stv_verify_attention_fp16acc(
+                _dev_ptr(q, torch.float32, "q"), T, hq, ctypes.byref(layer), ctx_len,
+                m.ctypes.data, float(softmax_scale), *common, ws_ptr, ws_len, n_splits,
+                _stream(q.device))
+        else:
+            rc = lib.stv_verify_attention(
+                _dev_ptr(q, torch.float32, "q"), T, hq, ctypes.byref(layer), ctx_len,
+                m.ctypes.data, float(softmax_scale), *common, ws_ptr, ws_len, n_splits,
+                *dbg_ptrs, _stream(q.device))
     _check(rc)
     # keep host/device buffers alive until the enqueued work has consumed them
     # (the mask is copied into kernel arguments at launch; the workspace is
@@ -296,6 +306,13 @@ def verify_attention(q, kv: KVCache, ctx_len: int, anc_mask, softmax_scale=None,
     a tuple of those names asks for a subset."""
     return _attention(q, kv, ctx_len, anc_mask, softmax_scale, out, out_lse, workspace,
                       n_splits, debug, causal=False)
+
+
+def verify_attention_fp16acc(q, kv: KVCache, ctx_len: int, anc_mask, softmax_scale=None,
+                             out=None, out_lse=None, workspace=None, n_splits: int = 0):
+    """verify_attention with P.V accumulated in fp16 (3-bit caches only)."""
+    return _attention(q, kv, ctx_len, anc_mask, softmax_scale, out, out_lse, workspace,
+                      n_splits, False, causal=False, fp16acc=True)
 
 
 def prefill_attention(q, kv: KVCache, ctx_len: int, softmax_scale=None, out=None,

@@ -82,7 +82,7 @@ int attention_common(const float *q, int T, int Hq, const stv_kv_layer *kv, int 
                      const uint64_t *mask, bool causal, float scale, float *out, float *out_lse,
                      void *ws, size_t ws_bytes, int n_splits, int32_t *dbg_logits, int8_t *dbg_q,
                      float *dbg_qscale, void *stream, float *partials_o = nullptr,
-                     float *partials_lse = nullptr) {
+                     float *partials_lse = nullptr, bool pv16 = false) {
     const bool partials_only = partials_o != nullptr;
     if (!q || (!out && !partials_only)) return fail(STV_EINVAL, "q and out must not be NULL");
     if (partials_only && !partials_lse) return fail(STV_EINVAL, "part_lse must not be NULL");
@@ -102,6 +102,8 @@ int attention_common(const float *q, int T, int Hq, const stv_kv_layer *kv, int 
     if (dbg_logits && (long long)T * Hq * (L + T) * (D / 32) >= (1ll << 40))
         return fail(STV_EINVAL, "dbg_logits would be too large");
     const int fmt = kv->kv_format;
+    if (pv16 && fmt != STV_KV_3BIT)
+        return fail(STV_EINVAL, "fp16-accumulated P.V reads the 3-bit format only");
     const stv::Plan plan = stv::make_plan(T, Hq, Hkv, D, L, causal, n_splits, fmt);
     if (!partials_only && plan.S > 1 && (!ws || ws_bytes < plan.ws_bytes))
         return fail(STV_EWORKSPACE, "workspace of %zu bytes needed for %d splits (got %zu)",
@@ -146,8 +148,8 @@ int attention_common(const float *q, int T, int Hq, const stv_kv_layer *kv, int 
 
     hipStream_t st = static_cast<hipStream_t>(stream);
     const bool debug = dbg_logits || dbg_q || dbg_qscale;
-    hipError_t e = plan.dec ? stv::launch_attention_dec(a, D, causal, debug, st)
-                            : stv::launch_attention(a, D, plan.NW, causal, debug, fmt, st);
+    hipError_t e = plan.dec ? stv::launch_attention_dec(a, D, causal, debug, pv16, st)
+                            : stv::launch_attention(a, D, plan.NW, causal, debug, fmt, pv16, st);
     if (e != hipSuccess) return fail(STV_EHIP, "attention launch failed: %s", hipGetErrorString(e));
     if (!partials_only && plan.S > 1) {
         e = stv::launch_merge(a.part_o, a.part_lse, plan.S, (int)rows, D, out, out_lse, st);
@@ -260,7 +262,7 @@ extern "C" {
 
 const char *stv_last_error(void) { return g_err; }
 
-int32_t stv_abi_version(void) { return 2; }
+int32_t stv_abi_version(void) { return 3; }
 
 int stv_kv_quant_pack(const float *x, int32_t n_tok, int32_t pos0, int32_t which,
                       uint32_t *codes, uint16_t *scales, int32_t n_kv_heads, int32_t head_dim,
@@ -314,6 +316,16 @@ int stv_verify_attention(const float *q, int32_t T, int32_t n_q_heads, const stv
     return attention_common(q, T, n_q_heads, kv, ctx_len, anc_mask, false, softmax_scale, out,
                             out_lse, workspace, workspace_bytes, n_splits, dbg_logits, dbg_q,
                             dbg_qscale, stream);
+}
+
+int stv_verify_attention_fp16acc(const float *q, int32_t T, int32_t n_q_heads,
+                                 const stv_kv_layer *kv, int32_t ctx_len,
+                                 const uint64_t *anc_mask, float softmax_scale, float *out,
+                                 float *out_lse, void *workspace, size_t workspace_bytes,
+                                 int32_t n_splits, void *stream) {
+    return attention_common(q, T, n_q_heads, kv, ctx_len, anc_mask, false, softmax_scale, out,
+                            out_lse, workspace, workspace_bytes, n_splits, nullptr, nullptr,
+                            nullptr, stream, nullptr, nullptr, true);
 }
 
 int stv_prefill_attention(const float *q, int32_t T, int32_t n_q_heads, const stv_kv_layer *kv,

@@ -59,10 +59,12 @@ long long attention_slots(int D, int NW, bool causal, bool dec, int fmt);
 
 Plan make_plan(int T, int Hq, int Hkv, int D, int L, bool causal, int n_splits_req, int fmt);
 
-// Launchers return the hipError_t of the launch.
+// Launchers return the hipError_t of the launch.  pv16 selects the
+// fp16-accumulated P.V variant (3-bit format, verify rows, no debug output;
+// anything else with pv16 set is hipErrorInvalidValue).
 hipError_t launch_attention(const AttnArgs &a, int D, int NW, bool causal, bool debug, int fmt,
-                            hipStream_t stream);
-hipError_t launch_attention_dec(const AttnArgs &a, int D, bool causal, bool debug,
+                            bool pv16, hipStream_t stream);
+hipError_t launch_attention_dec(const AttnArgs &a, int D, bool causal, bool debug, bool pv16,
                                 hipStream_t stream);
 hipError_t launch_merge(const float *part_o, const float *part_lse, int S, int rows, int D,
                         float *out, float *out_lse, hipStream_t stream);

@@ -558,7 +558,11 @@ struct TileIo4 {
 template <int D, int NT, int FMT>
 using TileIoOf = typename std::conditional<FMT == 0, TileIo<D, NT>, TileIo4<D, NT>>::type;
 
-template <int D, int NW, bool CAUSAL, bool DEBUG, int FMT>
+// PV16 selects the fp16-accumulated P.V variant (3-bit, verify only): each
+// 32-key tile's P.V product still comes out of an fp32 MFMA, but it is
+// rounded to fp16 and added into fp16 accumulators, and the running max
+// follows every increase (so P <= 1 and the fp16 sums stay in range).
+template <int D, int NW, bool CAUSAL, bool DEBUG, int FMT, bool PV16>
 __global__ __launch_bounds__(NW * 64) void attn_split_kernel(const AttnArgs a) {
     constexpr int NB = D / 32;
     constexpr int KT = kKeyTile;
@@ -687,9 +691,15 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(const AttnArgs a) {
     f32x16 oacc[NB];
 #pragma unroll
     for (int dt = 0; dt < NB; ++dt) oacc[dt] = f32x16{};
+    f16x2 oh[PV16 ? NB : 1][8];          // fp16 accumulators of the PV16 variant
+#pragma unroll
+    for (int dt = 0; dt < (PV16 ? NB : 1); ++dt)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) oh[dt][j] = f16x2{};
     // Running max in base-2 logit units.  It only moves when a tile's max
     // exceeds it by more than 8 (so exp2 stays below 256, well inside fp16),
-    // which makes rescaling the accumulators rare.
+    // which makes rescaling the accumulators rare.  PV16: by any amount.
+    constexpr float kLazy = PV16 ? 0.0f : 8.0f;
     float m_run = -INFINITY;
     float l_run = 0.0f;
 
@@ -792,14 +802,23 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(const AttnArgs a) {
             amax = max_halves(amax);
             // a row with c_row == 0 has all visible logits 0
             const float tmax = amax == -INFINITY ? -INFINITY : amax * c_row;
-            const float m_new = tmax > m_run + 8.0f ? tmax : m_run;
+            const float m_new = tmax > m_run + kLazy ? tmax : m_run;
             if (__any(m_new != m_run)) {
                 const float alpha = m_new != m_run ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
                 l_run *= alpha;
+                if constexpr (PV16) {
 #pragma unroll
-                for (int dt = 0; dt < NB; ++dt)
+                    for (int dt = 0; dt < NB; ++dt)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+                        for (int j = 0; j < 8; ++j)
+                            oh[dt][j] = __builtin_convertvector(
+                                __builtin_convertvector(oh[dt][j], f32x2) * alpha, f16x2);
+                } else {
+#pragma unroll
+                    for (int dt = 0; dt < NB; ++dt)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+                }
                 m_run = m_new;
             }
             const float mm = m_run == -INFINITY ? 0.0f : m_run;
@@ -828,13 +847,29 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(const AttnArgs a) {
                 }
             l_run += psum;
             __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
+            if constexpr (PV16) {
+                // the tile's 32 keys in one fp32 product, then one fp16
+                // rounding and one fp16 add per accumulator
 #pragma unroll
                 for (int dt = 0; dt < NB; ++dt) {
-                    const f16x8 vop = *reinterpret_cast<const f16x8 *>(
-                        vt_lane + (dt * 32) * L::VTS + dt * L::VBPAD + 16 * ks);
-                    oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vop, pk[ks], oacc[dt], 0, 0, 0);
+                    const _Float16 *vrow = vt_lane + (dt * 32) * L::VTS + dt * L::VBPAD;
+                    f32x16 tp = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                        *reinterpret_cast<const f16x8 *>(vrow), pk[0], f32x16{}, 0, 0, 0);
+                    tp = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                        *reinterpret_cast<const f16x8 *>(vrow + 16), pk[1], tp, 0, 0, 0);
+#pragma unroll
+                    for (int j = 0; j < 8; ++j)
+                        oh[dt][j] += __builtin_convertvector(f32x2{tp[2 * j], tp[2 * j + 1]}, f16x2);
+                }
+            } else {
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+                    for (int dt = 0; dt < NB; ++dt) {
+                        const f16x8 vop = *reinterpret_cast<const f16x8 *>(
+                            vt_lane + (dt * 32) * L::VTS + dt * L::VBPAD + 16 * ks);
+                        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vop, pk[ks], oacc[dt], 0, 0, 0);
+                    }
                 }
             }
             __builtin_amdgcn_s_setprio(0);
@@ -853,6 +888,15 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(const AttnArgs a) {
 
     // ---- epilogue
     if (!wave_active) return;
+    if constexpr (PV16) {
+#pragma unroll
+        for (int dt = 0; dt < NB; ++dt)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                oacc[dt][2 * j] = (float)oh[dt][j].x;
+                oacc[dt][2 * j + 1] = (float)oh[dt][j].y;
+            }
+    }
     const float l_tot = sum_halves(l_run);
     const float inv_l = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
     const float lse = l_tot > 0.0f ? (m_run + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
@@ -911,7 +955,8 @@ struct DecWaveLds {
     alignas(16) uint16_t svs[NB][32];
 };
 
-template <int D, bool CAUSAL, bool DEBUG>
+// PV16: the fp16-accumulated P.V variant, as in the split kernel.
+template <int D, bool CAUSAL, bool DEBUG, bool PV16>
 __global__ __launch_bounds__(kDecWaves * 64) void attn_dec_kernel(const AttnArgs a) {
     constexpr int NB = D / 32;
     constexpr int NDT = D / 16;
@@ -998,6 +1043,10 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_dec_kernel(const AttnArgs
     f32x4 oacc[NDT];
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) oacc[dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    f16x2 oh[PV16 ? NDT : 1][2];
+#pragma unroll
+    for (int dt = 0; dt < (PV16 ? NDT : 1); ++dt) oh[dt][0] = oh[dt][1] = f16x2{};
+    constexpr float kLazy = PV16 ? 0.0f : 8.0f;
     float m_run = -INFINITY;
     float l_run = 0.0f;
 
@@ -1114,7 +1163,8 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_dec_kernel(const AttnArgs
             }
         }
 
-        // ---- mask, online softmax in base 2 (running max moves by > 8 only)
+        // ---- mask, online softmax in base 2 (running max moves by > 8 only;
+        // PV16: by any amount)
         const bool masked = kb + KT > vis_from;
         if (masked) {
 #pragma unroll
@@ -1134,12 +1184,21 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_dec_kernel(const AttnArgs
         amax = fmaxf(amax, __shfl_xor(amax, 16));
         amax = max_halves(amax);
         const float tmax = amax == -INFINITY ? -INFINITY : amax * c_row;
-        const float m_new = tmax > m_run + 8.0f ? tmax : m_run;
+        const float m_new = tmax > m_run + kLazy ? tmax : m_run;
         if (__any(m_new != m_run)) {
             const float alpha = m_new != m_run ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
             l_run *= alpha;
+            if constexpr (PV16) {
 #pragma unroll
-            for (int dt = 0; dt < NDT; ++dt) oacc[dt] *= alpha;
+                for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                    for (int j = 0; j < 2; ++j)
+                        oh[dt][j] = __builtin_convertvector(
+                            __builtin_convertvector(oh[dt][j], f32x2) * alpha, f16x2);
+            } else {
+#pragma unroll
+                for (int dt = 0; dt < NDT; ++dt) oacc[dt] *= alpha;
+            }
             m_run = m_new;
         }
         const float mm = m_run == -INFINITY ? 0.0f : m_run;
@@ -1185,7 +1244,13 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_dec_kernel(const AttnArgs
                 const uint32_t v2 = __builtin_amdgcn_perm(tb, tb, 0x010C000Cu);
                 const uint32_t v3 = __builtin_amdgcn_perm(tb, tb, 0x030C020Cu);
                 const f16x8 vop = __builtin_bit_cast(f16x8, u32x4{v0, v1, v2, v3});
-                oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop, pb, oacc[dt], 0, 0, 0);
+                if constexpr (PV16) {
+                    const f32x4 tp = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop, pb, f32x4{}, 0, 0, 0);
+                    oh[dt][0] += __builtin_convertvector(f32x2{tp[0], tp[1]}, f16x2);
+                    oh[dt][1] += __builtin_convertvector(f32x2{tp[2], tp[3]}, f16x2);
+                } else {
+                    oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop, pb, oacc[dt], 0, 0, 0);
+                }
             }
         }
         __builtin_amdgcn_s_setprio(0);
@@ -1200,6 +1265,12 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_dec_kernel(const AttnArgs
         process(r1, kb + stride);
     }
 
+    if constexpr (PV16) {
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+            oacc[dt] = f32x4{(float)oh[dt][0].x, (float)oh[dt][0].y, (float)oh[dt][1].x,
+                             (float)oh[dt][1].y};
+    }
     // ---- merge the four waves' softmax states through LDS, in wave order
     float l_row = l_run + __shfl_xor(l_run, 16);
     l_row = sum_halves(l_row);
@@ -1361,27 +1432,34 @@ __global__ __launch_bounds__(kMergeMaxThreads) void merge_kernel(
     }
 }
 
-template <int D, int NW, bool CAUSAL, bool DEBUG, int FMT>
+template <int D, int NW, bool CAUSAL, bool DEBUG, int FMT, bool PV16 = false>
 hipError_t launch_t(const AttnArgs &a, hipStream_t stream) {
     const int grid = a.n_hs_pad * a.NRG;
-    hipLaunchKernelGGL((attn_split_kernel<D, NW, CAUSAL, DEBUG, FMT>), dim3(grid), dim3(NW * 64),
-                       0, stream, a);
+    hipLaunchKernelGGL((attn_split_kernel<D, NW, CAUSAL, DEBUG, FMT, PV16>), dim3(grid),
+                       dim3(NW * 64), 0, stream, a);
     return hipGetLastError();
 }
 
+// The PV16 variant exists for the 3-bit format, verify rows, no debug output.
 template <int D, int NW, int FMT>
-hipError_t launch_d(const AttnArgs &a, bool causal, bool debug, hipStream_t s) {
+hipError_t launch_d(const AttnArgs &a, bool causal, bool debug, bool pv16, hipStream_t s) {
+    if (pv16) {
+        if constexpr (FMT == 0) {
+            if (!causal && !debug) return launch_t<D, NW, false, false, 0, true>(a, s);
+        }
+        return hipErrorInvalidValue;
+    }
     if (causal)
         return debug ? launch_t<D, NW, true, true, FMT>(a, s) : launch_t<D, NW, true, false, FMT>(a, s);
     return debug ? launch_t<D, NW, false, true, FMT>(a, s) : launch_t<D, NW, false, false, FMT>(a, s);
 }
 
 template <int D, int FMT>
-hipError_t launch_nw(const AttnArgs &a, int NW, bool causal, bool debug, hipStream_t s) {
+hipError_t launch_nw(const AttnArgs &a, int NW, bool causal, bool debug, bool pv16, hipStream_t s) {
     switch (NW) {
-        case 1: return launch_d<D, 1, FMT>(a, causal, debug, s);
-        case 2: return launch_d<D, 2, FMT>(a, causal, debug, s);
-        case 4: return launch_d<D, 4, FMT>(a, causal, debug, s);
+        case 1: return launch_d<D, 1, FMT>(a, causal, debug, pv16, s);
+        case 2: return launch_d<D, 2, FMT>(a, causal, debug, pv16, s);
+        case 4: return launch_d<D, 4, FMT>(a, causal, debug, pv16, s);
         default: return hipErrorInvalidValue;
     }
 }
@@ -1390,7 +1468,7 @@ template <int D, int NW, bool CAUSAL, int FMT>
 int occupancy_t() {
     int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &n, reinterpret_cast<const void *>(&attn_split_kernel<D, NW, CAUSAL, false, FMT>),
+            &n, reinterpret_cast<const void *>(&attn_split_kernel<D, NW, CAUSAL, false, FMT, false>),
             NW * 64, 0) != hipSuccess)
         return 0;
     return n;
@@ -1406,15 +1484,19 @@ int occupancy_d(int NW, bool causal) {
     }
 }
 
-template <int D, bool CAUSAL, bool DEBUG>
+template <int D, bool CAUSAL, bool DEBUG, bool PV16 = false>
 hipError_t launch_dec_t(const AttnArgs &a, hipStream_t stream) {
-    hipLaunchKernelGGL((attn_dec_kernel<D, CAUSAL, DEBUG>), dim3(a.Hkv * a.S),
+    hipLaunchKernelGGL((attn_dec_kernel<D, CAUSAL, DEBUG, PV16>), dim3(a.Hkv * a.S),
                        dim3(kDecWaves * 64), 0, stream, a);
     return hipGetLastError();
 }
 
 template <int D>
-hipError_t launch_dec_d(const AttnArgs &a, bool causal, bool debug, hipStream_t s) {
+hipError_t launch_dec_d(const AttnArgs &a, bool causal, bool debug, bool pv16, hipStream_t s) {
+    if (pv16) {
+        if (causal || debug) return hipErrorInvalidValue;
+        return launch_dec_t<D, false, false, true>(a, s);
+    }
     if (causal) return debug ? launch_dec_t<D, true, true>(a, s) : launch_dec_t<D, true, false>(a, s);
     return debug ? launch_dec_t<D, false, true>(a, s) : launch_dec_t<D, false, false>(a, s);
 }
@@ -1423,7 +1505,7 @@ template <int D, bool CAUSAL>
 int occupancy_dec_t() {
     int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &n, reinterpret_cast<const void *>(&attn_dec_kernel<D, CAUSAL, false>), kDecWaves * 64,
+            &n, reinterpret_cast<const void *>(&attn_dec_kernel<D, CAUSAL, false, false>), kDecWaves * 64,
             0) != hipSuccess)
         return 0;
     return n;
@@ -1440,12 +1522,12 @@ int attention_dec_wgs_per_cu(int D, bool causal) {
     }
 }
 
-hipError_t launch_attention_dec(const AttnArgs &a, int D, bool causal, bool debug,
+hipError_t launch_attention_dec(const AttnArgs &a, int D, bool causal, bool debug, bool pv16,
                                 hipStream_t stream) {
     switch (D) {
-        case 64: return launch_dec_d<64>(a, causal, debug, stream);
-        case 128: return launch_dec_d<128>(a, causal, debug, stream);
-        case 256: return launch_dec_d<256>(a, causal, debug, stream);
+        case 64: return launch_dec_d<64>(a, causal, debug, pv16, stream);
+        case 128: return launch_dec_d<128>(a, causal, debug, pv16, stream);
+        case 256: return launch_dec_d<256>(a, causal, debug, pv16, stream);
         default: return hipErrorInvalidValue;
     }
 }
@@ -1468,19 +1550,19 @@ int attention_wgs_per_cu(int D, int NW, bool causal, int fmt) {
 }
 
 hipError_t launch_attention(const AttnArgs &a, int D, int NW, bool causal, bool debug, int fmt,
-                            hipStream_t stream) {
+                            bool pv16, hipStream_t stream) {
     if (fmt == 1) {
         switch (D) {
-            case 64: return launch_nw<64, 1>(a, NW, causal, debug, stream);
-            case 128: return launch_nw<128, 1>(a, NW, causal, debug, stream);
-            case 256: return launch_nw<256, 1>(a, NW, causal, debug, stream);
+            case 64: return launch_nw<64, 1>(a, NW, causal, debug, pv16, stream);
+            case 128: return launch_nw<128, 1>(a, NW, causal, debug, pv16, stream);
+            case 256: return launch_nw<256, 1>(a, NW, causal, debug, pv16, stream);
             default: return hipErrorInvalidValue;
         }
     }
     switch (D) {
-        case 64: return launch_nw<64, 0>(a, NW, causal, debug, stream);
-        case 128: return launch_nw<128, 0>(a, NW, causal, debug, stream);
-        case 256: return launch_nw<256, 0>(a, NW, causal, debug, stream);
+        case 64: return launch_nw<64, 0>(a, NW, causal, debug, pv16, stream);
+        case 128: return launch_nw<128, 0>(a, NW, causal, debug, pv16, stream);
+        case 256: return launch_nw<256, 0>(a, NW, causal, debug, pv16, stream);
         default: return hipErrorInvalidValue;
     }
 }

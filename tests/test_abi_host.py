@@ -37,14 +37,15 @@ def stvmod():
 
 def _declared():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(stv_[a-z_]+)\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(stv_[a-z_0-9]+)\(", text, re.M)))
 
 
 def test_header_declares_the_four_operations():
     names = _declared()
     for op in ("stv_kv_quant_pack", "stv_verify_attention", "stv_prefill_attention",
                "stv_split_merge", "stv_attention_plan", "stv_last_error", "stv_abi_version",
-               "stv_tree_accept", "stv_kv_commit", "stv_lookup_plan", "stv_lookup_draft"):
+               "stv_tree_accept", "stv_kv_commit", "stv_lookup_plan", "stv_lookup_draft",
+               "stv_verify_attention_fp16acc"):
         assert op in names
 
 
@@ -55,7 +56,7 @@ def test_library_exports_every_declared_symbol(lib, stvmod):
     for name in _declared():
         assert name in exported, name
         assert hasattr(lib, name)
-    assert lib.stv_abi_version() == 2
+    assert lib.stv_abi_version() == 3
 
 
 def _layer(stvmod, hkv=4, d=256, cap=1000):
@@ -116,6 +117,25 @@ def test_format_errors(lib, stvmod):
     unknown = stvmod._KVLayer(FAKE, FAKE, FAKE, FAKE, 4, 256, 1000, 3)
     assert lib.stv_kv_commit(ctypes.byref(unknown), 0, 8, FAKE, FAKE, None) == E.STV_EINVAL
     assert "kv_format" in _err(lib)
+
+
+def test_fp16acc_errors(lib, stvmod):
+    """The fp16-accumulated variant checks what verify checks, and reads the
+    3-bit format only."""
+    E = stvmod
+    m = np.ascontiguousarray(synth.ancestor_masks(synth.chain_parents(8)))
+    f = lib.stv_verify_attention_fp16acc
+    four = stvmod._KVLayer(FAKE, FAKE, FAKE, FAKE, 4, 256, 1000, 1)
+    assert f(FAKE, 8, 24, ctypes.byref(four), 100, m.ctypes.data, 0.0625, FAKE, None, None, 0,
+             0, None) == E.STV_EINVAL
+    assert "3-bit" in _err(lib)
+    three = _layer(stvmod)
+    assert f(FAKE, 8, 24, ctypes.byref(three), 993, m.ctypes.data, 0.0625, FAKE, None, None, 0,
+             0, None) == E.STV_ECAPACITY
+    bad = m.copy()
+    bad[3] &= ~np.uint64(1 << 3)
+    assert f(FAKE, 8, 24, ctypes.byref(three), 100, bad.ctypes.data, 0.0625, FAKE, None, None,
+             0, 0, None) == E.STV_EMASK
 
 
 def test_verify_mask_errors(lib, stvmod):

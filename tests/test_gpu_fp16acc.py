@@ -1,0 +1,149 @@
+"""GPU: the fp16-accumulated P.V variant of verify attention against the
+fp64 oracle (elpis, "What fast means": the fp16-accumulated P.V decode
+kernel, which the pages list as unresolved).
+
+The variant rounds each 32-key tile's P.V product to fp16 and adds it into
+fp16 accumulators, so it cannot meet the 2e-3 bar of the fp32 path in
+general.  What holds at any size is a bound derived from the arithmetic:
+with unit roundoff u = 2^-11, P <= 1 (the running max follows every
+increase) and |V| <= Vmax, each tile adds at most three roundings of
+magnitude u * l_tile-so-far * Vmax (tile rounding, fp16 add, rescale), so
+after n tiles
+
+    |o - o_ref| <= TOL * max|o_ref| + 3 u n Vmax + 3 n 2^-25
+
+per row (the last term covers fp16 subnormal spacing; l >= 1 because the
+row's maximum key has P = 1; the split merge is a convex combination and
+adds nothing).  TOL = 2e-3 covers, as for the fp32 path, the fp16 rounding
+of P and V and the fp32 sums.  The lse takes no fp16 accumulation and stays
+within 2e-3.  The test also checks that the variant is a different
+computation from the fp32 path (not bit-identical on a long context).
+"""
+import math
+
+import numpy as np
+import pytest
+
+import synth
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+U16 = 2.0 ** -11
+
+
+@pytest.fixture(scope="module")
+def gpu():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import speculative_tree_verify_amd as stv
+    stv.load_library()
+    return stv, torch
+
+
+def _row_err_abs(got, ref):
+    return np.max(np.abs(got - ref), axis=-1)
+
+
+def _vmax(orc, host):
+    """Largest |V| any key can take: 4 times the largest V scale."""
+    return 4.0 * orc.f16_bits_to_f64(int(np.max(host.v_scales)))
+
+
+def _tiles_per_split(n_keys, S):
+    n_tiles = -(-n_keys // 32)
+    return -(-n_tiles // S)
+
+
+def run_fp16acc(gpu, orc, hq, hkv, d, L, T, seed, rows=None, n_splits=0, scale_mul=1.0,
+                host=None, q=None, mask=None):
+    stv, torch = gpu
+    rng = np.random.default_rng(seed)
+    if host is None:
+        host = synth.make_kv(rng, hkv, d, L + T, L + T + 5)
+    if q is None:
+        q = synth.make_q(rng, T, hq, d)
+    if mask is None:
+        mask = synth.ancestor_masks(synth.make_tree_parents(rng, T, min(8, T)) if T > 1
+                                    else synth.chain_parents(1))
+    scale = scale_mul / math.sqrt(d)
+    ref = orc.attention(q, host, L, mask, scale, rows=rows)
+    kv = stv.KVCache.from_host(host)
+    qd = torch.from_numpy(q).cuda()
+    lse16 = torch.empty((T, hq), dtype=torch.float32, device="cuda")
+    lse32 = torch.empty((T, hq), dtype=torch.float32, device="cuda")
+    o16 = stv.verify_attention_fp16acc(qd, kv, L, mask, scale, out_lse=lse16, n_splits=n_splits)
+    o32 = stv.verify_attention(qd, kv, L, mask, scale, out_lse=lse32, n_splits=n_splits)
+    torch.cuda.synchronize()
+    flat = np.arange(T * hq) if rows is None else np.asarray(rows)
+    fd = torch.from_numpy(flat).cuda()
+    g16 = o16.reshape(T * hq, d)[fd].cpu().numpy()
+    g32 = o32.reshape(T * hq, d)[fd].cpu().numpy()
+    assert np.all(np.isfinite(g16))
+    S, _ = stv.attention_plan(T, hq, hkv, d, L, False, n_splits)
+    n = _tiles_per_split(L + T, S)
+    ref_o = ref["out"]
+    bound = (TOL * np.max(np.abs(ref_o), axis=-1) + 3 * U16 * n * _vmax(orc, host)
+             + 3 * n * 2.0 ** -25)
+    err16 = _row_err_abs(g16, ref_o)
+    assert np.all(err16 <= bound), f"row error {err16.max():.3g} above bound {bound.min():.3g}"
+    l16 = lse16.reshape(-1)[fd].cpu().numpy()
+    assert np.max(np.abs(l16 - ref["lse"])) <= TOL
+    den = np.maximum(np.max(np.abs(ref_o), axis=-1), 1e-30)
+    return {"rel16": float(np.max(err16 / den)),
+            "rel32": float(np.max(_row_err_abs(g32, ref_o) / den)),
+            "identical": bool(np.array_equal(g16, g32)), "tiles": n, "splits": S}
+
+
+CASES = [
+    # name, hq, hkv, d, L, T, seed, n_splits
+    ("dec_one_token", 24, 4, 256, 4000, 1, 300, 0),         # few-row kernel
+    ("dec_one_token_d64", 4, 1, 64, 777, 1, 301, 3),
+    ("tree8", 24, 4, 256, 5000, 8, 302, 0),                  # split kernel, 2 waves
+    ("tree8_d128_one_split", 8, 2, 128, 1500, 8, 303, 1),
+    ("tree64", 24, 4, 256, 3000, 64, 304, 0),                # split kernel, 4 waves
+    ("tree3_ragged", 6, 2, 64, 45, 3, 305, 2),
+]
+
+
+@pytest.mark.parametrize("name,hq,hkv,d,L,T,seed,ns", CASES, ids=[c[0] for c in CASES])
+def test_fp16acc_within_bound(gpu, orc, name, hq, hkv, d, L, T, seed, ns):
+    r = run_fp16acc(gpu, orc, hq, hkv, d, L, T, seed, n_splits=ns)
+    print(f"{name}: fp16-acc max row error {r['rel16']:.3g}, fp32 path {r['rel32']:.3g}")
+
+
+def test_fp16acc_peaked(gpu, orc):
+    """Peaked logits move the running max often (many fp16 rescales)."""
+    run_fp16acc(gpu, orc, 24, 4, 256, 6000, 8, 310, scale_mul=16.0)
+
+
+def test_fp16acc_differs_from_fp32_path(gpu, orc):
+    """One split over a long context: the fp16 sums must show up."""
+    r = run_fp16acc(gpu, orc, 24, 4, 256, 20000, 8, 311, rows=[0, 5, 100, 191], n_splits=1)
+    assert not r["identical"]
+
+
+def test_fp16acc_rejects_4bit_cache(gpu):
+    stv, torch = gpu
+    rng = np.random.default_rng(312)
+    host = synth.make_kv4(rng, 1, 64, 100)
+    kv = stv.KVCache.from_host(host)
+    q = torch.from_numpy(synth.make_q(rng, 1, 4, 64)).cuda()
+    with pytest.raises(stv.StvError):
+        stv.verify_attention_fp16acc(q, kv, 99, [1])
+
+
+def test_fp16acc_8row_262k_sampled(gpu, orc):
+    """The pages' shape: the 8-row tree over 262,144 keys, rows of one KV
+    head against the oracle; reports both paths' errors."""
+    geom = [g for g in synth.EXTRA_CONFIGS if g.name == "tree8_262k"][0]
+    rng = np.random.default_rng(geom.seed)
+    host = synth.make_kv(rng, geom.n_kv_heads, geom.head_dim, geom.n_keys)
+    q = synth.make_q(rng, geom.n_rows, geom.n_q_heads, geom.head_dim)
+    mask = synth.ancestor_masks(synth.make_tree_parents(rng, geom.n_rows, geom.max_depth))
+    hq = geom.n_q_heads
+    rows = [t * hq + h for t in (0, 3, 7) for h in (0, 5)]
+    r = run_fp16acc(gpu, orc, hq, geom.n_kv_heads, geom.head_dim, geom.ctx_len, geom.n_rows,
+                    geom.seed, rows=rows, host=host, q=q, mask=mask)
+    print(f"tree8_262k ({r['splits']} splits, {r['tiles']} tiles each): fp16-acc max row "
+          f"error {r['rel16']:.3g}, fp32 path {r['rel32']:.3g}")
