@@ -204,7 +204,7 @@ Plan make_plan(int T, int Hq, int Hkv, int D, int L, bool causal, int n_splits_r
     p.dec = R <= kDecMaxRows && fmt == 0;
     if (p.dec) {
         p.NW = 4;
-        p.NRG = 1;
+        p.NRG = (int)((R + 15) / 16);
     } else {
         const long long row_tiles = (R + kRowTile - 1) / kRowTile;
         p.NW = row_tiles >= 4 ? 4 : (row_tiles >= 2 ? 2 : 1);

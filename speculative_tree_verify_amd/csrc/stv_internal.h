@@ -34,11 +34,12 @@ struct AttnArgs {
 };
 
 // Query rows per KV head up to which the few-row kernel (16-row MFMA tiles,
-// per-wave key tiles) runs instead of the 32-row tile kernel.
+// per-wave key tiles, one work-group per group of 16 rows) runs instead of
+// the 32-row tile kernel.
 constexpr int kDecMaxRows = 16;
 
 struct Plan {
-    bool dec;        // few-row kernel (then NW = 4 waves and NRG = 1)
+    bool dec;        // few-row kernel (then NW = 4 waves and NRG groups of 16 rows)
     int NW;          // waves (32-row tiles) per work-group
     int NRG;         // row groups per kv head
     int S;           // context splits

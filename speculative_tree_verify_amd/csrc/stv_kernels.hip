@@ -966,24 +966,33 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_dec_kernel(const AttnArgs
                   "the merge stages a wave's 16 x D outputs in its tile region");
     __shared__ __attribute__((aligned(16))) W wl[kDecWaves];
 
-    const int hs = blockIdx.x;
+    // ---- work-group -> (kv head, split, group of 16 rows).  The row groups
+    // of one (head, split) get ids 8 apart, so they run on one XCD and read
+    // the split's tiles through its L2.
+    const int id = blockIdx.x;
+    const int chunk = id / (8 * a.NRG);
+    const int within = id - chunk * 8 * a.NRG;
+    const int rg = within >> 3;
+    const int hs = chunk * 8 + (within & 7);
+    if (hs >= a.Hkv * a.S) return;
     const int head = hs / a.S;
     const int split = hs - head * a.S;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: tile bases stay scalar
-    const int i16 = lane & 15;          // row of this lane (and MFMA row/column index)
+    const int i16 = lane & 15;          // row of this lane in the group (MFMA row/column index)
     const int qc = lane >> 4;           // 8-element chunk / 4-key group of this lane
     W &my = wl[wave];
+    const int row0 = rg * 16;           // first row (t * G + g order) of the group
 
-    const bool row_ok = i16 < a.R;
-    const int t = row_ok ? i16 / a.G : 0;
-    const int g = row_ok ? i16 - t * a.G : 0;
+    const bool row_ok = row0 + i16 < a.R;
+    const int t = row_ok ? (row0 + i16) / a.G : 0;
+    const int g = row_ok ? row0 + i16 - t * a.G : 0;
     const int flat = t * a.Hq + head * a.G + g;
 
     const int k0 = split * a.split_len;
     int k1 = min(a.N, k0 + a.split_len);
-    if (CAUSAL) k1 = min(k1, a.L + (a.R - 1) / a.G + 1);
+    if (CAUSAL) k1 = min(k1, a.L + (min(a.R, row0 + 16) - 1) / a.G + 1);
     const int vis_from = min(k1, a.L);
 
     // ---- Q: lane (row i16, chunk qc) holds elements 32b + 8qc + [0, 8) of
@@ -1287,7 +1296,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_dec_kernel(const AttnArgs
     // thread -> (row r, 16 consecutive elements)
     const int r = tid >> 4;
     const int c0 = (tid & 15) * (D / 16);
-    if (r >= a.R) return;
+    if (row0 + r >= a.R) return;
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < kDecWaves; ++w)
@@ -1303,7 +1312,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_dec_kernel(const AttnArgs
     }
     const float inv_l = Lsum > 0.0f ? 1.0f / Lsum : 0.0f;
     const float lse = Lsum > 0.0f ? (M + log2f(Lsum)) * 0.69314718055994531f : -INFINITY;
-    const int tr = r / a.G, gr = r - tr * a.G;
+    const int tr = (row0 + r) / a.G, gr = row0 + r - tr * a.G;
     const int flat_r = tr * a.Hq + head * a.G + gr;
     const size_t rows_total = (size_t)a.T * a.Hq;
     const bool partial = a.part_o != nullptr;
@@ -1337,6 +1346,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_dec_kernel(const AttnArgs
 // keep many loads in flight.
 constexpr int kMergeMaxThreads = 1024;
 constexpr int kMergeWeights = 1024;      // weights cached in LDS for s < this
+constexpr int kMergePre = 8;             // partial vectors a thread loads up front
 
 __device__ __forceinline__ float block_reduce(float v, float *red, bool is_max) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -1370,13 +1380,32 @@ __global__ __launch_bounds__(kMergeMaxThreads) void merge_kernel(
     const int row = blockIdx.x;
     const int tid = threadIdx.x;
     const int nt = blockDim.x;
-    float M = -INFINITY;
-    for (int s = tid; s < S; s += nt) M = fmaxf(M, part_lse[(size_t)s * rows + row]);
+    // Vector path: thread (g, c) owns column group c of splits g, g + G, ...
+    // Its first kMergePre partial vectors are loaded before the weights are
+    // known, so their latency overlaps the two block reductions.
+    const bool vec = (D & 3) == 0;
+    const int C = vec ? D / 4 : 1;
+    const int g = tid / C, c = tid - (tid / C) * C;
+    const bool gv = vec && g < G;
+    const size_t split_stride = (size_t)rows * D;
+    const float *col = part_o + (size_t)row * D + 4 * c;
+    f32x4 pre[kMergePre];
+#pragma unroll
+    for (int u = 0; u < kMergePre; ++u) {
+        const int s = g + u * G;
+        pre[u] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        if (gv && s < S) pre[u] = *reinterpret_cast<const f32x4 *>(col + (size_t)s * split_stride);
+    }
+    // lse values of this thread's splits s = tid, tid + nt, ... (the first
+    // one kept in a register for the second pass)
+    const float ls0 = tid < S ? part_lse[(size_t)tid * rows + row] : -INFINITY;
+    float M = ls0;
+    for (int s = tid + nt; s < S; s += nt) M = fmaxf(M, part_lse[(size_t)s * rows + row]);
     M = block_reduce(M, red, true);
     float W = 0.0f;
     if (M != -INFINITY)
         for (int s = tid; s < S; s += nt) {
-            const float ls = part_lse[(size_t)s * rows + row];
+            const float ls = s == tid ? ls0 : part_lse[(size_t)s * rows + row];
             const float w = ls == -INFINITY ? 0.0f : expf(ls - M);
             W += w;
             if (s < kMergeWeights) wgt[s] = w;
@@ -1389,15 +1418,16 @@ __global__ __launch_bounds__(kMergeMaxThreads) void merge_kernel(
         for (int d = tid; d < D; d += nt) out[(size_t)row * D + d] = 0.0f;
         return;
     }
-    if ((D & 3) == 0) {
+    if (vec) {
         // An empty split (lse = -inf) has weight 0 and an all-zero partial.
-        const int C = D / 4;
-        const int g = tid / C, c = tid - (tid / C) * C;
         f32x4 o = {0.0f, 0.0f, 0.0f, 0.0f};
-        if (g < G) {
-            const float *col = part_o + (size_t)row * D + 4 * c;
-            const size_t split_stride = (size_t)rows * D;
-            for (int s0 = g; s0 < S; s0 += 4 * G) {
+        if (gv) {
+#pragma unroll
+            for (int u = 0; u < kMergePre; ++u) {
+                const int s = g + u * G;
+                if (s < S) o += merge_weight(part_lse, wgt, s, rows, row, M) * pre[u];
+            }
+            for (int s0 = g + kMergePre * G; s0 < S; s0 += 4 * G) {
                 f32x4 v[4];
                 float w[4];
 #pragma unroll
@@ -1486,7 +1516,7 @@ int occupancy_d(int NW, bool causal) {
 
 template <int D, bool CAUSAL, bool DEBUG, bool PV16 = false>
 hipError_t launch_dec_t(const AttnArgs &a, hipStream_t stream) {
-    hipLaunchKernelGGL((attn_dec_kernel<D, CAUSAL, DEBUG, PV16>), dim3(a.Hkv * a.S),
+    hipLaunchKernelGGL((attn_dec_kernel<D, CAUSAL, DEBUG, PV16>), dim3(a.n_hs_pad * a.NRG),
                        dim3(kDecWaves * 64), 0, stream, a);
     return hipGetLastError();
 }
