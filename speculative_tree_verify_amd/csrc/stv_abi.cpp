@@ -148,8 +148,9 @@ int attention_common(const float *q, int T, int Hq, const stv_kv_layer *kv, int 
 
     hipStream_t st = static_cast<hipStream_t>(stream);
     const bool debug = dbg_logits || dbg_q || dbg_qscale;
-    hipError_t e = plan.dec ? stv::launch_attention_dec(a, D, causal, debug, pv16, st)
-                            : stv::launch_attention(a, D, plan.NW, causal, debug, fmt, pv16, st);
+    hipError_t e = plan.dec   ? stv::launch_attention_dec(a, D, causal, debug, pv16, st)
+                   : plan.s16 ? stv::launch_attention_s16(a, D, causal, debug, pv16, st)
+                              : stv::launch_attention(a, D, plan.NW, causal, debug, fmt, pv16, st);
     if (e != hipSuccess) return fail(STV_EHIP, "attention launch failed: %s", hipGetErrorString(e));
     if (!partials_only && plan.S > 1) {
         e = stv::launch_merge(a.part_o, a.part_lse, plan.S, (int)rows, D, out, out_lse, st);
@@ -162,13 +163,13 @@ int attention_common(const float *q, int T, int Hq, const stv_kv_layer *kv, int 
 
 namespace stv {
 
-long long attention_slots(int D, int NW, bool causal, bool dec, int fmt) {
+long long attention_slots(int D, int NW, bool causal, int kind, int fmt) {
     // MI355X: 256 CUs; the D = 256 four-wave kernels hold two work-groups per CU.
     constexpr long long kFallback = 256LL * 2;
     struct Entry {
         int dev, D, NW;
-        bool causal, dec;
-        int fmt;
+        bool causal;
+        int kind, fmt;
         long long slots;
     };
     static std::mutex mu;
@@ -180,7 +181,7 @@ long long attention_slots(int D, int NW, bool causal, bool dec, int fmt) {
     }
     std::lock_guard<std::mutex> lock(mu);
     for (const Entry &e : cache)
-        if (e.dev == dev && e.D == D && e.NW == NW && e.causal == causal && e.dec == dec &&
+        if (e.dev == dev && e.D == D && e.NW == NW && e.causal == causal && e.kind == kind &&
             e.fmt == fmt)
             return e.slots;
     int cus = 0;
@@ -189,10 +190,11 @@ long long attention_slots(int D, int NW, bool causal, bool dec, int fmt) {
         (void)hipGetLastError();
         return kFallback;
     }
-    const int per_cu =
-        dec ? attention_dec_wgs_per_cu(D, causal) : attention_wgs_per_cu(D, NW, causal, fmt);
+    const int per_cu = kind == 1   ? attention_dec_wgs_per_cu(D, causal)
+                       : kind == 2 ? attention_s16_wgs_per_cu(D, causal)
+                                   : attention_wgs_per_cu(D, NW, causal, fmt);
     const long long slots = per_cu > 0 ? (long long)cus * per_cu : kFallback;
-    cache.push_back({dev, D, NW, causal, dec, fmt, slots});
+    cache.push_back({dev, D, NW, causal, kind, fmt, slots});
     return slots;
 }
 
@@ -202,9 +204,13 @@ Plan make_plan(int T, int Hq, int Hkv, int D, int L, bool causal, int n_splits_r
     const long long R = (long long)T * G;
     // the few-row kernel reads the 3-bit format only
     p.dec = R <= kDecMaxRows && fmt == 0;
+    p.s16 = !p.dec && R <= kS16MaxRows && fmt == 0;
     if (p.dec) {
         p.NW = 4;
         p.NRG = (int)((R + 15) / 16);
+    } else if (p.s16) {
+        p.NW = 4;
+        p.NRG = (int)((R + 63) / 64);
     } else {
         const long long row_tiles = (R + kRowTile - 1) / kRowTile;
         p.NW = row_tiles >= 4 ? 4 : (row_tiles >= 2 ? 2 : 1);
@@ -219,7 +225,7 @@ Plan make_plan(int T, int Hq, int Hkv, int D, int L, bool causal, int n_splits_r
         // Fill the device's resident work-group slots exactly once: one
         // round of equal work-groups, no straggling partial round.  Splits
         // keep at least four tiles.
-        const long long slots = attention_slots(D, p.NW, causal, p.dec, fmt);
+        const long long slots = attention_slots(D, p.NW, causal, p.dec ? 1 : (p.s16 ? 2 : 0), fmt);
         const long long groups = (long long)Hkv * p.NRG;
         if (groups < slots) {
             S = slots / groups;

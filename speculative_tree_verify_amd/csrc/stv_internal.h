@@ -37,9 +37,13 @@ struct AttnArgs {
 // per-wave key tiles, one work-group per group of 16 rows) runs instead of
 // the 32-row tile kernel.
 constexpr int kDecMaxRows = 16;
+// Query rows per KV head up to which the 16-row shared-tile kernel runs
+// (3-bit format); above it, the 32-row tile kernel.
+constexpr int kS16MaxRows = 64;
 
 struct Plan {
     bool dec;        // few-row kernel (then NW = 4 waves and NRG groups of 16 rows)
+    bool s16;        // 16-row shared-tile kernel (then NW = 4 waves and NRG groups of 64 rows)
     int NW;          // waves (32-row tiles) per work-group
     int NRG;         // row groups per kv head
     int S;           // context splits
@@ -53,10 +57,12 @@ struct Plan {
 // per-token-head scales.
 int attention_wgs_per_cu(int D, int NW, bool causal, int fmt);
 int attention_dec_wgs_per_cu(int D, bool causal);
+int attention_s16_wgs_per_cu(int D, bool causal);
 
 // Resident work-group slots of the current device for a kernel variant
 // (CUs x work-groups per CU); a fixed MI355X figure when no device answers.
-long long attention_slots(int D, int NW, bool causal, bool dec, int fmt);
+// kind: 0 = 32-row tile kernel, 1 = few-row kernel, 2 = 16-row shared-tile kernel.
+long long attention_slots(int D, int NW, bool causal, int kind, int fmt);
 
 Plan make_plan(int T, int Hq, int Hkv, int D, int L, bool causal, int n_splits_req, int fmt);
 
@@ -66,6 +72,8 @@ Plan make_plan(int T, int Hq, int Hkv, int D, int L, bool causal, int n_splits_r
 hipError_t launch_attention(const AttnArgs &a, int D, int NW, bool causal, bool debug, int fmt,
                             bool pv16, hipStream_t stream);
 hipError_t launch_attention_dec(const AttnArgs &a, int D, bool causal, bool debug, bool pv16,
+                                hipStream_t stream);
+hipError_t launch_attention_s16(const AttnArgs &a, int D, bool causal, bool debug, bool pv16,
                                 hipStream_t stream);
 hipError_t launch_merge(const float *part_o, const float *part_lse, int S, int rows, int D,
                         float *out, float *out_lse, hipStream_t stream);

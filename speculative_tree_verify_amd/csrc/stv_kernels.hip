@@ -922,6 +922,260 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(const AttnArgs a) {
     }
 }
 
+// ------------------------------------------ attention, 16-row tiles, shared tiles
+//
+// For 17..64 query rows per KV head (the 8-row tree: 48 rows): the split
+// kernel's shared tile (one unpack per work-group into LDS: int8 K, fp16
+// V^ = s * (c - 4), fp16 K scales) feeding four waves of 16 rows each, with
+// 16x16 MFMAs: Q.K^T on v_mfma_i32_16x16x32_i8 (exact int32 per 32-element
+// block), P.V on v_mfma_f32_16x16x32_f16.  A wave holds 16 rows x D fp32
+// accumulators (64 VGPRs at D = 256, half the 32-row tile's), which with Q in
+// registers and the tile in LDS leaves room for three waves per SIMD.
+// 3-bit format only.  PV16: the fp16-accumulated P.V variant, as in the
+// split kernel.
+typedef int32_t i32x4s __attribute__((ext_vector_type(4)));
+typedef int64_t i64_t;
+
+template <int D, bool CAUSAL, bool DEBUG, bool PV16>
+__global__ __launch_bounds__(256) void attn_split16_kernel(const AttnArgs a) {
+    constexpr int NB = D / 32;
+    constexpr int NDT = D / 16;
+    constexpr int KT = kKeyTile;
+    constexpr int NW = 4;
+    constexpr int NT = NW * 64;
+    using L = TileLds<D>;
+    __shared__ __attribute__((aligned(16))) L lds;
+
+    // ---- work-group -> (kv head, split, group of 64 rows); the row groups of
+    // one (head, split) get ids 8 apart so they share an XCD and its L2.
+    const int id = blockIdx.x;
+    const int chunk = id / (8 * a.NRG);
+    const int within = id - chunk * 8 * a.NRG;
+    const int rg = within >> 3;
+    const int hs = chunk * 8 + (within & 7);
+    if (hs >= a.Hkv * a.S) return;
+    const int head = hs / a.S;
+    const int split = hs - head * a.S;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int i16 = lane & 15;          // row of this lane in the wave's 16 (MFMA column)
+    const int qc = lane >> 4;           // 8-element chunk / 8-key group of this lane
+    const int row0 = (rg * NW + wave) * 16;
+    const bool wave_active = row0 < a.R;
+    const bool row_ok = row0 + i16 < a.R;
+    const int t = row_ok ? (row0 + i16) / a.G : 0;
+    const int g = row_ok ? row0 + i16 - t * a.G : 0;
+    const int flat = t * a.Hq + head * a.G + g;
+
+    const int k0 = split * a.split_len;
+    int k1 = min(a.N, k0 + a.split_len);
+    if (CAUSAL) {
+        const int rho_last = min(a.R, (rg + 1) * NW * 16) - 1;
+        k1 = min(k1, a.L + rho_last / a.G + 1);
+    }
+    const int vis_from = min(k1, a.L);
+
+    // ---- Q: lane (row i16, chunk qc) quantizes and holds elements
+    // 32b + 8qc + [0, 8) of every block b (B operand of the 16x16x32 MFMA)
+    i64_t qop[NB];
+    float sq;
+    {
+        const float *qrow = a.q + (size_t)flat * D + 8 * qc;
+        float amax = 0.0f;
+        if (row_ok) {
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const f32x4 v = *reinterpret_cast<const f32x4 *>(qrow + 32 * b + 4 * j);
+                    amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+                }
+        }
+        amax = fmaxf(amax, __shfl_xor(amax, 16));
+        amax = max_halves(amax);
+        const float inv = amax > 0.0f ? 127.0f / amax : 0.0f;
+        sq = amax / 127.0f;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            uint32_t w2[2] = {0u, 0u};
+            if (row_ok) {
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const f32x4 v = *reinterpret_cast<const f32x4 *>(qrow + 32 * b + 4 * j);
+                    const float e[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        float r = rintf(e[i] * inv);
+                        r = fminf(fmaxf(r, -127.0f), 127.0f);
+                        w2[j] |= ((uint32_t)(int)r & 0xFFu) << (8 * i);
+                    }
+                }
+            }
+            qop[b] = (i64_t)((uint64_t)w2[0] | ((uint64_t)w2[1] << 32));
+        }
+        if (DEBUG && split == 0 && row_ok) {
+            if (a.dbg_q) {
+#pragma unroll
+                for (int b = 0; b < NB; ++b)
+                    *reinterpret_cast<i64_t *>(a.dbg_q + (size_t)flat * D + 32 * b + 8 * qc) = qop[b];
+            }
+            if (a.dbg_qscale && qc == 0) a.dbg_qscale[flat] = sq;
+        }
+    }
+    const float c_row = sq * a.scale_log2;
+    uint64_t mrow = 0;
+    if (!CAUSAL) {
+        for (int tt = 0; tt < a.T; ++tt)
+            if (tt == t) mrow = a.mask[tt];
+    }
+
+    // A operand row m of key half kh reads key 8(m / 4) + 4kh + m % 4, so the
+    // result registers of lane (i16, qc) hold keys 8qc + 4kh + [0, 4): its
+    // eight logits are keys 8qc + [0, 8), the run the P.V operand wants.
+    const int krow0 = 8 * (i16 >> 2) + (i16 & 3);
+    const int8_t *kq_lane = lds.kq + krow0 * L::KQS + 8 * qc;
+
+    f32x4 oacc[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) oacc[dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    f16x2 oh[PV16 ? NDT : 1][2];
+#pragma unroll
+    for (int dt = 0; dt < (PV16 ? NDT : 1); ++dt) oh[dt][0] = oh[dt][1] = f16x2{};
+    // base-2 running max; moves by more than 8 only (PV16: by any amount)
+    constexpr float kLazy = PV16 ? 0.0f : 8.0f;
+    float m_run = -INFINITY;
+    float l_run = 0.0f;
+
+    TileIo<D, NT> io;
+    io.load(a, head, k0, k0, k1, tid);
+    for (int kb = k0; kb < k1; kb += KT) {
+        io.store(lds, tid, min(KT, k1 - kb));
+        __syncthreads();
+        io.load(a, head, kb + KT, k0, k1, tid);
+
+        if (wave_active) {
+            // ---- Q.K^T, one int8 MFMA per (block, key half), fp32 epilogue
+            float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                const f16x8 h = *reinterpret_cast<const f16x8 *>(lds.skh + b * KT + 8 * qc);
+#pragma unroll
+                for (int kh = 0; kh < 2; ++kh) {
+                    const i64_t kop = *reinterpret_cast<const i64_t *>(kq_lane + 4 * kh * L::KQS + 32 * b);
+                    const i32x4s sres = __builtin_amdgcn_mfma_i32_16x16x32_i8(kop, qop[b], i32x4s{}, 0, 0, 0);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        acc[4 * kh + e] = fmaf((float)h[4 * kh + e], (float)sres[e], acc[4 * kh + e]);
+                    if (DEBUG && a.dbg_logits && row_ok) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int key = kb + 8 * qc + 4 * kh + e;
+                            if (key < k1) a.dbg_logits[((size_t)flat * a.N + key) * NB + b] = sres[e];
+                        }
+                    }
+                }
+            }
+
+            // ---- mask, online softmax in base 2
+            const bool masked = kb + KT > vis_from;
+            if (masked) {
+#pragma unroll
+                for (int r = 0; r < 8; ++r) {
+                    const int key = kb + 8 * qc + r;
+                    bool vis = key < k1;
+                    if (vis && key >= a.L) {
+                        const int u = key - a.L;
+                        vis = CAUSAL ? (u <= t) : (((mrow >> u) & 1ull) != 0ull);
+                    }
+                    if (!vis) acc[r] = -INFINITY;
+                }
+            }
+            float amax = acc[0];
+#pragma unroll
+            for (int r = 1; r < 8; ++r) amax = fmaxf(amax, acc[r]);
+            amax = fmaxf(amax, __shfl_xor(amax, 16));
+            amax = max_halves(amax);
+            const float tmax = amax == -INFINITY ? -INFINITY : amax * c_row;
+            const float m_new = tmax > m_run + kLazy ? tmax : m_run;
+            if (__any(m_new != m_run)) {
+                const float alpha = m_new != m_run ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+                l_run *= alpha;
+                if constexpr (PV16) {
+#pragma unroll
+                    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                        for (int j = 0; j < 2; ++j)
+                            oh[dt][j] = __builtin_convertvector(
+                                __builtin_convertvector(oh[dt][j], f32x2) * alpha, f16x2);
+                } else {
+#pragma unroll
+                    for (int dt = 0; dt < NDT; ++dt) oacc[dt] *= alpha;
+                }
+                m_run = m_new;
+            }
+            const float mm = m_run == -INFINITY ? 0.0f : m_run;
+            f16x8 pk;
+            float psum = 0.0f;
+            const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) {
+                const float p0 = acc[e] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(fmaf(acc[e], c_row, -mm));
+                const float p1 = acc[e + 1] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(fmaf(acc[e + 1], c_row, -mm));
+                const f16x2 h2 = __builtin_convertvector(f32x2{p0, p1}, f16x2);
+                pk[e] = h2.x;
+                pk[e + 1] = h2.y;
+                psum = __builtin_amdgcn_fdot2(h2, ones, psum, false);
+            }
+            l_run += psum;
+
+            // ---- P.V: A operand = V^T rows d = 16dt + i16, keys 8qc + [0, 8)
+            __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) {
+                const int d = 16 * dt + i16;
+                const f16x8 vop = *reinterpret_cast<const f16x8 *>(lds.vt + d * L::VTS + (d / 32) * L::VBPAD + 8 * qc);
+                if constexpr (PV16) {
+                    const f32x4 tp = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop, pk, f32x4{}, 0, 0, 0);
+                    oh[dt][0] += __builtin_convertvector(f32x2{tp[0], tp[1]}, f16x2);
+                    oh[dt][1] += __builtin_convertvector(f32x2{tp[2], tp[3]}, f16x2);
+                } else {
+                    oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop, pk, oacc[dt], 0, 0, 0);
+                }
+            }
+            __builtin_amdgcn_s_setprio(0);
+        }
+        __syncthreads();
+    }
+
+    // ---- epilogue: row sums over the four key groups of the row
+    if (!wave_active) return;
+    if constexpr (PV16) {
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+            oacc[dt] = f32x4{(float)oh[dt][0].x, (float)oh[dt][0].y, (float)oh[dt][1].x,
+                             (float)oh[dt][1].y};
+    }
+    float l_tot = l_run + __shfl_xor(l_run, 16);
+    l_tot = sum_halves(l_tot);
+    const float inv_l = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+    const float lse = l_tot > 0.0f ? (m_run + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
+    if (!row_ok) return;
+    const size_t rows_total = (size_t)a.T * a.Hq;
+    const bool partial = a.part_o != nullptr;
+    float *dst = (partial ? a.part_o + (size_t)split * rows_total * D : a.out) + (size_t)flat * D;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+        *reinterpret_cast<f32x4 *>(dst + 16 * dt + 4 * qc) = oacc[dt] * inv_l;
+    if (qc == 0) {
+        if (partial)
+            a.part_lse[(size_t)split * rows_total + flat] = lse;
+        else if (a.out_lse)
+            a.out_lse[flat] = lse;
+    }
+}
+
 // ------------------------------------------------- attention, few query rows
 //
 // For at most 16 query rows per KV head (one token, or a few tree rows): the
@@ -936,7 +1190,6 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(const AttnArgs a) {
 // formed.  The four waves of a work-group stride over the split's tiles and
 // merge their softmax states through LDS at the end.
 
-typedef int64_t i64_t;
 typedef int32_t i32x4v __attribute__((ext_vector_type(4)));
 
 constexpr int kDecWaves = 4;
@@ -1515,6 +1768,33 @@ int occupancy_d(int NW, bool causal) {
 }
 
 template <int D, bool CAUSAL, bool DEBUG, bool PV16 = false>
+hipError_t launch_s16_t(const AttnArgs &a, hipStream_t stream) {
+    hipLaunchKernelGGL((attn_split16_kernel<D, CAUSAL, DEBUG, PV16>), dim3(a.n_hs_pad * a.NRG),
+                       dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_s16_d(const AttnArgs &a, bool causal, bool debug, bool pv16, hipStream_t s) {
+    if (pv16) {
+        if (causal || debug) return hipErrorInvalidValue;
+        return launch_s16_t<D, false, false, true>(a, s);
+    }
+    if (causal) return debug ? launch_s16_t<D, true, true>(a, s) : launch_s16_t<D, true, false>(a, s);
+    return debug ? launch_s16_t<D, false, true>(a, s) : launch_s16_t<D, false, false>(a, s);
+}
+
+template <int D, bool CAUSAL>
+int occupancy_s16_t() {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &n, reinterpret_cast<const void *>(&attn_split16_kernel<D, CAUSAL, false, false>), 256,
+            0) != hipSuccess)
+        return 0;
+    return n;
+}
+
+template <int D, bool CAUSAL, bool DEBUG, bool PV16 = false>
 hipError_t launch_dec_t(const AttnArgs &a, hipStream_t stream) {
     hipLaunchKernelGGL((attn_dec_kernel<D, CAUSAL, DEBUG, PV16>), dim3(a.n_hs_pad * a.NRG),
                        dim3(kDecWaves * 64), 0, stream, a);
@@ -1542,6 +1822,25 @@ int occupancy_dec_t() {
 }
 
 }  // namespace
+
+int attention_s16_wgs_per_cu(int D, bool causal) {
+    switch (D) {
+        case 64: return causal ? occupancy_s16_t<64, true>() : occupancy_s16_t<64, false>();
+        case 128: return causal ? occupancy_s16_t<128, true>() : occupancy_s16_t<128, false>();
+        case 256: return causal ? occupancy_s16_t<256, true>() : occupancy_s16_t<256, false>();
+        default: return 0;
+    }
+}
+
+hipError_t launch_attention_s16(const AttnArgs &a, int D, bool causal, bool debug, bool pv16,
+                                hipStream_t stream) {
+    switch (D) {
+        case 64: return launch_s16_d<64>(a, causal, debug, pv16, stream);
+        case 128: return launch_s16_d<128>(a, causal, debug, pv16, stream);
+        case 256: return launch_s16_d<256>(a, causal, debug, pv16, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
 
 int attention_dec_wgs_per_cu(int D, bool causal) {
     switch (D) {

@@ -120,6 +120,12 @@ CASES = [
     ("prefill_small",   12, 2,  128,  100,  70, "prefill", 109, 0),
     ("prefill_splits",  24, 4,  256,   64,  40, "prefill", 110, 4),
     ("prefill_L0",       6, 3,   64,    0,  97, "prefill", 111, 0),
+    # 17..64 rows per KV head: the 16-row shared-tile kernel
+    ("tree8_d256_r48",  24, 4,  256, 1234,   8, "tree",  112, 0),
+    ("tree3_r18",       24, 4,  256,  500,   3, "tree",  113, 2),
+    ("tree16_r64",       8, 2,  128,  300,  16, "tree",  114, 0),
+    ("prefill_r60",     24, 4,  256,  200,  10, "prefill", 115, 3),
+    ("prefill_r36_d64",  8, 2,   64,   50,   9, "prefill", 116, 0),
 ]
 
 
