@@ -37,8 +37,9 @@ struct AttnArgs {
 // per-wave key tiles, one work-group per group of 16 rows) runs instead of
 // the 32-row tile kernel.
 constexpr int kDecMaxRows = 16;
-// Query rows per KV head up to which the 16-row shared-tile kernel runs
-// (3-bit format); above it, the 32-row tile kernel.
+// Query rows per KV head up to which the 16-row shared-tile kernel runs for
+// the 3-bit format (above the few-row kernel's range; the 4-bit format uses
+// it up to kDecMaxRows); above it, the 32-row tile kernel.
 constexpr int kS16MaxRows = 64;
 
 struct Plan {
@@ -57,7 +58,7 @@ struct Plan {
 // per-token-head scales.
 int attention_wgs_per_cu(int D, int NW, bool causal, int fmt);
 int attention_dec_wgs_per_cu(int D, bool causal);
-int attention_s16_wgs_per_cu(int D, bool causal);
+int attention_s16_wgs_per_cu(int D, bool causal, int fmt);
 
 // Resident work-group slots of the current device for a kernel variant
 // (CUs x work-groups per CU); a fixed MI355X figure when no device answers.
@@ -74,7 +75,7 @@ hipError_t launch_attention(const AttnArgs &a, int D, int NW, bool causal, bool 
 hipError_t launch_attention_dec(const AttnArgs &a, int D, bool causal, bool debug, bool pv16,
                                 hipStream_t stream);
 hipError_t launch_attention_s16(const AttnArgs &a, int D, bool causal, bool debug, bool pv16,
-                                hipStream_t stream);
+                                int fmt, hipStream_t stream);
 hipError_t launch_merge(const float *part_o, const float *part_lse, int S, int rows, int D,
                         float *out, float *out_lse, hipStream_t stream);
 hipError_t launch_kv_pack(const float *x, int n_tok, int pos0, uint32_t *codes,

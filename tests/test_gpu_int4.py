@@ -92,6 +92,8 @@ CASES = [
     ("tree_L0", 4, 2, 64, 0, 5, "tree", 205, 0),
     ("prefill_small", 12, 2, 128, 100, 70, "prefill", 206, 0),
     ("prefill_splits", 8, 1, 64, 300, 40, "prefill", 207, 4),
+    ("tree8_d256_r48", 24, 4, 256, 1500, 8, "tree", 208, 0),
+    ("prefill_r60", 24, 4, 256, 200, 10, "prefill", 209, 3),
 ]
 
 
