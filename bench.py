@@ -313,12 +313,14 @@ def summarize(wl: Workload, r, steps):
     attn = float(np.mean(r["attn_ms"]))
     merge = float(np.mean(r["merge_ms"]))
     call_us = (attn + merge) * 1e3
+    call_med_us = float(np.median(np.add(r["attn_ms"], r["merge_ms"]))) * 1e3
     mfma_s = w["qk_ops"] / (INT8_PEAK_TOPS * 1e12) + w["pv_ops"] / (FP16_PEAK_TFLOPS * 1e12)
     return {
         "ms_per_step": ms_step,
         "attn_kernel_us": attn * 1e3,
         "merge_kernel_us": merge * 1e3,
         "us_per_call": call_us,
+        "us_per_call_median": call_med_us,
         "splits": wl.S,
         "hbm_gbs": w["attn_bytes"] / (call_us * 1e-6) / 1e9,
         "hbm_frac": w["attn_bytes"] / (call_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
@@ -341,8 +343,14 @@ def cpu_baseline(wl: Workload, n_rows: int):
     oracle.attention(wl.q_host, wl.host, g.ctx_len, wl.mask, wl.scale, rows=rows)
     el = time.perf_counter() - t0
     full_s = el * total / n_rows
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": wl.work["attn_bytes"] / full_s / 1e9, "unit": "GB/s", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": model,
             "sample": f"{n_rows} of {total} query rows of {g.name} (full context), {el:.1f} s; "
                       f"scaled to the whole call: {full_s * 1e6:.0f} us"}
 
@@ -359,7 +367,7 @@ def parse_workload(name: str):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="tree64_262k")
     ap.add_argument("--extra", default="prefill_4k_32k,tree8_262k,decode_262k,decode_8k,tree64_32k,"
@@ -415,6 +423,7 @@ def main():
                    "q_heads": g.n_q_heads, "kv_heads": g.n_kv_heads, "head_dim": g.head_dim,
                    "kv_bits": 3, "splits": wl.S, "kv_buffers_rotated": N_BUFFERS},
         "us_per_verify_call": round(s["us_per_call"], 2),
+        "us_per_verify_call_median": round(s["us_per_call_median"], 2),
         "hbm_gbs_per_call": round(s["hbm_gbs"], 1),
         "hbm_frac_per_call": round(s["hbm_frac"], 4),
         "roofline": {

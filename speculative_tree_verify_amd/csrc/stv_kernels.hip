@@ -1665,6 +1665,52 @@ __device__ __forceinline__ float merge_weight(const float *part_lse, const float
     return ls == -INFINITY ? 0.0f : expf(ls - M);
 }
 
+// Few splits (S <= kMergeSmallS, D % 4 == 0): one thread per (row, 4
+// columns), several rows per work-group; each thread reads the row's S lse
+// values itself, so there is no block reduction, barrier or LDS, and many
+// rows run per CU (the chunked prefill merges ~10^5 rows over 2 splits).
+constexpr int kMergeSmallS = 8;
+constexpr int kMergeSmallThreads = 256;
+
+__global__ __launch_bounds__(kMergeSmallThreads) void merge_small_kernel(
+    const float *__restrict__ part_o, const float *__restrict__ part_lse, int S, int rows, int D,
+    float *__restrict__ out, float *__restrict__ out_lse) {
+    const int C = D / 4;
+    const int per_wg = kMergeSmallThreads / C;
+    if ((int)threadIdx.x >= per_wg * C) return;
+    const int row = blockIdx.x * per_wg + threadIdx.x / C;
+    const int c = threadIdx.x % C;
+    if (row >= rows) return;
+    float ls[kMergeSmallS];
+    float M = -INFINITY;
+#pragma unroll
+    for (int s = 0; s < kMergeSmallS; ++s) {
+        ls[s] = s < S ? part_lse[(size_t)s * rows + row] : -INFINITY;
+        M = fmaxf(M, ls[s]);
+    }
+    f32x4 *dst = reinterpret_cast<f32x4 *>(out + (size_t)row * D + 4 * c);
+    if (M == -INFINITY) {
+        *dst = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        if (out_lse && c == 0) out_lse[row] = -INFINITY;
+        return;
+    }
+    // An empty split (lse = -inf) has weight 0 and an all-zero partial.
+    float W = 0.0f;
+    f32x4 o = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int s = 0; s < kMergeSmallS; ++s) {
+        if (s < S) {
+            const f32x4 v = *reinterpret_cast<const f32x4 *>(part_o + ((size_t)s * rows + row) * D + 4 * c);
+            const float w = ls[s] == -INFINITY ? 0.0f : expf(ls[s] - M);
+            W += w;
+            o += w * v;
+        }
+    }
+    const float invW = W > 0.0f ? 1.0f / W : 0.0f;
+    *dst = o * invW;
+    if (out_lse && c == 0) out_lse[row] = M + logf(W);
+}
+
 __global__ __launch_bounds__(kMergeMaxThreads) void merge_kernel(
     const float *__restrict__ part_o, const float *__restrict__ part_lse, int S, int rows, int D,
     int G, float *__restrict__ out, float *__restrict__ out_lse) {
@@ -1956,6 +2002,13 @@ hipError_t launch_attention(const AttnArgs &a, int D, int NW, bool causal, bool 
 hipError_t launch_merge(const float *part_o, const float *part_lse, int S, int rows, int D,
                         float *out, float *out_lse, hipStream_t stream) {
     if (rows == 0) return hipSuccess;
+    if ((D & 3) == 0 && S <= kMergeSmallS && D / 4 <= kMergeSmallThreads) {
+        const int per_wg = kMergeSmallThreads / (D / 4);
+        hipLaunchKernelGGL(merge_small_kernel, dim3((rows + per_wg - 1) / per_wg),
+                           dim3(kMergeSmallThreads), 0, stream, part_o, part_lse, S, rows, D, out,
+                           out_lse);
+        return hipGetLastError();
+    }
     // Vector path: C = D / 4 columns times G split groups, about eight
     // splits per group (so many rows keep blocks small), at most 1024
     // threads.  Scalar path (D % 4 != 0): 256 threads over the columns.

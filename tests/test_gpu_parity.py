@@ -210,7 +210,8 @@ def test_determinism(gpu, orc):
 def test_split_merge_parity(gpu, orc):
     stv, torch = gpu
     rng = np.random.default_rng(150)
-    for S, rows, d in ((1, 5, 64), (7, 33, 256), (64, 3, 128), (3, 10, 200)):
+    for S, rows, d in ((1, 5, 64), (7, 33, 256), (64, 3, 128), (3, 10, 200), (2, 1001, 256),
+                       (8, 77, 128), (9, 40, 64)):
         po = rng.standard_normal((S, rows, d)).astype(np.float32)
         pl = (rng.standard_normal((S, rows)) * 5).astype(np.float32)
         pl[rng.random((S, rows)) < 0.2] = -np.inf
