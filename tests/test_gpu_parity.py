@@ -140,6 +140,8 @@ def test_parity_peaked(gpu, orc, scale_mul):
     distributions give diffuse attention, which averages errors away)."""
     run_case(gpu, orc, 24, 4, 256, 700, 16, "tree", 120, scale_mul=scale_mul)
     run_case(gpu, orc, 12, 2, 128, 90, 50, "prefill", 121, scale_mul=scale_mul)
+    run_case(gpu, orc, 24, 4, 256, 900, 8, "tree", 124, scale_mul=scale_mul)     # 48 rows per KV head
+    run_case(gpu, orc, 24, 4, 256, 1500, 1, "tree", 125, scale_mul=scale_mul)    # one token
 
 
 def test_parity_planted_keys(gpu, orc):
@@ -203,8 +205,15 @@ def test_determinism(gpu, orc):
     b = stv.verify_attention(q, kv, 5000, mask)
     c = stv.prefill_attention(q, kv, 5000)
     d2 = stv.prefill_attention(q, kv, 5000)
+    # the 16-row and the few-row kernels: 8 rows and one row of the tree
+    m8 = synth.ancestor_masks(synth.make_tree_parents(rng, 8, 8))
+    e = stv.verify_attention(q[:8].contiguous(), kv, 5000, m8)
+    f = stv.verify_attention(q[:8].contiguous(), kv, 5000, m8)
+    g1 = stv.verify_attention(q[:1].contiguous(), kv, 5000, mask[:1])
+    h1 = stv.verify_attention(q[:1].contiguous(), kv, 5000, mask[:1])
     torch.cuda.synchronize()
     assert torch.equal(a, b) and torch.equal(c, d2)
+    assert torch.equal(e, f) and torch.equal(g1, h1)
 
 
 def test_split_merge_parity(gpu, orc):
