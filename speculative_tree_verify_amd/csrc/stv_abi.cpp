@@ -148,7 +148,7 @@ int attention_common(const float *q, int T, int Hq, const stv_kv_layer *kv, int 
 
     hipStream_t st = static_cast<hipStream_t>(stream);
     const bool debug = dbg_logits || dbg_q || dbg_qscale;
-    hipError_t e = plan.dec   ? stv::launch_attention_dec(a, D, causal, debug, pv16, st)
+    hipError_t e = plan.dec   ? stv::launch_attention_dec(a, D, causal, debug, pv16, fmt, st)
                    : plan.s16 ? stv::launch_attention_s16(a, D, causal, debug, pv16, fmt, st)
                               : stv::launch_attention(a, D, plan.NW, causal, debug, fmt, pv16, st);
     if (e != hipSuccess) return fail(STV_EHIP, "attention launch failed: %s", hipGetErrorString(e));
@@ -190,7 +190,7 @@ long long attention_slots(int D, int NW, bool causal, int kind, int fmt) {
         (void)hipGetLastError();
         return kFallback;
     }
-    const int per_cu = kind == 1   ? attention_dec_wgs_per_cu(D, causal)
+    const int per_cu = kind == 1   ? attention_dec_wgs_per_cu(D, causal, fmt)
                        : kind == 2 ? attention_s16_wgs_per_cu(D, causal, fmt)
                                    : attention_wgs_per_cu(D, NW, causal, fmt);
     const long long slots = per_cu > 0 ? (long long)cus * per_cu : kFallback;
@@ -202,12 +202,11 @@ Plan make_plan(int T, int Hq, int Hkv, int D, int L, bool causal, int n_splits_r
     Plan p;
     const int G = Hq / Hkv;
     const long long R = (long long)T * G;
-    // the few-row kernel reads the 3-bit format only
-    p.dec = R <= kDecMaxRows && fmt == 0;
-    // 4-bit: the 16-row kernel for up to 16 rows (one token: measured 20% faster
-    // than the 32-row kernel with one wave); above that the 32-row kernel,
-    // which measured as fast at the 8-row tree
-    p.s16 = !p.dec && R <= (fmt == 0 ? kS16MaxRows : kDecMaxRows);
+    // up to 16 rows per KV head: the few-row kernel (both formats)
+    p.dec = R <= kDecMaxRows;
+    // 4-bit above 16 rows: the 32-row kernel, which measured as fast as the
+    // 16-row one at the 8-row tree
+    p.s16 = !p.dec && R <= kS16MaxRows && fmt == 0;
     if (p.dec) {
         p.NW = 4;
         p.NRG = (int)((R + 15) / 16);

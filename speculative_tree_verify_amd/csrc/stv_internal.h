@@ -38,8 +38,8 @@ struct AttnArgs {
 // the 32-row tile kernel.
 constexpr int kDecMaxRows = 16;
 // Query rows per KV head up to which the 16-row shared-tile kernel runs for
-// the 3-bit format (above the few-row kernel's range; the 4-bit format uses
-// it up to kDecMaxRows); above it, the 32-row tile kernel.
+// the 3-bit format (above the few-row kernel's range); above it, and for the
+// 4-bit format above the few-row kernel's range, the 32-row tile kernel.
 constexpr int kS16MaxRows = 64;
 
 struct Plan {
@@ -57,7 +57,7 @@ struct Plan {
 // fmt: 0 = 3-bit codes with per-32-element scales, 1 = 4-bit codes with
 // per-token-head scales.
 int attention_wgs_per_cu(int D, int NW, bool causal, int fmt);
-int attention_dec_wgs_per_cu(int D, bool causal);
+int attention_dec_wgs_per_cu(int D, bool causal, int fmt);
 int attention_s16_wgs_per_cu(int D, bool causal, int fmt);
 
 // Resident work-group slots of the current device for a kernel variant
@@ -73,7 +73,7 @@ Plan make_plan(int T, int Hq, int Hkv, int D, int L, bool causal, int n_splits_r
 hipError_t launch_attention(const AttnArgs &a, int D, int NW, bool causal, bool debug, int fmt,
                             bool pv16, hipStream_t stream);
 hipError_t launch_attention_dec(const AttnArgs &a, int D, bool causal, bool debug, bool pv16,
-                                hipStream_t stream);
+                                int fmt, hipStream_t stream);
 hipError_t launch_attention_s16(const AttnArgs &a, int D, bool causal, bool debug, bool pv16,
                                 int fmt, hipStream_t stream);
 hipError_t launch_merge(const float *part_o, const float *part_lse, int S, int rows, int D,

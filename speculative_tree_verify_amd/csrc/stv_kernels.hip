@@ -1254,8 +1254,13 @@ struct DecWaveLds {
     alignas(16) uint16_t svs[NB][32];
 };
 
-// PV16: the fp16-accumulated P.V variant, as in the split kernel.
-template <int D, bool CAUSAL, bool DEBUG, bool PV16>
+// PV16: the fp16-accumulated P.V variant (3-bit only), as in the split
+// kernel.  FMT 1: the 4-bit per-token-head format: the K chunks become int8
+// 16 (c - 8) in the split kernel's even/odd order (Q permuted alike), the
+// eight block MFMAs of a key half chain into one int32 sum scaled once per
+// key, V code words are expanded to fp16 c - 8 by the 0x6400 | c pattern,
+// and P times the key's V scale serves all blocks.
+template <int D, bool CAUSAL, bool DEBUG, bool PV16, int FMT>
 __global__ __launch_bounds__(kDecWaves * 64) void attn_dec_kernel(const AttnArgs a) {
     constexpr int NB = D / 32;
     constexpr int NDT = D / 16;
@@ -1340,6 +1345,17 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_dec_kernel(const AttnArgs
             }
             if (a.dbg_qscale && qc == 0) a.dbg_qscale[flat] = sq;
         }
+        if constexpr (FMT == 1) {
+            // even elements of the 8-element chunk first, as the K codes
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                const uint64_t w = (uint64_t)qop[b];
+                const uint32_t q0 = (uint32_t)w, q1 = (uint32_t)(w >> 32);
+                const uint32_t e = __builtin_amdgcn_perm(q1, q0, 0x06040200u);
+                const uint32_t o = __builtin_amdgcn_perm(q1, q0, 0x07050301u);
+                qop[b] = (i64_t)((uint64_t)e | ((uint64_t)o << 32));
+            }
+        }
     }
     const float c_row = sq * a.scale_log2;
     uint64_t mrow = 0;
@@ -1357,12 +1373,16 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_dec_kernel(const AttnArgs
     constexpr float kLazy = PV16 ? 0.0f : 8.0f;
     float m_run = -INFINITY;
     float l_run = 0.0f;
+    float lv_run = 0.0f;        // 4-bit: running sum of P times the V scale (this lane's keys)
 
     // ---- per-wave register prefetch of one tile: 4 K items, 4 V rows and
     // 4 V scales per lane
     constexpr int PER = (KT * NB) / 64;     // = D / 64
+    // 3-bit: three code words per K item and V row, a K and a V scale per
+    // item.  4-bit: four words each; one K and one V scale per key (lane % 32).
+    constexpr int KW = FMT == 1 ? 4 : 3;
     struct TileRegs {
-        uint32_t k[PER][3], v[PER][3];
+        uint32_t k[PER][KW], v[PER][KW];
         uint16_t ks[PER], vs[PER];
     };
     // Loads go through buffer descriptors whose base is the tile and whose
@@ -1377,8 +1397,36 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_dec_kernel(const AttnArgs
         const bool valid = kb < k1;
         const int kt = valid ? kb : k0;
         const int nk = valid ? min(KT, k1 - kb) : 0;
-        const int vbytes = valid ? D * 12 : 0, vsbytes = valid ? D * 2 : 0;
         const size_t grp = (size_t)head * a.ngroups + (size_t)(kt / KT);
+        if constexpr (FMT == 1) {
+            const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<uint32_t *>(a.kc + (head_k + kt) * (D / 8)), (short)0, nk * (D / 2), kBufWord3);
+            const __amdgpu_buffer_rsrc_t rks = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<uint16_t *>(a.ks + head_k + kt), (short)0, nk * 2, kBufWord3);
+            const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<uint32_t *>(a.vc + grp * D * 4), (short)0, valid ? D * 16 : 0, kBufWord3);
+            const __amdgpu_buffer_rsrc_t rvs = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<uint16_t *>(a.vs + head_k + kt), (short)0, nk * 2, kBufWord3);
+#pragma unroll
+            for (int i = 0; i < PER; ++i) {
+                // K item = (key item % 32, block item / 32): 16 bytes of the
+                // key's codes; V row d = item of the key-transposed group
+                const int item = lane + 64 * i;
+                const int key = item & 31, b = item >> 5;
+                const u32x4 kw = __builtin_amdgcn_raw_buffer_load_b128(rk, (key * (D / 8) + 4 * b) * 4, 0, 0);
+                const u32x4 vw = __builtin_amdgcn_raw_buffer_load_b128(rv, item * 16, 0, 0);
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    r.k[i][w] = kw[w];
+                    r.v[i][w] = vw[w];
+                }
+            }
+            // key lane % 32's scales (the same key for every item of a lane)
+            r.ks[0] = __builtin_amdgcn_raw_buffer_load_b16(rks, (lane & 31) * 2, 0, 0);
+            r.vs[0] = __builtin_amdgcn_raw_buffer_load_b16(rvs, (lane & 31) * 2, 0, 0);
+            return;
+        }
+        const int vbytes = valid ? D * 12 : 0, vsbytes = valid ? D * 2 : 0;
         const __amdgpu_buffer_rsrc_t rsk = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<uint32_t *>(a.kc + (head_k + kt) * NB * 3), (short)0, nk * NB * 12, kBufWord3);
         const __amdgpu_buffer_rsrc_t rss = __builtin_amdgcn_make_buffer_rsrc(
@@ -1418,6 +1466,26 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_dec_kernel(const AttnArgs
         // ---- unpack the held tile into this wave's LDS region
         const int nk = min(KT, k1 - kb);
         wave_lds_sync();
+        if constexpr (FMT == 1) {
+#pragma unroll
+            for (int i = 0; i < PER; ++i) {
+                const int item = lane + 64 * i;
+                const int key = item & 31, b = item >> 5;
+                const int d = item, dt = d >> 4;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    // K chunk j: int8 16 (c - 8) = (c ^ 8) << 4, even elements first
+                    my.kq[b][j][key][0] = ((r.k[i][j] << 4) & 0xF0F0F0F0u) ^ 0x80808080u;
+                    my.kq[b][j][key][1] = (r.k[i][j] & 0xF0F0F0F0u) ^ 0x80808080u;
+                    // V row d, keys 8j .. 8j + 7 (key 8j + e in bits 4e)
+                    my.vc[dt][j ^ (dt & 3)][d & 15][0] = r.v[i][j];
+                }
+            }
+            if (lane < KT) {
+                my.skf[0][lane] = half_bits_to_float(r.ks[0]) * 0.0625f;
+                my.svs[0][lane] = lane < nk ? r.vs[0] : (uint16_t)0;
+            }
+        } else {
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
             const int item = lane + 64 * i;
@@ -1440,6 +1508,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_dec_kernel(const AttnArgs
             }
             my.svs[b][key] = key < nk ? r.vs[i] : (uint16_t)0;
         }
+        }
         wave_lds_sync();
         // the registers are free again: fetch the tile two strides ahead
         load_tile(r, kb + 2 * stride);
@@ -1448,6 +1517,34 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_dec_kernel(const AttnArgs
         // 8qc + 4kh + [0, 4) for half kh, so its 8 logits are keys 8qc + [0, 8)
         float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
         const int krow0 = 8 * (i16 >> 2) + (i16 & 3);
+        if constexpr (FMT == 1) {
+            // the block MFMAs of each key half chain into one int32 sum
+            // (16 times the natural one; the 1/16 sits in the K scale)
+            i32x4v sacc[2] = {i32x4v{}, i32x4v{}};
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+#pragma unroll
+                for (int kh = 0; kh < 2; ++kh)
+                    sacc[kh] = __builtin_amdgcn_mfma_i32_16x16x32_i8(
+                        *reinterpret_cast<const i64_t *>(&my.kq[b][qc][krow0 + 4 * kh][0]), qop[b],
+                        sacc[kh], 0, 0, 0);
+            const f32x4 sk0 = *reinterpret_cast<const f32x4 *>(&my.skf[0][8 * qc]);
+            const f32x4 sk1 = *reinterpret_cast<const f32x4 *>(&my.skf[0][8 * qc + 4]);
+            const float skr[8] = {sk0.x, sk0.y, sk0.z, sk0.w, sk1.x, sk1.y, sk1.z, sk1.w};
+#pragma unroll
+            for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[4 * kh + e] = skr[4 * kh + e] * (float)sacc[kh][e];
+            if (DEBUG && a.dbg_logits && row_ok) {
+#pragma unroll
+                for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int key = kb + 8 * qc + 4 * kh + e;
+                        if (key < k1) a.dbg_logits[(size_t)flat * a.N + key] = sacc[kh][e] >> 4;
+                    }
+            }
+        } else {
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
             const f32x4 sk0 = *reinterpret_cast<const f32x4 *>(&my.skf[b][8 * qc]);
@@ -1469,6 +1566,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_dec_kernel(const AttnArgs
                     }
                 }
             }
+        }
         }
 
         // ---- mask, online softmax in base 2 (running max moves by > 8 only;
@@ -1496,6 +1594,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_dec_kernel(const AttnArgs
         if (__any(m_new != m_run)) {
             const float alpha = m_new != m_run ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
             l_run *= alpha;
+            lv_run *= alpha;
             if constexpr (PV16) {
 #pragma unroll
                 for (int dt = 0; dt < NDT; ++dt)
@@ -1528,6 +1627,36 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_dec_kernel(const AttnArgs
         // V^T rows d = 16dt + i16, keys 8qc + [0, 8); B operand = P times the
         // V scales of those keys in block d / 32 (keys 8qc + [0, 8), row i16).
         __builtin_amdgcn_s_setprio(1);
+        if constexpr (FMT == 1) {
+            // 4-bit: one V scale per key, so P times it serves every d-tile.
+            // The A operand holds the codes c as fp16 bit patterns, i.e. the
+            // subnormals c * 2^-24 (exact; the MFMA keeps subnormal inputs):
+            // the product is 2^-24 sum pb c, and sum pb (c - 8) = 2^24 acc -
+            // 8 sum pb, with sum pb kept per row in lv_run.
+            const u32x4 svw = *reinterpret_cast<const u32x4 *>(&my.svs[0][8 * qc]);
+            const uint32_t s01 = svw[0], s23 = svw[1], s45 = svw[2], s67 = svw[3];
+            const f16x2 p01 = f16x2{pk[0], pk[1]} * __builtin_bit_cast(f16x2, s01);
+            const f16x2 p23 = f16x2{pk[2], pk[3]} * __builtin_bit_cast(f16x2, s23);
+            const f16x2 p45 = f16x2{pk[4], pk[5]} * __builtin_bit_cast(f16x2, s45);
+            const f16x2 p67 = f16x2{pk[6], pk[7]} * __builtin_bit_cast(f16x2, s67);
+            const f16x8 pb = {p01.x, p01.y, p23.x, p23.y, p45.x, p45.y, p67.x, p67.y};
+            float lsum = __builtin_amdgcn_fdot2(p01, ones, 0.0f, false);
+            lsum = __builtin_amdgcn_fdot2(p23, ones, lsum, false);
+            lsum = __builtin_amdgcn_fdot2(p45, ones, lsum, false);
+            lv_run += __builtin_amdgcn_fdot2(p67, ones, lsum, false);
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) {
+                const uint32_t w = my.vc[dt][qc ^ (dt & 3)][i16][0];
+                const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+                // keys 2m (low nibbles) and 2m + 1 (high nibbles) as two fp16
+                const uint32_t v0 = __builtin_amdgcn_perm(hi, lo, 0x0C040C00u);
+                const uint32_t v1 = __builtin_amdgcn_perm(hi, lo, 0x0C050C01u);
+                const uint32_t v2 = __builtin_amdgcn_perm(hi, lo, 0x0C060C02u);
+                const uint32_t v3 = __builtin_amdgcn_perm(hi, lo, 0x0C070C03u);
+                const f16x8 vop = __builtin_bit_cast(f16x8, u32x4{v0, v1, v2, v3});
+                oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop, pb, oacc[dt], 0, 0, 0);
+            }
+        } else {
 #pragma unroll
         for (int bb = 0; bb < NB; ++bb) {
             // Scales of keys 8qc + [0, 8), two per word.  Each word goes
@@ -1561,6 +1690,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_dec_kernel(const AttnArgs
                 }
             }
         }
+        }
         __builtin_amdgcn_s_setprio(0);
     };
     TileRegs r0, r1;
@@ -1578,6 +1708,16 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_dec_kernel(const AttnArgs
         for (int dt = 0; dt < NDT; ++dt)
             oacc[dt] = f32x4{(float)oh[dt][0].x, (float)oh[dt][0].y, (float)oh[dt][1].x,
                              (float)oh[dt][1].y};
+    }
+    if constexpr (FMT == 1) {
+        // sum pb (c - 8) = 2^24 acc - 8 sum pb, per row
+        float lv = lv_run + __shfl_xor(lv_run, 16);
+        lv = sum_halves(lv);
+        const float corr = -8.0f * lv;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) oacc[dt][i] = fmaf(oacc[dt][i], 16777216.0f, corr);
     }
     // ---- merge the four waves' softmax states through LDS, in wave order
     float l_row = l_run + __shfl_xor(l_run, 16);
@@ -1890,29 +2030,33 @@ int occupancy_s16_t() {
     return n;
 }
 
-template <int D, bool CAUSAL, bool DEBUG, bool PV16 = false>
+template <int D, bool CAUSAL, bool DEBUG, int FMT, bool PV16 = false>
 hipError_t launch_dec_t(const AttnArgs &a, hipStream_t stream) {
-    hipLaunchKernelGGL((attn_dec_kernel<D, CAUSAL, DEBUG, PV16>), dim3(a.n_hs_pad * a.NRG),
+    hipLaunchKernelGGL((attn_dec_kernel<D, CAUSAL, DEBUG, PV16, FMT>), dim3(a.n_hs_pad * a.NRG),
                        dim3(kDecWaves * 64), 0, stream, a);
     return hipGetLastError();
 }
 
-template <int D>
+// The PV16 variant exists for the 3-bit format, verify rows, no debug output.
+template <int D, int FMT>
 hipError_t launch_dec_d(const AttnArgs &a, bool causal, bool debug, bool pv16, hipStream_t s) {
     if (pv16) {
-        if (causal || debug) return hipErrorInvalidValue;
-        return launch_dec_t<D, false, false, true>(a, s);
+        if constexpr (FMT == 0) {
+            if (!causal && !debug) return launch_dec_t<D, false, false, 0, true>(a, s);
+        }
+        return hipErrorInvalidValue;
     }
-    if (causal) return debug ? launch_dec_t<D, true, true>(a, s) : launch_dec_t<D, true, false>(a, s);
-    return debug ? launch_dec_t<D, false, true>(a, s) : launch_dec_t<D, false, false>(a, s);
+    if (causal)
+        return debug ? launch_dec_t<D, true, true, FMT>(a, s) : launch_dec_t<D, true, false, FMT>(a, s);
+    return debug ? launch_dec_t<D, false, true, FMT>(a, s) : launch_dec_t<D, false, false, FMT>(a, s);
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, int FMT>
 int occupancy_dec_t() {
     int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &n, reinterpret_cast<const void *>(&attn_dec_kernel<D, CAUSAL, false, false>), kDecWaves * 64,
-            0) != hipSuccess)
+            &n, reinterpret_cast<const void *>(&attn_dec_kernel<D, CAUSAL, false, false, FMT>),
+            kDecWaves * 64, 0) != hipSuccess)
         return 0;
     return n;
 }
@@ -1950,23 +2094,35 @@ hipError_t launch_attention_s16(const AttnArgs &a, int D, bool causal, bool debu
                     : launch_s16_f<0>(a, D, causal, debug, pv16, stream);
 }
 
-int attention_dec_wgs_per_cu(int D, bool causal) {
+template <int FMT>
+int dec_wgs_per_cu_f(int D, bool causal) {
     switch (D) {
-        case 64: return causal ? occupancy_dec_t<64, true>() : occupancy_dec_t<64, false>();
-        case 128: return causal ? occupancy_dec_t<128, true>() : occupancy_dec_t<128, false>();
-        case 256: return causal ? occupancy_dec_t<256, true>() : occupancy_dec_t<256, false>();
+        case 64: return causal ? occupancy_dec_t<64, true, FMT>() : occupancy_dec_t<64, false, FMT>();
+        case 128: return causal ? occupancy_dec_t<128, true, FMT>() : occupancy_dec_t<128, false, FMT>();
+        case 256: return causal ? occupancy_dec_t<256, true, FMT>() : occupancy_dec_t<256, false, FMT>();
         default: return 0;
     }
 }
 
-hipError_t launch_attention_dec(const AttnArgs &a, int D, bool causal, bool debug, bool pv16,
-                                hipStream_t stream) {
+int attention_dec_wgs_per_cu(int D, bool causal, int fmt) {
+    return fmt == 1 ? dec_wgs_per_cu_f<1>(D, causal) : dec_wgs_per_cu_f<0>(D, causal);
+}
+
+template <int FMT>
+hipError_t launch_dec_f(const AttnArgs &a, int D, bool causal, bool debug, bool pv16,
+                        hipStream_t stream) {
     switch (D) {
-        case 64: return launch_dec_d<64>(a, causal, debug, pv16, stream);
-        case 128: return launch_dec_d<128>(a, causal, debug, pv16, stream);
-        case 256: return launch_dec_d<256>(a, causal, debug, pv16, stream);
+        case 64: return launch_dec_d<64, FMT>(a, causal, debug, pv16, stream);
+        case 128: return launch_dec_d<128, FMT>(a, causal, debug, pv16, stream);
+        case 256: return launch_dec_d<256, FMT>(a, causal, debug, pv16, stream);
         default: return hipErrorInvalidValue;
     }
+}
+
+hipError_t launch_attention_dec(const AttnArgs &a, int D, bool causal, bool debug, bool pv16,
+                                int fmt, hipStream_t stream) {
+    return fmt == 1 ? launch_dec_f<1>(a, D, causal, debug, pv16, stream)
+                    : launch_dec_f<0>(a, D, causal, debug, pv16, stream);
 }
 
 int attention_wgs_per_cu(int D, int NW, bool causal, int fmt) {
