@@ -202,10 +202,8 @@ Plan make_plan(int T, int Hq, int Hkv, int D, int L, bool causal, int n_splits_r
     Plan p;
     const int G = Hq / Hkv;
     const long long R = (long long)T * G;
-    // up to 16 rows per KV head: the few-row kernel (both formats)
-    p.dec = R <= kDecMaxRows;
-    // 4-bit above 16 rows: the 32-row kernel, which measured as fast as the
-    // 16-row one at the 8-row tree
+    // the few-row kernel: up to 16 rows per KV head (3-bit), 64 (4-bit)
+    p.dec = R <= (fmt == 1 ? kDecMaxRows4 : kDecMaxRows);
     p.s16 = !p.dec && R <= kS16MaxRows && fmt == 0;
     if (p.dec) {
         p.NW = 4;

@@ -37,9 +37,13 @@ struct AttnArgs {
 // per-wave key tiles, one work-group per group of 16 rows) runs instead of
 // the 32-row tile kernel.
 constexpr int kDecMaxRows = 16;
+// The same for the 4-bit format, whose cheaper unpack and one-scale-per-key
+// epilogue make a separate unpack per 16-row group pay (the 8-row tree:
+// 48 rows).
+constexpr int kDecMaxRows4 = 64;
 // Query rows per KV head up to which the 16-row shared-tile kernel runs for
 // the 3-bit format (above the few-row kernel's range); above it, and for the
-// 4-bit format above the few-row kernel's range, the 32-row tile kernel.
+// 4-bit format above kDecMaxRows4, the 32-row tile kernel.
 constexpr int kS16MaxRows = 64;
 
 struct Plan {
