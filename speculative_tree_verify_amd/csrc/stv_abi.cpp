@@ -149,7 +149,7 @@ int attention_common(const float *q, int T, int Hq, const stv_kv_layer *kv, int 
     hipStream_t st = static_cast<hipStream_t>(stream);
     const bool debug = dbg_logits || dbg_q || dbg_qscale;
     hipError_t e = plan.dec   ? stv::launch_attention_dec(a, D, causal, debug, pv16, fmt, st)
-                   : plan.s16 ? stv::launch_attention_s16(a, D, causal, debug, pv16, fmt, st)
+                   : plan.s16 ? stv::launch_attention_s16(a, D, causal, debug, pv16, st)
                               : stv::launch_attention(a, D, plan.NW, causal, debug, fmt, pv16, st);
     if (e != hipSuccess) return fail(STV_EHIP, "attention launch failed: %s", hipGetErrorString(e));
     if (!partials_only && plan.S > 1) {
@@ -191,7 +191,7 @@ long long attention_slots(int D, int NW, bool causal, int kind, int fmt) {
         return kFallback;
     }
     const int per_cu = kind == 1   ? attention_dec_wgs_per_cu(D, causal, fmt)
-                       : kind == 2 ? attention_s16_wgs_per_cu(D, causal, fmt)
+                       : kind == 2 ? attention_s16_wgs_per_cu(D, causal)
                                    : attention_wgs_per_cu(D, NW, causal, fmt);
     const long long slots = per_cu > 0 ? (long long)cus * per_cu : kFallback;
     cache.push_back({dev, D, NW, causal, kind, fmt, slots});

@@ -62,7 +62,7 @@ struct Plan {
 // per-token-head scales.
 int attention_wgs_per_cu(int D, int NW, bool causal, int fmt);
 int attention_dec_wgs_per_cu(int D, bool causal, int fmt);
-int attention_s16_wgs_per_cu(int D, bool causal, int fmt);
+int attention_s16_wgs_per_cu(int D, bool causal);     // 3-bit format
 
 // Resident work-group slots of the current device for a kernel variant
 // (CUs x work-groups per CU); a fixed MI355X figure when no device answers.
@@ -79,7 +79,7 @@ hipError_t launch_attention(const AttnArgs &a, int D, int NW, bool causal, bool 
 hipError_t launch_attention_dec(const AttnArgs &a, int D, bool causal, bool debug, bool pv16,
                                 int fmt, hipStream_t stream);
 hipError_t launch_attention_s16(const AttnArgs &a, int D, bool causal, bool debug, bool pv16,
-                                int fmt, hipStream_t stream);
+                                hipStream_t stream);   // 3-bit format
 hipError_t launch_merge(const float *part_o, const float *part_lse, int S, int rows, int D,
                         float *out, float *out_lse, hipStream_t stream);
 hipError_t launch_kv_pack(const float *x, int n_tok, int pos0, uint32_t *codes,

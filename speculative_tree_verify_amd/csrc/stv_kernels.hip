@@ -936,13 +936,12 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(const AttnArgs a) {
 // block), P.V on v_mfma_f32_16x16x32_f16.  A wave holds 16 rows x D fp32
 // accumulators (64 VGPRs at D = 256, half the 32-row tile's), which with Q in
 // registers and the tile in LDS leaves room for three waves per SIMD.
-// FMT as in the split kernel (1: 4-bit per-token-head, whose eight block
-// MFMAs chain into one int32 sum per (row, key) scaled once).  PV16: the
-// fp16-accumulated P.V variant (3-bit only), as in the split kernel.
+// 3-bit format (the 4-bit format's small shapes run the few-row kernel).
+// PV16: the fp16-accumulated P.V variant, as in the split kernel.
 typedef int32_t i32x4s __attribute__((ext_vector_type(4)));
 typedef int64_t i64_t;
 
-template <int D, bool CAUSAL, bool DEBUG, bool PV16, int FMT>
+template <int D, bool CAUSAL, bool DEBUG, bool PV16>
 __global__ __launch_bounds__(256) void attn_split16_kernel(const AttnArgs a) {
     constexpr int NB = D / 32;
     constexpr int NDT = D / 16;
@@ -1029,17 +1028,6 @@ __global__ __launch_bounds__(256) void attn_split16_kernel(const AttnArgs a) {
             }
             if (a.dbg_qscale && qc == 0) a.dbg_qscale[flat] = sq;
         }
-        if constexpr (FMT == 1) {
-            // even elements of the 8-element group first, as the K codes
-#pragma unroll
-            for (int b = 0; b < NB; ++b) {
-                const uint64_t w = (uint64_t)qop[b];
-                const uint32_t q0 = (uint32_t)w, q1 = (uint32_t)(w >> 32);
-                const uint32_t e = __builtin_amdgcn_perm(q1, q0, 0x06040200u);
-                const uint32_t o = __builtin_amdgcn_perm(q1, q0, 0x07050301u);
-                qop[b] = (i64_t)((uint64_t)e | ((uint64_t)o << 32));
-            }
-        }
     }
     const float c_row = sq * a.scale_log2;
     uint64_t mrow = 0;
@@ -1065,7 +1053,7 @@ __global__ __launch_bounds__(256) void attn_split16_kernel(const AttnArgs a) {
     float m_run = -INFINITY;
     float l_run = 0.0f;
 
-    TileIoOf<D, NT, FMT> io;
+    TileIo<D, NT> io;
     io.load(a, head, k0, k0, k1, tid);
     for (int kb = k0; kb < k1; kb += KT) {
         io.store(lds, tid, min(KT, k1 - kb));
@@ -1074,51 +1062,22 @@ __global__ __launch_bounds__(256) void attn_split16_kernel(const AttnArgs a) {
 
         if (wave_active) {
             float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-            if constexpr (FMT == 1) {
-                // ---- 4-bit: the block MFMAs of each key half chain into one
-                // int32 sum per (row, key) (16 times the natural sum)
-                i32x4s sacc[2] = {i32x4s{}, i32x4s{}};
+            // ---- Q.K^T, one int8 MFMA per (block, key half), fp32 epilogue
 #pragma unroll
-                for (int b = 0; b < NB; ++b)
+            for (int b = 0; b < NB; ++b) {
+                const f16x8 h = *reinterpret_cast<const f16x8 *>(lds.skh + b * KT + 8 * qc);
 #pragma unroll
-                    for (int kh = 0; kh < 2; ++kh)
-                        sacc[kh] = __builtin_amdgcn_mfma_i32_16x16x32_i8(
-                            *reinterpret_cast<const i64_t *>(kq_lane + 4 * kh * L::KQS + 32 * b), qop[b],
-                            sacc[kh], 0, 0, 0);
-                const f32x4 s0 = *reinterpret_cast<const f32x4 *>(lds.skf + 8 * qc);
-                const f32x4 s1 = *reinterpret_cast<const f32x4 *>(lds.skf + 8 * qc + 4);
-                const float skr[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+                for (int kh = 0; kh < 2; ++kh) {
+                    const i64_t kop = *reinterpret_cast<const i64_t *>(kq_lane + 4 * kh * L::KQS + 32 * b);
+                    const i32x4s sres = __builtin_amdgcn_mfma_i32_16x16x32_i8(kop, qop[b], i32x4s{}, 0, 0, 0);
 #pragma unroll
-                for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) acc[4 * kh + e] = skr[4 * kh + e] * (float)sacc[kh][e];
-                if (DEBUG && a.dbg_logits && row_ok) {
-#pragma unroll
-                    for (int kh = 0; kh < 2; ++kh)
+                    for (int e = 0; e < 4; ++e)
+                        acc[4 * kh + e] = fmaf((float)h[4 * kh + e], (float)sres[e], acc[4 * kh + e]);
+                    if (DEBUG && a.dbg_logits && row_ok) {
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
                             const int key = kb + 8 * qc + 4 * kh + e;
-                            if (key < k1) a.dbg_logits[(size_t)flat * a.N + key] = sacc[kh][e] >> 4;
-                        }
-                }
-            } else {
-                // ---- Q.K^T, one int8 MFMA per (block, key half), fp32 epilogue
-#pragma unroll
-                for (int b = 0; b < NB; ++b) {
-                    const f16x8 h = *reinterpret_cast<const f16x8 *>(lds.skh + b * KT + 8 * qc);
-#pragma unroll
-                    for (int kh = 0; kh < 2; ++kh) {
-                        const i64_t kop = *reinterpret_cast<const i64_t *>(kq_lane + 4 * kh * L::KQS + 32 * b);
-                        const i32x4s sres = __builtin_amdgcn_mfma_i32_16x16x32_i8(kop, qop[b], i32x4s{}, 0, 0, 0);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            acc[4 * kh + e] = fmaf((float)h[4 * kh + e], (float)sres[e], acc[4 * kh + e]);
-                        if (DEBUG && a.dbg_logits && row_ok) {
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) {
-                                const int key = kb + 8 * qc + 4 * kh + e;
-                                if (key < k1) a.dbg_logits[((size_t)flat * a.N + key) * NB + b] = sres[e];
-                            }
+                            if (key < k1) a.dbg_logits[((size_t)flat * a.N + key) * NB + b] = sres[e];
                         }
                     }
                 }
@@ -1999,33 +1958,30 @@ int occupancy_d(int NW, bool causal) {
     }
 }
 
-template <int D, bool CAUSAL, bool DEBUG, int FMT, bool PV16 = false>
+template <int D, bool CAUSAL, bool DEBUG, bool PV16 = false>
 hipError_t launch_s16_t(const AttnArgs &a, hipStream_t stream) {
-    hipLaunchKernelGGL((attn_split16_kernel<D, CAUSAL, DEBUG, PV16, FMT>), dim3(a.n_hs_pad * a.NRG),
+    hipLaunchKernelGGL((attn_split16_kernel<D, CAUSAL, DEBUG, PV16>), dim3(a.n_hs_pad * a.NRG),
                        dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 
-// The PV16 variant exists for the 3-bit format, verify rows, no debug output.
-template <int D, int FMT>
+// The PV16 variant: verify rows, no debug output.
+template <int D>
 hipError_t launch_s16_d(const AttnArgs &a, bool causal, bool debug, bool pv16, hipStream_t s) {
     if (pv16) {
-        if constexpr (FMT == 0) {
-            if (!causal && !debug) return launch_s16_t<D, false, false, 0, true>(a, s);
-        }
-        return hipErrorInvalidValue;
+        if (causal || debug) return hipErrorInvalidValue;
+        return launch_s16_t<D, false, false, true>(a, s);
     }
-    if (causal)
-        return debug ? launch_s16_t<D, true, true, FMT>(a, s) : launch_s16_t<D, true, false, FMT>(a, s);
-    return debug ? launch_s16_t<D, false, true, FMT>(a, s) : launch_s16_t<D, false, false, FMT>(a, s);
+    if (causal) return debug ? launch_s16_t<D, true, true>(a, s) : launch_s16_t<D, true, false>(a, s);
+    return debug ? launch_s16_t<D, false, true>(a, s) : launch_s16_t<D, false, false>(a, s);
 }
 
-template <int D, bool CAUSAL, int FMT>
+template <int D, bool CAUSAL>
 int occupancy_s16_t() {
     int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &n, reinterpret_cast<const void *>(&attn_split16_kernel<D, CAUSAL, false, false, FMT>),
-            256, 0) != hipSuccess)
+            &n, reinterpret_cast<const void *>(&attn_split16_kernel<D, CAUSAL, false, false>), 256,
+            0) != hipSuccess)
         return 0;
     return n;
 }
@@ -2063,35 +2019,23 @@ int occupancy_dec_t() {
 
 }  // namespace
 
-template <int FMT>
-int s16_wgs_per_cu_f(int D, bool causal) {
+int attention_s16_wgs_per_cu(int D, bool causal) {
     switch (D) {
-        case 64: return causal ? occupancy_s16_t<64, true, FMT>() : occupancy_s16_t<64, false, FMT>();
-        case 128: return causal ? occupancy_s16_t<128, true, FMT>() : occupancy_s16_t<128, false, FMT>();
-        case 256: return causal ? occupancy_s16_t<256, true, FMT>() : occupancy_s16_t<256, false, FMT>();
+        case 64: return causal ? occupancy_s16_t<64, true>() : occupancy_s16_t<64, false>();
+        case 128: return causal ? occupancy_s16_t<128, true>() : occupancy_s16_t<128, false>();
+        case 256: return causal ? occupancy_s16_t<256, true>() : occupancy_s16_t<256, false>();
         default: return 0;
     }
 }
 
-int attention_s16_wgs_per_cu(int D, bool causal, int fmt) {
-    return fmt == 1 ? s16_wgs_per_cu_f<1>(D, causal) : s16_wgs_per_cu_f<0>(D, causal);
-}
-
-template <int FMT>
-hipError_t launch_s16_f(const AttnArgs &a, int D, bool causal, bool debug, bool pv16,
-                        hipStream_t stream) {
+hipError_t launch_attention_s16(const AttnArgs &a, int D, bool causal, bool debug, bool pv16,
+                                hipStream_t stream) {
     switch (D) {
-        case 64: return launch_s16_d<64, FMT>(a, causal, debug, pv16, stream);
-        case 128: return launch_s16_d<128, FMT>(a, causal, debug, pv16, stream);
-        case 256: return launch_s16_d<256, FMT>(a, causal, debug, pv16, stream);
+        case 64: return launch_s16_d<64>(a, causal, debug, pv16, stream);
+        case 128: return launch_s16_d<128>(a, causal, debug, pv16, stream);
+        case 256: return launch_s16_d<256>(a, causal, debug, pv16, stream);
         default: return hipErrorInvalidValue;
     }
-}
-
-hipError_t launch_attention_s16(const AttnArgs &a, int D, bool causal, bool debug, bool pv16,
-                                int fmt, hipStream_t stream) {
-    return fmt == 1 ? launch_s16_f<1>(a, D, causal, debug, pv16, stream)
-                    : launch_s16_f<0>(a, D, causal, debug, pv16, stream);
 }
 
 template <int FMT>
