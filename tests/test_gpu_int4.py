@@ -36,7 +36,8 @@ def _visible(T, L, mask, n):
     return vis
 
 
-def run4(gpu, orc, hq, hkv, d, L, T, kind, seed, n_splits=0, rows=None, check_logits=True):
+def run4(gpu, orc, hq, hkv, d, L, T, kind, seed, n_splits=0, rows=None, check_logits=True,
+         scale_mul=1.0):
     stv, torch = gpu
     rng = np.random.default_rng(seed)
     host = synth.make_kv4(rng, hkv, d, L + T, L + T + 3)
@@ -46,7 +47,7 @@ def run4(gpu, orc, hq, hkv, d, L, T, kind, seed, n_splits=0, rows=None, check_lo
         mask = synth.ancestor_masks(synth.chain_parents(T))
     elif kind == "tree":
         mask = synth.ancestor_masks(synth.make_tree_parents(rng, T, 8))
-    scale = 1.0 / math.sqrt(d)
+    scale = scale_mul / math.sqrt(d)
     ref = orc.attention(q, host, L, mask, scale, rows=rows, want_logits=check_logits)
     kv = stv.KVCache.from_host(host)
     qd = torch.from_numpy(q).cuda()
@@ -105,6 +106,23 @@ def test_parity_int4(gpu, orc, name, hq, hkv, d, L, T, kind, seed, ns):
 def test_full_size_tree_sampled_rows(gpu, orc):
     rows = np.linspace(0, 64 * 24 - 1, 24).round().astype(np.int32)
     run4(gpu, orc, 24, 4, 256, 65536, 64, "tree", 208, rows=rows, check_logits=False)
+
+
+@pytest.mark.parametrize("T,n_rows", [(1, 24), (8, 12)], ids=["one_token", "tree8"])
+def test_full_size_262k_sampled_rows(gpu, orc, T, n_rows):
+    """One token and the 8-row tree over 262,144 keys (the few-row kernel,
+    in the split plan the benchmark times)."""
+    rows = np.linspace(0, T * 24 - 1, n_rows).round().astype(np.int32)
+    run4(gpu, orc, 24, 4, 256, 262144 - T, T, "tree", 210 + T, rows=rows, check_logits=False)
+
+
+@pytest.mark.parametrize("scale_mul", [8.0, 32.0])
+def test_parity_int4_peaked(gpu, orc, scale_mul):
+    """Nearly one-hot softmax: the running max moves often, which rescales
+    the few-row kernel's per-row V-scale sums with the accumulators."""
+    run4(gpu, orc, 24, 4, 256, 1500, 1, "tree", 212, scale_mul=scale_mul)
+    run4(gpu, orc, 24, 4, 256, 900, 8, "tree", 213, scale_mul=scale_mul)
+    run4(gpu, orc, 24, 4, 256, 700, 16, "tree", 214, scale_mul=scale_mul)
 
 
 @pytest.mark.parametrize("d,pos0,n_tok", [(64, 0, 1), (128, 29, 8), (256, 61, 64), (256, 0, 100)])
