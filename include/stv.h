@@ -177,6 +177,8 @@ int stv_attention_plan(int32_t T, int32_t n_q_heads, int32_t n_kv_heads, int32_t
  *               format); entries of keys a row cannot see are unspecified
  *   dbg_q       nullable int8 [T][n_q_heads][head_dim]: the quantized Q
  *   dbg_qscale  nullable fp32 [T][n_q_heads]: the Q scales
+ * q, out and workspace must be 16-byte aligned (the kernels move them in
+ * 16-byte vectors).
  * Per-row Q quantizer: amax = max|q|; inv = 127 / amax (correctly rounded);
  * q8 = clamp(rint(q * inv), -127, 127); sq = amax / 127; a zero row gives
  * sq = 0 and zero codes.  Logit of key j: softmax_scale * sq *
@@ -231,7 +233,8 @@ int stv_prefill_attention(const float *q, int32_t T, int32_t n_q_heads,
  *               stv_verify_attention / stv_prefill_attention
  *   anc_mask    [host] uint64 [T] tree masks (as for verify), or NULL for
  *               the causal chunk rule of prefill
- *   part_o      fp32 [S][T][n_q_heads][head_dim], S from stv_attention_plan
+ *   part_o      fp32 [S][T][n_q_heads][head_dim], S from stv_attention_plan;
+ *               16-byte aligned, as are q
  *   part_lse    fp32 [S][T][n_q_heads], natural log; -inf where a split saw
  *               no key of that row (its part_o row is then zero)
  * Split s covers keys [s*P, min(ctx_len+T, (s+1)*P)) with
@@ -253,7 +256,9 @@ int stv_attention_partials(const float *q, int32_t T, int32_t n_q_heads,
  *             LSE = log sum_s exp(lse_s); rows whose splits are all -inf
  *             get zeros
  *   out_lse   nullable fp32 [rows], receives LSE
- * Splits are summed in order s = 0 .. S-1.  D: 1 .. 1024.
+ * The summation order depends only on S and D (no atomics), so results are
+ * reproducible bit for bit.  D: 1 .. 1024; part_o and out 16-byte aligned
+ * when D is a multiple of 4.
  * Errors: STV_EINVAL, STV_EHIP.
  */
 int stv_split_merge(const float *part_o, const float *part_lse, int32_t S, int32_t rows,

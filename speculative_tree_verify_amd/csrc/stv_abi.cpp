@@ -86,6 +86,10 @@ int attention_common(const float *q, int T, int Hq, const stv_kv_layer *kv, int 
     const bool partials_only = partials_o != nullptr;
     if (!q || (!out && !partials_only)) return fail(STV_EINVAL, "q and out must not be NULL");
     if (partials_only && !partials_lse) return fail(STV_EINVAL, "part_lse must not be NULL");
+    // the kernels move q, out and the partials in 16-byte vectors
+    if (((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(out) |
+          reinterpret_cast<uintptr_t>(partials_o) | reinterpret_cast<uintptr_t>(ws)) & 15u) != 0)
+        return fail(STV_EINVAL, "q, out, workspace and part_o must be 16-byte aligned");
     if (T < 1) return fail(STV_EINVAL, "T must be >= 1 (got %d)", T);
     if (!causal && T > STV_MAX_TREE_ROWS) return fail(STV_EINVAL, "verify supports at most 64 tree rows (got %d)", T);
     if ((long long)T * Hq >= (1ll << 31)) return fail(STV_EINVAL, "T * n_q_heads too large");
@@ -360,6 +364,9 @@ int stv_split_merge(const float *part_o, const float *part_lse, int32_t S, int32
     if (D < 1 || D > 1024) return fail(STV_EINVAL, "D must be in 1..1024");
     if (rows == 0) return ok();
     if (!part_o || !part_lse || !out) return fail(STV_EINVAL, "part_o, part_lse and out must not be NULL");
+    if ((D & 3) == 0 &&
+        ((reinterpret_cast<uintptr_t>(part_o) | reinterpret_cast<uintptr_t>(out)) & 15u) != 0)
+        return fail(STV_EINVAL, "part_o and out must be 16-byte aligned when D %% 4 == 0");
     hipError_t e = stv::launch_merge(part_o, part_lse, S, rows, D, out, out_lse,
                                      static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(STV_EHIP, "merge launch failed: %s", hipGetErrorString(e));

@@ -119,6 +119,23 @@ def test_format_errors(lib, stvmod):
     assert "kv_format" in _err(lib)
 
 
+def test_alignment_errors(lib, stvmod):
+    """q, out, the workspace and the partials move in 16-byte vectors."""
+    E = stvmod
+    assert _verify(lib, stvmod, q=FAKE + 4) == E.STV_EINVAL
+    assert "aligned" in _err(lib)
+    assert _verify(lib, stvmod, out=FAKE + 8) == E.STV_EINVAL
+    assert _verify(lib, stvmod, ws=FAKE + 12, ws_bytes=1 << 30) == E.STV_EINVAL
+    m = np.ascontiguousarray(synth.ancestor_masks(synth.chain_parents(8)))
+    layer = _layer(stvmod)
+    assert lib.stv_attention_partials(FAKE, 8, 24, ctypes.byref(layer), 100, m.ctypes.data,
+                                      0.0625, 2, FAKE + 4, FAKE, None) == E.STV_EINVAL
+    f = lib.stv_split_merge
+    assert f(FAKE + 4, FAKE, 2, 10, 64, FAKE, None, None) == E.STV_EINVAL
+    assert f(FAKE, FAKE, 2, 10, 64, FAKE + 4, None, None) == E.STV_EINVAL
+    assert "aligned" in _err(lib)
+
+
 def test_fp16acc_errors(lib, stvmod):
     """The fp16-accumulated variant checks what verify checks, and reads the
     3-bit format only."""
