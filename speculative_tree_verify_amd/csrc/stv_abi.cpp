@@ -76,8 +76,8 @@ int check_kv(const stv_kv_layer *kv, int Hq, int L, int T) {
     return STV_OK;
 }
 
-// With partials_o set, only the split kernel runs and every split (even when
-// S == 1) writes its partial to partials_o / partials_lse.
+// With partials_o set, every split (even when S == 1) writes its partial to
+// partials_o / partials_lse and no merge runs.
 int attention_common(const float *q, int T, int Hq, const stv_kv_layer *kv, int L,
                      const uint64_t *mask, bool causal, float scale, float *out, float *out_lse,
                      void *ws, size_t ws_bytes, int n_splits, int32_t *dbg_logits, int8_t *dbg_q,

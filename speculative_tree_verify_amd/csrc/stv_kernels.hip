@@ -3,9 +3,9 @@
 // fp16-in / fp32-accumulate MFMA P.V stage, and the log-sum-exp merge of
 // split partials.  Three attention kernels share that scheme:
 // attn_split_kernel (32-row tiles, more than 64 rows per KV head: the 64-node
-// tree, the prefill chunk), attn_split16_kernel (16-row tiles, 17..64 rows:
-// the 8-row tree) and attn_dec_kernel (at most 16 rows, one token; per-wave
-// tiles without work-group barriers).
+// tree, the prefill chunk), attn_split16_kernel (16-row tiles, 17..64 rows,
+// 3-bit: the 8-row tree) and attn_dec_kernel (at most 16 rows, one token; up to
+// 64 rows for the 4-bit format; per-wave tiles without work-group barriers).
 //
 // Method (elpis, "Why fast": decode-verify and prefill int8 Q.K^T with the
 // 3-bit K codes widened to exact int8, the double-buffered K/V ring, the

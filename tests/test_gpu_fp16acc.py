@@ -99,9 +99,9 @@ CASES = [
     # name, hq, hkv, d, L, T, seed, n_splits
     ("dec_one_token", 24, 4, 256, 4000, 1, 300, 0),         # few-row kernel
     ("dec_one_token_d64", 4, 1, 64, 777, 1, 301, 3),
-    ("tree8", 24, 4, 256, 5000, 8, 302, 0),                  # split kernel, 2 waves
+    ("tree8", 24, 4, 256, 5000, 8, 302, 0),                  # 16-row kernel
     ("tree8_d128_one_split", 8, 2, 128, 1500, 8, 303, 1),
-    ("tree64", 24, 4, 256, 3000, 64, 304, 0),                # split kernel, 4 waves
+    ("tree64", 24, 4, 256, 3000, 64, 304, 0),                # 32-row split kernel
     ("tree3_ragged", 6, 2, 64, 45, 3, 305, 2),
 ]
 
