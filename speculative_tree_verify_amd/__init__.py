@@ -1,4 +1,5 @@
-"""Speculative tree-verify attention over a 3-bit KV cache, for MI355X.
+"""Speculative tree-verify attention over a quantized KV cache (3-bit blocks
+or 4-bit per token-head), for MI355X.
 
 Thin ctypes binding of ``libstv.so`` (hand-written HIP kernels for gfx950
 behind the C ABI declared in ``include/stv.h``).  This module only checks and
@@ -28,8 +29,10 @@ STV_EHIP = -5
 
 __all__ = [
     "StvError", "KVCache", "load_library", "kv_quant_pack", "attention_plan",
-    "verify_attention", "prefill_attention", "attention_partials", "split_merge",
-    "STV_OK", "STV_EINVAL", "STV_EMASK", "STV_ECAPACITY", "STV_EWORKSPACE", "STV_EHIP",
+    "verify_attention", "verify_attention_fp16acc", "prefill_attention",
+    "attention_partials", "split_merge", "tree_accept", "kv_commit", "lookup_plan",
+    "lookup_draft", "STV_OK", "STV_EINVAL", "STV_EMASK", "STV_ECAPACITY", "STV_EWORKSPACE",
+    "STV_EHIP", "STV_KV_3BIT", "STV_KV_4BIT_TOKEN",
 ]
 
 
