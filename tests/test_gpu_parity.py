@@ -216,6 +216,27 @@ def test_determinism(gpu, orc):
     assert torch.equal(e, f) and torch.equal(g1, h1)
 
 
+def test_determinism_rows_1_to_8(gpu, orc):
+    """Tree row counts 1..8 (the few-row and 16-row kernels), each call
+    repeated: bitwise-identical outputs and lse."""
+    stv, torch = gpu
+    rng = np.random.default_rng(141)
+    host = synth.make_kv(rng, 4, 256, 7000 + 8, 7000 + 8)
+    kv = stv.KVCache.from_host(host)
+    for T in range(1, 9):
+        q = torch.from_numpy(synth.make_q(rng, T, 24, 256)).cuda()
+        mask = synth.ancestor_masks(synth.make_tree_parents(rng, T, 8) if T > 1
+                                    else synth.chain_parents(1))
+        outs = []
+        for _ in range(3):
+            lse = torch.empty((T, 24), dtype=torch.float32, device="cuda")
+            o = stv.verify_attention(q, kv, 7000, mask, out_lse=lse)
+            outs.append((o, lse))
+        torch.cuda.synchronize()
+        for o, lse in outs[1:]:
+            assert torch.equal(o, outs[0][0]) and torch.equal(lse, outs[0][1]), T
+
+
 def test_split_merge_parity(gpu, orc):
     stv, torch = gpu
     rng = np.random.default_rng(150)
