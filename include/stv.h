@@ -106,7 +106,7 @@ typedef struct stv_kv_layer {
 /* Description of the last failure on the calling thread ("" after success). */
 const char *stv_last_error(void);
 
-/* ABI version; bumped on any change of the interface.  Currently 3. */
+/* ABI version; bumped on any change of the interface.  Currently 4. */
 int32_t stv_abi_version(void);
 
 /*
@@ -245,6 +245,30 @@ int stv_attention_partials(const float *q, int32_t T, int32_t n_q_heads,
                            const stv_kv_layer *kv, int32_t ctx_len, const uint64_t *anc_mask,
                            float softmax_scale, int32_t n_splits, float *part_o,
                            float *part_lse, void *stream);
+
+/*
+ * stv_context_plan / stv_context_partials -- the split phase over a slice of
+ * the context with no tree keys: every one of the T rows sees keys
+ * 0 .. n_keys-1 of kv (elpis-lossless, "Trust base": split-K over the
+ * context; the partials of a context range held elsewhere, e.g. on another
+ * device, joined by stv_split_merge with those of the slice that holds the
+ * tree keys, which stv_attention_partials computes).
+ *   q, T (1 .. 64), n_q_heads, softmax_scale, n_splits: as for
+ *               stv_attention_partials
+ *   n_keys      keys of the slice (>= 1, at most the cache capacity)
+ *   part_o, part_lse  as for stv_attention_partials, S from stv_context_plan;
+ *               split s covers keys [s*P, min(n_keys, (s+1)*P)) with
+ *               P = 32 * ceil(ceil(n_keys/32) / S)
+ * A slice whose length is a multiple of 32 gives, split for split, the same
+ * partials bit for bit as the matching splits of one call over the whole
+ * context.  Errors: STV_EINVAL, STV_ECAPACITY, STV_EHIP.
+ */
+int stv_context_plan(int32_t T, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                     int32_t n_keys, int32_t kv_format, int32_t n_splits_req,
+                     int32_t *n_splits_out, size_t *workspace_bytes_out);
+int stv_context_partials(const float *q, int32_t T, int32_t n_q_heads, const stv_kv_layer *kv,
+                         int32_t n_keys, float softmax_scale, int32_t n_splits, float *part_o,
+                         float *part_lse, void *stream);
 
 /*
  * stv_split_merge -- join split partials with a log-sum-exp merge

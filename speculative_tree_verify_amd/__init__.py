@@ -30,7 +30,7 @@ STV_EHIP = -5
 __all__ = [
     "StvError", "KVCache", "load_library", "kv_quant_pack", "attention_plan",
     "verify_attention", "verify_attention_fp16acc", "prefill_attention",
-    "attention_partials", "split_merge", "tree_accept", "kv_commit", "lookup_plan",
+    "attention_partials", "context_plan", "context_partials", "split_merge", "tree_accept", "kv_commit", "lookup_plan",
     "lookup_draft", "STV_OK", "STV_EINVAL", "STV_EMASK", "STV_ECAPACITY", "STV_EWORKSPACE",
     "STV_EHIP", "STV_KV_3BIT", "STV_KV_4BIT_TOKEN",
 ]
@@ -83,6 +83,12 @@ def load_library():
         lib.stv_verify_attention_fp16acc.argtypes = [P, i32, i32, ctypes.POINTER(_KVLayer), i32,
                                                      P, ctypes.c_float, P, P, P, ctypes.c_size_t,
                                                      i32, P]
+        lib.stv_context_plan.restype = ctypes.c_int
+        lib.stv_context_plan.argtypes = [i32, i32, i32, i32, i32, i32, i32,
+                                         ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_size_t)]
+        lib.stv_context_partials.restype = ctypes.c_int
+        lib.stv_context_partials.argtypes = [P, i32, i32, ctypes.POINTER(_KVLayer), i32,
+                                             ctypes.c_float, i32, P, P, P]
         lib.stv_prefill_attention.restype = ctypes.c_int
         lib.stv_prefill_attention.argtypes = [P, i32, i32, ctypes.POINTER(_KVLayer), i32,
                                               ctypes.c_float, P, P, P, ctypes.c_size_t, i32,
@@ -349,6 +355,39 @@ def attention_partials(q, kv: KVCache, ctx_len: int, anc_mask=None, softmax_scal
     rc = load_library().stv_attention_partials(
         _dev_ptr(q, torch.float32, "q"), T, hq, ctypes.byref(layer), ctx_len, m_ptr,
         float(softmax_scale), n_splits, _dev_ptr(part_o, torch.float32, "part_o", (S, T, hq, d)),
+        _dev_ptr(part_lse, torch.float32, "part_lse", (S, T, hq)), _stream(q.device))
+    _check(rc)
+    return part_o, part_lse
+
+
+def context_plan(T: int, n_q_heads: int, n_kv_heads: int, head_dim: int, n_keys: int,
+                 n_splits: int = 0, fmt: str = "b3") -> tuple[int, int]:
+    """(split count, workspace bytes) of a context-slice call (no tree keys)."""
+    s = ctypes.c_int32()
+    ws = ctypes.c_size_t()
+    _check(load_library().stv_context_plan(T, n_q_heads, n_kv_heads, head_dim, n_keys,
+                                           _FORMATS[fmt], n_splits, ctypes.byref(s),
+                                           ctypes.byref(ws)))
+    return int(s.value), int(ws.value)
+
+
+def context_partials(q, kv: KVCache, n_keys: int, softmax_scale=None, n_splits: int = 0,
+                     part_o=None, part_lse=None):
+    """Split phase over keys 0 .. n_keys-1 of kv for all T rows (a context
+    slice without tree keys): returns (part_o [S][T][Hq][D], part_lse [S][T][Hq])."""
+    torch = _torch()
+    T, hq, d = q.shape
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d)
+    S, _ = context_plan(T, hq, kv.n_kv_heads, d, n_keys, n_splits, kv.fmt)
+    if part_o is None:
+        part_o = torch.empty((S, T, hq, d), dtype=torch.float32, device=q.device)
+    if part_lse is None:
+        part_lse = torch.empty((S, T, hq), dtype=torch.float32, device=q.device)
+    layer = kv._layer()
+    rc = load_library().stv_context_partials(
+        _dev_ptr(q, torch.float32, "q"), T, hq, ctypes.byref(layer), n_keys, float(softmax_scale),
+        n_splits, _dev_ptr(part_o, torch.float32, "part_o", (S, T, hq, d)),
         _dev_ptr(part_lse, torch.float32, "part_lse", (S, T, hq)), _stream(q.device))
     _check(rc)
     return part_o, part_lse

@@ -14,6 +14,12 @@
 #include "stv_lookup.h"
 #include "stv_internal.h"
 
+namespace stv {
+// the split plan for L context keys followed by n_after more (defined below)
+Plan make_plan_keys(int T, int Hq, int Hkv, int D, int L, bool causal, int n_splits_req, int fmt,
+                    int n_after);
+}  // namespace stv
+
 namespace {
 
 thread_local char g_err[512] = "";
@@ -77,12 +83,13 @@ int check_kv(const stv_kv_layer *kv, int Hq, int L, int T) {
 }
 
 // With partials_o set, every split (even when S == 1) writes its partial to
-// partials_o / partials_lse and no merge runs.
+// partials_o / partials_lse and no merge runs.  ctx_only: the T rows see
+// keys 0 .. L-1 only (a context slice without tree keys; no mask).
 int attention_common(const float *q, int T, int Hq, const stv_kv_layer *kv, int L,
                      const uint64_t *mask, bool causal, float scale, float *out, float *out_lse,
                      void *ws, size_t ws_bytes, int n_splits, int32_t *dbg_logits, int8_t *dbg_q,
                      float *dbg_qscale, void *stream, float *partials_o = nullptr,
-                     float *partials_lse = nullptr, bool pv16 = false) {
+                     float *partials_lse = nullptr, bool pv16 = false, bool ctx_only = false) {
     const bool partials_only = partials_o != nullptr;
     if (!q || (!out && !partials_only)) return fail(STV_EINVAL, "q and out must not be NULL");
     if (partials_only && !partials_lse) return fail(STV_EINVAL, "part_lse must not be NULL");
@@ -95,9 +102,10 @@ int attention_common(const float *q, int T, int Hq, const stv_kv_layer *kv, int 
     if ((long long)T * Hq >= (1ll << 31)) return fail(STV_EINVAL, "T * n_q_heads too large");
     if (n_splits < 0) return fail(STV_EINVAL, "n_splits must be >= 0");
     if (!(scale > 0.0f) || !isfinite(scale)) return fail(STV_EINVAL, "softmax_scale must be positive and finite");
-    int rc = check_kv(kv, Hq, L, T);
+    if (ctx_only && L < 1) return fail(STV_EINVAL, "n_keys must be >= 1");
+    int rc = check_kv(kv, Hq, L, ctx_only ? 0 : T);
     if (rc) return rc;
-    if (!causal) {
+    if (!causal && !ctx_only) {
         if (!mask) return fail(STV_EINVAL, "anc_mask must not be NULL");
         rc = check_mask(mask, T);
         if (rc) return rc;
@@ -108,7 +116,8 @@ int attention_common(const float *q, int T, int Hq, const stv_kv_layer *kv, int 
     const int fmt = kv->kv_format;
     if (pv16 && fmt != STV_KV_3BIT)
         return fail(STV_EINVAL, "fp16-accumulated P.V reads the 3-bit format only");
-    const stv::Plan plan = stv::make_plan(T, Hq, Hkv, D, L, causal, n_splits, fmt);
+    const stv::Plan plan =
+        stv::make_plan_keys(T, Hq, Hkv, D, L, causal, n_splits, fmt, ctx_only ? 0 : T);
     if (!partials_only && plan.S > 1 && (!ws || ws_bytes < plan.ws_bytes))
         return fail(STV_EWORKSPACE, "workspace of %zu bytes needed for %d splits (got %zu)",
                     plan.ws_bytes, plan.S, ws ? ws_bytes : (size_t)0);
@@ -140,14 +149,14 @@ int attention_common(const float *q, int T, int Hq, const stv_kv_layer *kv, int 
     a.cap = kv->capacity;
     a.ngroups = (kv->capacity + kKeyTileC - 1) / kKeyTileC;
     a.L = L;
-    a.N = L + T;
+    a.N = ctx_only ? L : L + T;
     a.R = T * a.G;
     a.S = plan.S;
     a.split_len = plan.split_len;
     a.NRG = plan.NRG;
     a.n_hs_pad = ((Hkv * plan.S + 7) / 8) * 8;
     a.scale_log2 = scale * 1.44269504088896340736f;
-    if (!causal)
+    if (!causal && !ctx_only)
         for (int i = 0; i < T; ++i) a.mask[i] = mask[i];
 
     hipStream_t st = static_cast<hipStream_t>(stream);
@@ -202,7 +211,10 @@ long long attention_slots(int D, int NW, bool causal, int kind, int fmt) {
     return slots;
 }
 
-Plan make_plan(int T, int Hq, int Hkv, int D, int L, bool causal, int n_splits_req, int fmt) {
+// n_after: keys after the L context keys (T for verify and prefill, 0 for a
+// context slice).
+Plan make_plan_keys(int T, int Hq, int Hkv, int D, int L, bool causal, int n_splits_req, int fmt,
+                    int n_after) {
     Plan p;
     const int G = Hq / Hkv;
     const long long R = (long long)T * G;
@@ -220,7 +232,7 @@ Plan make_plan(int T, int Hq, int Hkv, int D, int L, bool causal, int n_splits_r
         p.NW = row_tiles >= 4 ? 4 : (row_tiles >= 2 ? 2 : 1);
         p.NRG = (int)((row_tiles + p.NW - 1) / p.NW);
     }
-    const long long N = (long long)L + T;
+    const long long N = (long long)L + n_after;
     const long long n_tiles = (N + kKeyTile - 1) / kKeyTile;
     long long S;
     if (n_splits_req > 0) {
@@ -266,13 +278,17 @@ Plan make_plan(int T, int Hq, int Hkv, int D, int L, bool causal, int n_splits_r
     return p;
 }
 
+Plan make_plan(int T, int Hq, int Hkv, int D, int L, bool causal, int n_splits_req, int fmt) {
+    return make_plan_keys(T, Hq, Hkv, D, L, causal, n_splits_req, fmt, T);
+}
+
 }  // namespace stv
 
 extern "C" {
 
 const char *stv_last_error(void) { return g_err; }
 
-int32_t stv_abi_version(void) { return 3; }
+int32_t stv_abi_version(void) { return 4; }
 
 int stv_kv_quant_pack(const float *x, int32_t n_tok, int32_t pos0, int32_t which,
                       uint32_t *codes, uint16_t *scales, int32_t n_kv_heads, int32_t head_dim,
@@ -355,6 +371,32 @@ int stv_attention_partials(const float *q, int32_t T, int32_t n_q_heads,
     return attention_common(q, T, n_q_heads, kv, ctx_len, anc_mask, anc_mask == nullptr,
                             softmax_scale, nullptr, nullptr, nullptr, 0, n_splits, nullptr,
                             nullptr, nullptr, stream, part_o, part_lse);
+}
+
+int stv_context_plan(int32_t T, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                     int32_t n_keys, int32_t kv_format, int32_t n_splits_req,
+                     int32_t *n_splits_out, size_t *workspace_bytes_out) {
+    if (kv_format != STV_KV_3BIT && kv_format != STV_KV_4BIT_TOKEN)
+        return fail(STV_EINVAL, "kv_format %d unknown", kv_format);
+    if (T < 1 || T > STV_MAX_TREE_ROWS) return fail(STV_EINVAL, "T must be in 1..64");
+    int rc = check_heads(n_q_heads, n_kv_heads, head_dim);
+    if (rc) return rc;
+    if (n_keys < 1) return fail(STV_EINVAL, "n_keys must be >= 1");
+    if (n_splits_req < 0) return fail(STV_EINVAL, "n_splits must be >= 0");
+    const stv::Plan p = stv::make_plan_keys(T, n_q_heads, n_kv_heads, head_dim, n_keys, false,
+                                            n_splits_req, kv_format, 0);
+    if (n_splits_out) *n_splits_out = p.S;
+    if (workspace_bytes_out) *workspace_bytes_out = p.ws_bytes;
+    return ok();
+}
+
+int stv_context_partials(const float *q, int32_t T, int32_t n_q_heads, const stv_kv_layer *kv,
+                         int32_t n_keys, float softmax_scale, int32_t n_splits, float *part_o,
+                         float *part_lse, void *stream) {
+    if (!part_o) return fail(STV_EINVAL, "part_o must not be NULL");
+    return attention_common(q, T, n_q_heads, kv, n_keys, nullptr, false, softmax_scale, nullptr,
+                            nullptr, nullptr, 0, n_splits, nullptr, nullptr, nullptr, stream,
+                            part_o, part_lse, false, true);
 }
 
 int stv_split_merge(const float *part_o, const float *part_lse, int32_t S, int32_t rows,

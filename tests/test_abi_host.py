@@ -45,7 +45,7 @@ def test_header_declares_the_four_operations():
     for op in ("stv_kv_quant_pack", "stv_verify_attention", "stv_prefill_attention",
                "stv_split_merge", "stv_attention_plan", "stv_last_error", "stv_abi_version",
                "stv_tree_accept", "stv_kv_commit", "stv_lookup_plan", "stv_lookup_draft",
-               "stv_verify_attention_fp16acc"):
+               "stv_verify_attention_fp16acc", "stv_context_plan", "stv_context_partials"):
         assert op in names
 
 
@@ -56,7 +56,7 @@ def test_library_exports_every_declared_symbol(lib, stvmod):
     for name in _declared():
         assert name in exported, name
         assert hasattr(lib, name)
-    assert lib.stv_abi_version() == 3
+    assert lib.stv_abi_version() == 4
 
 
 def _layer(stvmod, hkv=4, d=256, cap=1000):
@@ -134,6 +134,21 @@ def test_alignment_errors(lib, stvmod):
     assert f(FAKE + 4, FAKE, 2, 10, 64, FAKE, None, None) == E.STV_EINVAL
     assert f(FAKE, FAKE, 2, 10, 64, FAKE + 4, None, None) == E.STV_EINVAL
     assert "aligned" in _err(lib)
+
+
+def test_context_errors(lib, stvmod):
+    E = stvmod
+    s, ws = ctypes.c_int32(), ctypes.c_size_t()
+    assert lib.stv_context_plan(8, 24, 4, 256, 0, 0, 0, ctypes.byref(s), ctypes.byref(ws)) == E.STV_EINVAL
+    assert lib.stv_context_plan(65, 24, 4, 256, 100, 0, 0, ctypes.byref(s), ctypes.byref(ws)) == E.STV_EINVAL
+    assert lib.stv_context_plan(8, 24, 4, 256, 1000, 2, 0, ctypes.byref(s), ctypes.byref(ws)) == E.STV_EINVAL
+    layer = _layer(stvmod)          # capacity 1000
+    f = lib.stv_context_partials
+    assert f(FAKE, 8, 24, ctypes.byref(layer), 1001, 0.0625, 0, FAKE, FAKE, None) == E.STV_ECAPACITY
+    assert f(FAKE, 8, 24, ctypes.byref(layer), 0, 0.0625, 0, FAKE, FAKE, None) == E.STV_EINVAL
+    assert f(FAKE, 8, 24, ctypes.byref(layer), 100, 0.0625, 0, None, FAKE, None) == E.STV_EINVAL
+    assert f(FAKE, 8, 24, ctypes.byref(layer), 100, 0.0625, 0, FAKE, None, None) == E.STV_EINVAL
+    assert f(FAKE, 65, 24, ctypes.byref(layer), 100, 0.0625, 0, FAKE, FAKE, None) == E.STV_EINVAL
 
 
 def test_fp16acc_errors(lib, stvmod):
