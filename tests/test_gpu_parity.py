@@ -334,6 +334,24 @@ def test_full_size_sampled(gpu, orc, geom, n_rows):
              check_logits=geom.n_keys * geom.n_rows <= 64 * 40000)
 
 
+@pytest.mark.parametrize("T", [1, 8])
+def test_context_length_sweep(gpu, orc, T):
+    """Error against the fp64 oracle at ten context lengths from 1 to
+    262,143 keys (one token and the 8-row tree, automatic split plan)."""
+    worst = []
+    for i, L in enumerate([1, 100, 1000, 4095, 8192, 16385, 32768, 65537, 131072, 262143]):
+        rng = np.random.default_rng(600 + 10 * T + i)
+        host = synth.make_kv(rng, 4, 256, L + T)
+        q = synth.make_q(rng, T, 24, 256)
+        mask = synth.ancestor_masks(synth.make_tree_parents(rng, T, 8) if T > 1
+                                    else synth.chain_parents(1))
+        rows = np.unique(np.linspace(0, T * 24 - 1, 8).round().astype(np.int32))
+        _, err = run_case(gpu, orc, 24, 4, 256, L, T, "tree", 0, rows=rows, host=host, q=q,
+                          mask=mask, check_logits=L <= 16385)
+        worst.append(err)
+    print(f"T={T}: max row error per context length {['%.2g' % e for e in worst]}")
+
+
 def test_partials_then_merge_equals_verify(gpu, orc):
     """The split phase plus the merge entry point reproduce the verify call
     bit for bit (the verify call runs exactly these two kernels)."""
