@@ -211,10 +211,11 @@ __device__ __forceinline__ uint32_t code4_of(float x, float s) {
 }
 
 template <bool IS_V>
-__global__ __launch_bounds__(64) void kv4_pack_kernel(const float *__restrict__ x, int n_tok,
-                                                      int pos0, uint32_t *__restrict__ codes,
+__global__ __launch_bounds__(64) void kv4_pack_kernel(const float *__restrict__ x, int pos0,
+                                                      uint32_t *__restrict__ codes,
                                                       uint16_t *__restrict__ scales, int Hkv,
                                                       int D, int cap) {
+    // one work-group per (new token t, KV head g): the grid is n_tok * Hkv
     const int t = blockIdx.x / Hkv, g = blockIdx.x - (blockIdx.x / Hkv) * Hkv;
     const int l = threadIdx.x;
     const bool act = l < D / 8;
@@ -2158,12 +2159,12 @@ hipError_t launch_kv_pack4(const float *x, int n_tok, int pos0, uint32_t *codes,
     if (n_tok == 0) return hipSuccess;
     const int rows = n_tok * Hkv;
     if (!is_v) {
-        hipLaunchKernelGGL(kv4_pack_kernel<false>, dim3(rows), dim3(64), 0, stream, x, n_tok, pos0,
-                           codes, scales, Hkv, D, cap);
+        hipLaunchKernelGGL(kv4_pack_kernel<false>, dim3(rows), dim3(64), 0, stream, x, pos0, codes,
+                           scales, Hkv, D, cap);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL(kv4_pack_kernel<true>, dim3(rows), dim3(64), 0, stream, x, n_tok, pos0,
-                       codes, scales, Hkv, D, cap);
+    hipLaunchKernelGGL(kv4_pack_kernel<true>, dim3(rows), dim3(64), 0, stream, x, pos0, codes,
+                       scales, Hkv, D, cap);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int ng = (cap + 31) / 32;
