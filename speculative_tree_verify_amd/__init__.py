@@ -55,10 +55,12 @@ _FORMATS = {"b3": STV_KV_3BIT, "i4": STV_KV_4BIT_TOKEN}
 
 
 _lib = None
+ABI_VERSION = 4      # the argument lists below follow this version of include/stv.h
 
 
 def load_library():
-    """Load libstv.so; raises if it has not been built."""
+    """Load libstv.so; raises if it has not been built or was built from
+    another version of the ABI than this binding's."""
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
@@ -70,6 +72,9 @@ def load_library():
         lib.stv_last_error.argtypes = []
         lib.stv_abi_version.restype = i32
         lib.stv_abi_version.argtypes = []
+        if lib.stv_abi_version() != ABI_VERSION:
+            raise RuntimeError(f"{LIB_PATH} implements ABI version {lib.stv_abi_version()}, "
+                               f"this binding expects {ABI_VERSION}: rebuild the library")
         lib.stv_kv_quant_pack.restype = ctypes.c_int
         lib.stv_kv_quant_pack.argtypes = [P, i32, i32, i32, P, P, i32, i32, i32, P]
         lib.stv_attention_plan.restype = ctypes.c_int

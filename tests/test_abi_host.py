@@ -56,7 +56,10 @@ def test_library_exports_every_declared_symbol(lib, stvmod):
     for name in _declared():
         assert name in exported, name
         assert hasattr(lib, name)
-    assert lib.stv_abi_version() == 4
+    assert lib.stv_abi_version() == 4 == stvmod.ABI_VERSION
+    # the header states the same version
+    with open(os.path.join(ROOT, "include", "stv.h")) as f:
+        assert re.search(r"Currently 4\b", f.read())
 
 
 def _layer(stvmod, hkv=4, d=256, cap=1000):
