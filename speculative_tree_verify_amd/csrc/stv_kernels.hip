@@ -70,6 +70,72 @@ __device__ __forceinline__ float half_bits_to_float(uint16_t h) {
     return (float)__builtin_bit_cast(_Float16, h);
 }
 
+// ---- integer form of a key's fp16 block scales (3-bit format).
+//
+// A finite binary16 scale is s = m * 2^(e - 25), with e its exponent field
+// (1 for subnormals) and m its integer significand (hidden bit included for
+// normals).  Over the nonzero scales of one key, with emin the smallest e,
+// s_b = M_b * 2^(emin - 25) and M_b = m_b << (e_b - emin).  When every
+// e_b - emin <= 3, M_b <= 2047 * 8 < 2^14, and with |S_b| <= 32 * 127 * 4 =
+// 16,256 the key's whole sum  sum_b M_b * S_b  stays below 2^31 in magnitude:
+// the block-scaled logit is one exact int32 sum, converted and scaled once.
+// Keys whose exponents spread wider, or with an Inf/NaN scale, flag their
+// tile for the per-block fp32 epilogue instead.
+constexpr uint32_t kScaleNoExp = 31u;      // exponent of a zero scale: constrains nothing
+constexpr uint32_t kScaleMaxShift = 3u;
+
+// v_mad_i32_i16: sext(s[15:0]) * sext(16-bit half HI of m) + acc, exact for
+// the operands above (|S_b| < 2^15, 0 <= M_b < 2^15, sums below 2^31).
+//
+// s is an MFMA result.  The compiler inserts the wait states a VALU read of
+// an MFMA result needs only before instructions it can see, not before
+// inline asm, so every asm read of an MFMA's results takes as an extra
+// input `ready`, the result of a compiler-visible VALU read of the same
+// MFMA (mfma_ready): the asm is then ordered after that read and its waits.
+template <int HI>
+__device__ __forceinline__ int32_t mad_i16(int32_t s, uint32_t m, int32_t acc, int32_t ready) {
+    int32_t d;
+    if constexpr (HI)
+        asm("v_mad_i32_i16 %0, %1, %2, %3 op_sel:[0,1,0,0]"
+            : "=v"(d) : "v"(s), "v"(m), "v"(acc), "v"(ready));
+    else
+        asm("v_mad_i32_i16 %0, %1, %2, %3" : "=v"(d) : "v"(s), "v"(m), "v"(acc), "v"(ready));
+    return d;
+}
+// A compiler-visible VALU read of one result register of an MFMA (all of an
+// MFMA's result registers are written when it completes).
+__device__ __forceinline__ int32_t mfma_ready(int32_t s0) { return s0 & 1; }
+
+// Minimum over the NB consecutive lanes (NB = 2, 4 or 8, aligned) holding
+// the blocks of one key: quad permutations, then a half-row mirror.
+template <int NB>
+__device__ __forceinline__ uint32_t min_over_blocks(uint32_t v) {
+    if constexpr (NB >= 2)
+        v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));
+    if constexpr (NB >= 4)
+        v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));
+    if constexpr (NB >= 8)
+        v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));
+    return v;
+}
+
+struct ScaleInt {
+    uint32_t e, m;      // exponent field (1 for subnormals; kScaleNoExp when m == 0), significand
+    bool special;       // Inf or NaN
+};
+__device__ __forceinline__ ScaleInt scale_int(uint16_t s16) {
+    const uint32_t E = (s16 >> 10) & 31u, man = s16 & 1023u;
+    ScaleInt r;
+    r.special = E == 31u;
+    r.m = E ? (man | 1024u) : man;
+    r.e = r.m ? (E ? E : 1u) : kScaleNoExp;
+    return r;
+}
+// 2^(emin - 25) as fp32 (emin in [1, 31])
+__device__ __forceinline__ float scale_unit(uint32_t emin) {
+    return __uint_as_float((emin + 102u) << 23);
+}
+
 // ------------------------------------------------------------- kv pack
 
 // Quantize the 32 elements v[] with the symmetric rule: scale fp16(amax / 3)
@@ -295,6 +361,8 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 //        all 64 banks.
 //   skh: fp16 K scales, [D/32][32 keys] (3-bit format); skf: fp32 K scale
 //        per key (4-bit per-token-head format)
+//   skm, skf: the 3-bit K scales in integer form (M [D/32][32 keys], and the
+//        key's unit 2^(emin - 25)); wide_kb flags a tile that needs skh
 //   svs: fp16 V scales as stored, [D/32][32 keys]
 template <int D>
 struct TileLds {
@@ -304,8 +372,11 @@ struct TileLds {
     static constexpr int VBPAD = 32;
     int8_t kq[kKeyTile * KQS];
     _Float16 vt[D * VTS + NB * VBPAD];
-    float skf[kKeyTile];                  // fp32 K scales per key (4-bit format)
+    // fp32 K scale per key (4-bit format); the key's unit 2^(emin - 25) (3-bit)
+    float skf[kKeyTile];
     alignas(16) _Float16 skh[NB * kKeyTile];  // fp16 K scales [D/32][32 keys] (3-bit format)
+    alignas(16) uint16_t skm[NB * kKeyTile];  // integer K scales M [D/32][32 keys] (3-bit)
+    int wide_kb;                          // = the tile's first key when a key needs the fp32 epilogue
     // the tile's V scales: [D/32][32 keys] (3-bit), or per wave [NW][32 keys]
     // (4-bit per-token-head)
     alignas(16) uint16_t svs[D > 128 ? D : 128];
@@ -332,7 +403,10 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <int D, int NT>
+// INT_SCALES: also stage the K scales in integer form (the 32-row kernel's
+// epilogue); the 16-row kernel, whose unpack sits between two barriers on
+// its critical path, uses the fp16 scales only.
+template <int D, int NT, bool INT_SCALES>
 struct TileIo {
     static constexpr int NB = D / 32;
     static constexpr int KI = kKeyTile * NB;           // K items per tile
@@ -382,8 +456,11 @@ struct TileIo {
         }
     }
 
-    // nk: keys of the tile below k1 (V scales of later keys become 0)
-    __device__ __forceinline__ void store(TileLds<D> &t, int tid, int nk) const {
+    // nk: keys of the tile below k1 (V scales of later keys become 0); kb:
+    // the tile's first key, written to t.wide_kb when a key of the tile has
+    // no exact integer scale form (the NB items of a key sit on NB
+    // consecutive lanes, all present or all absent)
+    __device__ __forceinline__ void store(TileLds<D> &t, int tid, int nk, int kb) const {
         using L = TileLds<D>;
 #pragma unroll
         for (int i = 0; i < KPT; ++i) {
@@ -399,6 +476,14 @@ struct TileIo {
                 *reinterpret_cast<u32x4 *>(t.kq + kk * L::KQS + 32 * b) = lo;
                 *reinterpret_cast<u32x4 *>(t.kq + kk * L::KQS + 32 * b + 16) = hi;
                 t.skh[b * kKeyTile + kk] = __builtin_bit_cast(_Float16, k[i].s);
+                if constexpr (INT_SCALES) {
+                    const ScaleInt si = scale_int(k[i].s);
+                    const uint32_t emin = min_over_blocks<NB>(si.e);
+                    const uint32_t shift = si.e - emin;      // 0 .. 30 (zero scales: M = 0)
+                    t.skm[b * kKeyTile + kk] = (uint16_t)(shift <= kScaleMaxShift ? si.m << shift : 0u);
+                    if (b == 0) t.skf[kk] = scale_unit(emin);
+                    if (si.special || (si.m != 0u && shift > kScaleMaxShift)) t.wide_kb = kb;
+                }
             }
         }
         // V scales: every wave stages the entries its own rows need; keys
@@ -507,7 +592,7 @@ struct TileIo4 {
         vs = __builtin_amdgcn_raw_buffer_load_b16(rvs, (tid & 31) * 2, 0, 0);
     }
 
-    __device__ __forceinline__ void store(TileLds<D> &t, int tid, int) const {
+    __device__ __forceinline__ void store(TileLds<D> &t, int tid, int, int) const {
         using L = TileLds<D>;
 #pragma unroll
         for (int i = 0; i < KPT; ++i) {
@@ -562,14 +647,15 @@ struct TileIo4 {
 };
 
 template <int D, int NT, int FMT>
-using TileIoOf = typename std::conditional<FMT == 0, TileIo<D, NT>, TileIo4<D, NT>>::type;
+using TileIoOf = typename std::conditional<FMT == 0, TileIo<D, NT, true>, TileIo4<D, NT>>::type;
 
 // PV16 selects the fp16-accumulated P.V variant (3-bit, verify only): each
 // 32-key tile's P.V product still comes out of an fp32 MFMA, but it is
 // rounded to fp16 and added into fp16 accumulators, and the running max
 // follows every increase (so P <= 1 and the fp16 sums stay in range).
 template <int D, int NW, bool CAUSAL, bool DEBUG, int FMT, bool PV16>
-__global__ __launch_bounds__(NW * 64) void attn_split_kernel(const AttnArgs a) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D == 256 && NW > 1 && !DEBUG ? 2 : 1)))
+void attn_split_kernel(const AttnArgs a) {
     constexpr int NB = D / 32;
     constexpr int KT = kKeyTile;
     constexpr int NT = NW * 64;
@@ -720,18 +806,26 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(const AttnArgs a) {
     TileIoOf<D, NT, FMT> io0, io1;
     io0.load(a, head, k0, k0, k1, tid);
     if constexpr (AHEAD == 2) io1.load(a, head, k0 + KT, k0, k1, tid);
+    if constexpr (FMT == 0) {
+        if (tid == 0) lds.wide_kb = -1;
+        __syncthreads();
+    }
 
     auto tile = [&](TileIoOf<D, NT, FMT> &io, int kb) {
-        io.store(lds, tid, min(KT, k1 - kb));
+        io.store(lds, tid, min(KT, k1 - kb), kb);
         __syncthreads();
         io.load(a, head, kb + AHEAD * KT, k0, k1, tid);
 
         if (wave_active) {
             f32x16 acc = f32x16{};
-            if constexpr (FMT == 0) {
-                // ---- Q.K^T: one int8 MFMA per 32-element block, fp32 epilogue.
-                // The MFMA of block b + 1 is issued before the epilogue of block b
-                // reads its results, so the matrix unit and the VALU overlap.
+            const bool exact_int = FMT == 0 && __builtin_amdgcn_readfirstlane(lds.wide_kb) != kb;
+            if (exact_int) {
+                // ---- Q.K^T: one int8 MFMA per 32-element block; the block
+                // scales in integer form, so the key's logit is one int32
+                // sum (one v_mad_i32_i16 per block), converted and scaled
+                // once.  The MFMA of block b + 1 is issued before block b's
+                // sums read its results.
+                i32x16 iacc = i32x16{};
                 i32x16 s_cur = __builtin_amdgcn_mfma_i32_32x32x32_i8(
                     *reinterpret_cast<const i32x4 *>(kq_lane),
                     *reinterpret_cast<const i32x4 *>(q_lane), i32x16{}, 0, 0, 0);
@@ -742,6 +836,44 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(const AttnArgs a) {
                         s_next = __builtin_amdgcn_mfma_i32_32x32x32_i8(
                             *reinterpret_cast<const i32x4 *>(kq_lane + 32 * (b + 1)),
                             *reinterpret_cast<const i32x4 *>(q_lane + 32 * (b + 1)), i32x16{}, 0, 0, 0);
+                    // M of keys 8hl + [0, 8) and 16 + 8hl + [0, 8), two per word
+                    const u32x4 m0 = *reinterpret_cast<const u32x4 *>(lds.skm + b * KT + 8 * hl);
+                    const u32x4 m1 = *reinterpret_cast<const u32x4 *>(lds.skm + b * KT + 16 + 8 * hl);
+                    const int32_t ready = mfma_ready(s_cur[0]);
+#pragma unroll
+                    for (int r = 0; r < 8; r += 2) {
+                        iacc[r] = mad_i16<0>(s_cur[r], m0[r >> 1], iacc[r], ready);
+                        iacc[r + 1] = mad_i16<1>(s_cur[r + 1], m0[r >> 1], iacc[r + 1], ready);
+                        iacc[8 + r] = mad_i16<0>(s_cur[8 + r], m1[r >> 1], iacc[8 + r], ready);
+                        iacc[9 + r] = mad_i16<1>(s_cur[9 + r], m1[r >> 1], iacc[9 + r], ready);
+                    }
+                    if (DEBUG && a.dbg_logits && row_ok) {
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int key = kb + (r < 8 ? 8 * hl + r : 16 + 8 * hl + (r - 8));
+                            if (key < k1)
+                                a.dbg_logits[((size_t)flat * a.N + key) * NB + b] = s_cur[r];
+                        }
+                    }
+                    if (b + 1 < NB) s_cur = s_next;
+                }
+                const f32x4 u0 = *reinterpret_cast<const f32x4 *>(lds.skf + 8 * hl);
+                const f32x4 u1 = *reinterpret_cast<const f32x4 *>(lds.skf + 8 * hl + 4);
+                const f32x4 u2 = *reinterpret_cast<const f32x4 *>(lds.skf + 16 + 8 * hl);
+                const f32x4 u3 = *reinterpret_cast<const f32x4 *>(lds.skf + 16 + 8 * hl + 4);
+                const float unit[16] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w,
+                                        u2.x, u2.y, u2.z, u2.w, u3.x, u3.y, u3.z, u3.w};
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[r] = unit[r] * (float)iacc[r];
+            } else if constexpr (FMT == 0) {
+                // ---- the per-block fp32 epilogue, for tiles with a key
+                // whose scales have no exact integer form (rare: kept short,
+                // without the MFMA pipelining, to spare registers)
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    const i32x16 s_cur = __builtin_amdgcn_mfma_i32_32x32x32_i8(
+                        *reinterpret_cast<const i32x4 *>(kq_lane + 32 * b),
+                        *reinterpret_cast<const i32x4 *>(q_lane + 32 * b), i32x16{}, 0, 0, 0);
                     // fp16 scales of keys 8hl + [0, 8) and 16 + 8hl + [0, 8); the FMA
                     // widens them in the instruction (v_fma_mix_f32)
                     const f16x8 h0 = *reinterpret_cast<const f16x8 *>(lds.skh + b * KT + 8 * hl);
@@ -759,7 +891,6 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(const AttnArgs a) {
                                 a.dbg_logits[((size_t)flat * a.N + key) * NB + b] = s_cur[r];
                         }
                     }
-                    if (b + 1 < NB) s_cur = s_next;
                 }
             } else {
                 // ---- 4-bit per-token-head: the int8 MFMAs of all blocks
@@ -1054,10 +1185,10 @@ __global__ __launch_bounds__(256) void attn_split16_kernel(const AttnArgs a) {
     float m_run = -INFINITY;
     float l_run = 0.0f;
 
-    TileIo<D, NT> io;
+    TileIo<D, NT, false> io;
     io.load(a, head, k0, k0, k1, tid);
     for (int kb = k0; kb < k1; kb += KT) {
-        io.store(lds, tid, min(KT, k1 - kb));
+        io.store(lds, tid, min(KT, k1 - kb), kb);
         __syncthreads();
         io.load(a, head, kb + KT, k0, k1, tid);
 

@@ -159,6 +159,70 @@ def test_parity_planted_keys(gpu, orc):
     run_case(gpu, orc, hq, hkv, d, L, T, "tree", 123, host=host, q=q)
 
 
+def _f16_bits(x):
+    return np.asarray(x, dtype=np.float16).view(np.uint16)
+
+
+@pytest.mark.parametrize("kind,T", [("tree", 64), ("prefill", 40)])
+def test_k_scale_exponent_spread(gpu, orc, kind, T):
+    """Keys whose fp16 block scales span more than three binades, or hold
+    zeros and subnormals, next to ordinary keys in one call.  For more than
+    64 rows per KV head the kernel sums a key's blocks in int32 with integer
+    scales when the spread allows it and takes the per-block fp32 epilogue
+    for tiles where it does not; both match the oracle."""
+    rng = np.random.default_rng(150 if kind == "tree" else 151)
+    hq, hkv, d, L = 24, 4, 256, 2000
+    host = synth.make_kv(rng, hkv, d, L + T, L + T + 3)
+    ks = host.k_scales                       # [Hkv][cap][D/32], fp16 bits
+
+    def key(tile, i):
+        return 32 * tile + i
+
+    # four binades (0.01 .. 0.2): the tile takes the fp32 epilogue
+    ks[0, key(3, 5)] = _f16_bits([0.01, 0.2, 0.05, 0.05, 0.05, 0.05, 0.05, 0.05])
+    # one block 64 times the others: fp32 epilogue
+    ks[1, key(7, 0), 0] = _f16_bits(ks[1, key(7, 0), 0].view(np.float16).astype(np.float32) * 64)
+    # exactly three binades (2^-7 and just under 2^-3): integer path
+    ks[2, key(12, 9)] = _f16_bits([2**-7, 0.1249, 2**-7, 0.1249, 0.05, 0.02, 0.0625, 0.09])
+    # every block subnormal
+    ks[3, key(10, 31)] = _f16_bits(rng.uniform(1e-7, 5e-6, 8))
+    # the smallest normal next to subnormals (one exponent for all)
+    ks[2, key(14, 8)] = _f16_bits([2**-14, 2**-15, 2**-16, 2**-17] * 2)
+    # zero blocks, and a key of zeros only
+    ks[:, key(11, 2), ::3] = 0
+    ks[1, key(13, 4)] = 0
+    # a tree or chunk key (position >= L) with a wide spread
+    ks[0, L + 2] = _f16_bits([0.001, 0.5, 0.05, 0.05, 0.05, 0.05, 0.05, 0.05])
+    run_case(gpu, orc, hq, hkv, d, L, T, kind, 152, host=host)
+    run_case(gpu, orc, hq, hkv, d, L, T, kind, 153, host=host, scale_mul=16.0)
+
+
+@pytest.mark.parametrize("kind,T", [("tree", 64), ("prefill", 40)])
+def test_k_scale_integer_sum_bound(gpu, orc, kind, T):
+    """The largest sums the integer-scale path can meet.  Rows whose Q
+    elements are all equal quantize to int8 +-127; keys with every code 0
+    (k = -4) then give block sums of -+16,256, and their scales put seven
+    blocks three binades above the eighth with the largest significand
+    (65504 and 8188), so sum_b M_b * S_b = 16,256 * (7 * 16,376 + 2,047) in
+    magnitude, 88% of the int32 range.  The int32 block sums stay bit-exact
+    and the outputs match the oracle."""
+    rng = np.random.default_rng(154 if kind == "tree" else 155)
+    hq, hkv, d, L = 24, 4, 256, 700
+    host = synth.make_kv(rng, hkv, d, L + T, L + T + 3)
+    q = synth.make_q(rng, T, hq, d)
+    q[:, 0::3] = 1.0
+    q[:, 1::3] = -1.0
+    heavy = rng.choice(L, 40, replace=False)
+    zero_codes = orc.pack_block(np.zeros(32, dtype=int))
+    scales = np.array([0x6FFF] + [0x7BFF] * 7, dtype=np.uint16)
+    assert np.float16(scales.view(np.float16)[0]) == 8188 and scales.view(np.float16)[1] == 65504
+    for j in heavy:
+        host.k_codes[:, j] = zero_codes
+        host.k_scales[:, j] = scales
+    # logits of the heavy keys near +-6 for the equal-element rows
+    run_case(gpu, orc, hq, hkv, d, L, T, kind, 156, host=host, q=q, scale_mul=1.6e-6)
+
+
 def test_residue_sweep(gpu, orc):
     """Context lengths over every residue of the 32-key tile, and split
     boundaries moved with them (a length-dependent corruption shows up as
