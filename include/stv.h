@@ -150,6 +150,23 @@ int stv_attention_plan(int32_t T, int32_t n_q_heads, int32_t n_kv_heads, int32_t
                        int32_t *n_splits_out, size_t *workspace_bytes_out);
 
 /*
+ * stv_workspace_bytes -- workspace a verify or prefill call with a known
+ * split count S needs: the split partials O_s (fp32 [S][T * n_q_heads]
+ * [head_dim]) followed by their log-sum-exps (fp32 [S][T * n_q_heads]),
+ * i.e. S * T * n_q_heads * (head_dim + 1) * 4 bytes, or 0 when S = 1 (one
+ * split writes the output directly).  Split-K with a merge of the partials:
+ * elpis-lossless, "Trust base" (the split-K barrier); elpis, "Why fast" (the
+ * prefill merge).  stv_attention_plan gives S (and this same size) for a
+ * call whose split count the library chooses.
+ *   T, n_q_heads  query rows and heads of the call (T >= 1, n_q_heads >= 1)
+ *   head_dim      64, 128 or 256
+ *   n_splits      the call's effective split count S >= 1
+ * Returns the byte count; on invalid arguments returns 0 and sets
+ * stv_last_error.  No HIP call, no allocation.
+ */
+size_t stv_workspace_bytes(int32_t T, int32_t n_q_heads, int32_t head_dim, int32_t n_splits);
+
+/*
  * stv_verify_attention -- attention of T draft-tree rows over the cache
  * (elpis, "Why fast": decode verify with int8 Q.K^T; "How": the token tree).
  *   q           fp32 [T][n_q_heads][head_dim]; query head h reads kv head

@@ -28,7 +28,7 @@ STV_EWORKSPACE = -4
 STV_EHIP = -5
 
 __all__ = [
-    "StvError", "KVCache", "load_library", "kv_quant_pack", "attention_plan",
+    "StvError", "KVCache", "load_library", "kv_quant_pack", "attention_plan", "workspace_bytes",
     "verify_attention", "verify_attention_fp16acc", "prefill_attention",
     "attention_partials", "context_plan", "context_partials", "split_merge", "tree_accept", "kv_commit", "lookup_plan",
     "lookup_draft", "STV_OK", "STV_EINVAL", "STV_EMASK", "STV_ECAPACITY", "STV_EWORKSPACE",
@@ -77,6 +77,8 @@ def load_library():
                                f"this binding expects {ABI_VERSION}: rebuild the library")
         lib.stv_kv_quant_pack.restype = ctypes.c_int
         lib.stv_kv_quant_pack.argtypes = [P, i32, i32, i32, P, P, i32, i32, i32, P]
+        lib.stv_workspace_bytes.restype = ctypes.c_size_t
+        lib.stv_workspace_bytes.argtypes = [i32, i32, i32, i32]
         lib.stv_attention_plan.restype = ctypes.c_int
         lib.stv_attention_plan.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32,
                                            ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_size_t)]
@@ -253,6 +255,15 @@ def attention_plan(T: int, n_q_heads: int, n_kv_heads: int, head_dim: int, ctx_l
                                              int(bool(causal)), _FORMATS[fmt], n_splits,
                                              ctypes.byref(s), ctypes.byref(ws)))
     return int(s.value), int(ws.value)
+
+
+def workspace_bytes(T: int, n_q_heads: int, head_dim: int, n_splits: int) -> int:
+    """Workspace bytes of a call with split count n_splits (0 when it is 1)."""
+    lib = load_library()
+    n = int(lib.stv_workspace_bytes(T, n_q_heads, head_dim, n_splits))
+    if n == 0 and lib.stv_last_error():
+        raise StvError(STV_EINVAL, lib.stv_last_error().decode())
+    return n
 
 
 def _attention(q, kv: KVCache, ctx_len: int, mask, softmax_scale, out, out_lse, workspace,

@@ -334,6 +334,20 @@ int stv_attention_plan(int32_t T, int32_t n_q_heads, int32_t n_kv_heads, int32_t
     return ok();
 }
 
+size_t stv_workspace_bytes(int32_t T, int32_t n_q_heads, int32_t head_dim, int32_t n_splits) {
+    if (T < 1) return fail(STV_EINVAL, "T must be >= 1"), (size_t)0;
+    if (n_q_heads < 1) return fail(STV_EINVAL, "n_q_heads must be >= 1"), (size_t)0;
+    if (!head_dim_ok(head_dim))
+        return fail(STV_EINVAL, "head_dim %d unsupported (64, 128 or 256)", head_dim), (size_t)0;
+    if (n_splits < 1)
+        return fail(STV_EINVAL, "n_splits must be >= 1 (stv_attention_plan chooses it)"), (size_t)0;
+    if ((long long)T * n_q_heads >= (1ll << 31))
+        return fail(STV_EINVAL, "T * n_q_heads too large"), (size_t)0;
+    ok();
+    if (n_splits == 1) return 0;
+    return (size_t)n_splits * (size_t)T * (size_t)n_q_heads * ((size_t)head_dim + 1) * sizeof(float);
+}
+
 int stv_verify_attention(const float *q, int32_t T, int32_t n_q_heads, const stv_kv_layer *kv,
                          int32_t ctx_len, const uint64_t *anc_mask, float softmax_scale,
                          float *out, float *out_lse, void *workspace, size_t workspace_bytes,

@@ -45,7 +45,8 @@ def test_header_declares_the_four_operations():
     for op in ("stv_kv_quant_pack", "stv_verify_attention", "stv_prefill_attention",
                "stv_split_merge", "stv_attention_plan", "stv_last_error", "stv_abi_version",
                "stv_tree_accept", "stv_kv_commit", "stv_lookup_plan", "stv_lookup_draft",
-               "stv_verify_attention_fp16acc", "stv_context_plan", "stv_context_partials"):
+               "stv_verify_attention_fp16acc", "stv_context_plan", "stv_context_partials",
+               "stv_workspace_bytes"):
         assert op in names
 
 
@@ -325,12 +326,26 @@ def test_plan_is_consistent(stvmod, T, hq, hkv, d, L, causal, fmt):
         if req:
             assert S <= req
         assert ws == (S * T * hq * (d + 1) * 4 if S > 1 else 0)
+        assert ws == stvmod.workspace_bytes(T, hq, d, S)
         # the documented split layout covers every key, each split non-empty
         P = 32 * -(-n_tiles // S)
         assert (S - 1) * P < L + T <= S * P
     S0, _ = stvmod.attention_plan(T, hq, hkv, d, L, bool(causal), 0)
     S1, _ = stvmod.attention_plan(T, hq, hkv, d, L, bool(causal), 0)
     assert S0 == S1
+
+
+def test_workspace_bytes(stvmod):
+    lib = stvmod.load_library()
+    assert stvmod.workspace_bytes(64, 24, 256, 42) == 42 * 64 * 24 * 257 * 4
+    assert stvmod.workspace_bytes(1, 24, 256, 1) == 0
+    assert lib.stv_last_error() == b""
+    for args in ((0, 24, 256, 2), (8, 0, 256, 2), (8, 24, 96, 2), (8, 24, 256, 0),
+                 (8, 24, 256, -3), (1 << 30, 4, 256, 2)):
+        assert lib.stv_workspace_bytes(*args) == 0
+        assert lib.stv_last_error() != b""
+        with pytest.raises(stvmod.StvError):
+            stvmod.workspace_bytes(*args)
 
 
 def test_product_path_refuses_to_run_without_the_library(stvmod, monkeypatch, tmp_path):
