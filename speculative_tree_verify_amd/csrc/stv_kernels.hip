@@ -1256,11 +1256,19 @@ __global__ __launch_bounds__(256) void attn_split16_kernel(const AttnArgs a) {
             f16x8 pk;
             float psum = 0.0f;
             const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+            // only a tile holding masked keys (the split's last) has -inf logits
+            float pe[8];
+            if (masked) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    pe[e] = acc[e] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(fmaf(acc[e], c_row, -mm));
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) pe[e] = __builtin_amdgcn_exp2f(fmaf(acc[e], c_row, -mm));
+            }
 #pragma unroll
             for (int e = 0; e < 8; e += 2) {
-                const float p0 = acc[e] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(fmaf(acc[e], c_row, -mm));
-                const float p1 = acc[e + 1] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(fmaf(acc[e + 1], c_row, -mm));
-                const f16x2 h2 = __builtin_convertvector(f32x2{p0, p1}, f16x2);
+                const f16x2 h2 = __builtin_convertvector(f32x2{pe[e], pe[e + 1]}, f16x2);
                 pk[e] = h2.x;
                 pk[e + 1] = h2.y;
                 psum = __builtin_amdgcn_fdot2(h2, ones, psum, false);
@@ -1703,11 +1711,19 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_dec_kernel(const AttnArgs
         f16x8 pk;
         float psum = 0.0f;
         const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+        // only a tile holding masked keys (the split's last) has -inf logits
+        float pe[8];
+        if (masked) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                pe[e] = acc[e] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(fmaf(acc[e], c_row, -mm));
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) pe[e] = __builtin_amdgcn_exp2f(fmaf(acc[e], c_row, -mm));
+        }
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
-            const float p0 = acc[e] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(fmaf(acc[e], c_row, -mm));
-            const float p1 = acc[e + 1] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(fmaf(acc[e + 1], c_row, -mm));
-            const f16x2 h2 = __builtin_convertvector(f32x2{p0, p1}, f16x2);
+            const f16x2 h2 = __builtin_convertvector(f32x2{pe[e], pe[e + 1]}, f16x2);
             pk[e] = h2.x;
             pk[e + 1] = h2.y;
             psum = __builtin_amdgcn_fdot2(h2, ones, psum, false);
