@@ -38,6 +38,7 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // Word 3 of a raw buffer descriptor on gfx9: 32-bit data format, no swizzle.
 constexpr int kBufWord3 = 0x00020000;
@@ -364,10 +365,15 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 //   skm, skf: the 3-bit K scales in integer form (M [D/32][32 keys], and the
 //        key's unit 2^(emin - 25)); wide_kb flags a tile that needs skh
 //   svs: fp16 V scales as stored, [D/32][32 keys]
-template <int D>
+//   KROT: the 16-row kernel's K layout.  Its Q.K^T operand read takes rows
+//        8(i / 4) + i % 4 (+ 4) for lanes i = 0..15, so rows 16 apart meet in
+//        one read; with a 272-byte stride they share banks.  Rows of 296
+//        bytes, with row k's data shifted by 8 (k % 4) bytes, put the 32
+//        8-byte reads of every half-wave on 64 distinct banks.
+template <int D, bool KROT = false>
 struct TileLds {
     static constexpr int NB = D / 32;
-    static constexpr int KQS = D + 16;
+    static constexpr int KQS = KROT ? D + 40 : D + 16;
     static constexpr int VTS = kKeyTile + 8;
     static constexpr int VBPAD = 32;
     int8_t kq[kKeyTile * KQS];
@@ -406,7 +412,7 @@ __device__ __forceinline__ void wave_lds_sync() {
 // INT_SCALES: also stage the K scales in integer form (the 32-row kernel's
 // epilogue); the 16-row kernel, whose unpack sits between two barriers on
 // its critical path, uses the fp16 scales only.
-template <int D, int NT, bool INT_SCALES>
+template <int D, int NT, bool INT_SCALES, bool KROT = false>
 struct TileIo {
     static constexpr int NB = D / 32;
     static constexpr int KI = kKeyTile * NB;           // K items per tile
@@ -460,8 +466,8 @@ struct TileIo {
     // the tile's first key, written to t.wide_kb when a key of the tile has
     // no exact integer scale form (the NB items of a key sit on NB
     // consecutive lanes, all present or all absent)
-    __device__ __forceinline__ void store(TileLds<D> &t, int tid, int nk, int kb) const {
-        using L = TileLds<D>;
+    __device__ __forceinline__ void store(TileLds<D, KROT> &t, int tid, int nk, int kb) const {
+        using L = TileLds<D, KROT>;
 #pragma unroll
         for (int i = 0; i < KPT; ++i) {
             const int item = tid + i * NT;
@@ -469,12 +475,21 @@ struct TileIo {
                 const int kk = item / NB, b = item % NB;
                 uint32_t o[8];
                 unpack_bytes(k[i].w[0], k[i].w[1], k[i].w[2], o);
-                const u32x4 lo = {codes_to_i8(o[0]), codes_to_i8(o[1]), codes_to_i8(o[2]),
-                                  codes_to_i8(o[3])};
-                const u32x4 hi = {codes_to_i8(o[4]), codes_to_i8(o[5]), codes_to_i8(o[6]),
-                                  codes_to_i8(o[7])};
-                *reinterpret_cast<u32x4 *>(t.kq + kk * L::KQS + 32 * b) = lo;
-                *reinterpret_cast<u32x4 *>(t.kq + kk * L::KQS + 32 * b + 16) = hi;
+                if constexpr (KROT) {
+                    // 8-byte pieces: the row shift keeps them 8-byte aligned only
+                    int8_t *row = t.kq + kk * L::KQS + 8 * (kk & 3) + 32 * b;
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+                        *reinterpret_cast<u32x2 *>(row + 8 * c) =
+                            u32x2{codes_to_i8(o[2 * c]), codes_to_i8(o[2 * c + 1])};
+                } else {
+                    const u32x4 lo = {codes_to_i8(o[0]), codes_to_i8(o[1]), codes_to_i8(o[2]),
+                                      codes_to_i8(o[3])};
+                    const u32x4 hi = {codes_to_i8(o[4]), codes_to_i8(o[5]), codes_to_i8(o[6]),
+                                      codes_to_i8(o[7])};
+                    *reinterpret_cast<u32x4 *>(t.kq + kk * L::KQS + 32 * b) = lo;
+                    *reinterpret_cast<u32x4 *>(t.kq + kk * L::KQS + 32 * b + 16) = hi;
+                }
                 t.skh[b * kKeyTile + kk] = __builtin_bit_cast(_Float16, k[i].s);
                 if constexpr (INT_SCALES) {
                     const ScaleInt si = scale_int(k[i].s);
@@ -1080,7 +1095,7 @@ __global__ __launch_bounds__(256) void attn_split16_kernel(const AttnArgs a) {
     constexpr int KT = kKeyTile;
     constexpr int NW = 4;
     constexpr int NT = NW * 64;
-    using L = TileLds<D>;
+    using L = TileLds<D, true>;
     __shared__ __attribute__((aligned(16))) L lds;
 
     // ---- work-group -> (kv head, split, group of 64 rows); the row groups of
@@ -1172,7 +1187,8 @@ __global__ __launch_bounds__(256) void attn_split16_kernel(const AttnArgs a) {
     // result registers of lane (i16, qc) hold keys 8qc + 4kh + [0, 4): its
     // eight logits are keys 8qc + [0, 8), the run the P.V operand wants.
     const int krow0 = 8 * (i16 >> 2) + (i16 & 3);
-    const int8_t *kq_lane = lds.kq + krow0 * L::KQS + 8 * qc;
+    // (row shift: rows krow0 and krow0 + 4 both start 8 (i16 % 4) bytes in)
+    const int8_t *kq_lane = lds.kq + krow0 * L::KQS + 8 * (i16 & 3) + 8 * qc;
 
     f32x4 oacc[NDT];
 #pragma unroll
@@ -1185,7 +1201,7 @@ __global__ __launch_bounds__(256) void attn_split16_kernel(const AttnArgs a) {
     float m_run = -INFINITY;
     float l_run = 0.0f;
 
-    TileIo<D, NT, false> io;
+    TileIo<D, NT, false, true> io;
     io.load(a, head, k0, k0, k1, tid);
     for (int kb = k0; kb < k1; kb += KT) {
         io.store(lds, tid, min(KT, k1 - kb), kb);
