@@ -365,17 +365,22 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 //   skm, skf: the 3-bit K scales in integer form (M [D/32][32 keys], and the
 //        key's unit 2^(emin - 25)); wide_kb flags a tile that needs skh
 //   svs: fp16 V scales as stored, [D/32][32 keys]
-//   KROT: the 16-row kernel's K layout.  Its Q.K^T operand read takes rows
-//        8(i / 4) + i % 4 (+ 4) for lanes i = 0..15, so rows 16 apart meet in
-//        one read; with a 272-byte stride they share banks.  Rows of 296
-//        bytes, with row k's data shifted by 8 (k % 4) bytes, put the 32
-//        8-byte reads of every half-wave on 64 distinct banks.
-template <int D, bool KROT = false>
+//   S16: the 16-row kernel's layout, set by what its operand reads measure
+//        on gfx950 (8-byte reads: 64 banks, 32 lanes a cycle).
+//        K: its Q.K^T operand read takes rows 8(i / 4) + i % 4 (+ 4) for
+//        lanes i = 0..15, so rows 16 apart meet in one read; with a 272-byte
+//        stride they share banks.  Rows of 296 bytes, with row k's data
+//        shifted by 8 (k % 4) bytes, put the 8-byte reads on distinct banks.
+//        V^T: its P.V operand read takes 16 bytes (keys 8q .. 8q + 7) of
+//        rows d .. d + 15; 40-key rows measure two cycles per read where
+//        one suffices.  Unpadded 32-key rows with the 16-byte chunk q stored
+//        at q ^ ((d >> 1) & 3) measure one.
+template <int D, bool S16 = false>
 struct TileLds {
     static constexpr int NB = D / 32;
-    static constexpr int KQS = KROT ? D + 40 : D + 16;
-    static constexpr int VTS = kKeyTile + 8;
-    static constexpr int VBPAD = 32;
+    static constexpr int KQS = S16 ? D + 40 : D + 16;
+    static constexpr int VTS = S16 ? kKeyTile : kKeyTile + 8;
+    static constexpr int VBPAD = S16 ? 0 : 32;
     int8_t kq[kKeyTile * KQS];
     _Float16 vt[D * VTS + NB * VBPAD];
     // fp32 K scale per key (4-bit format); the key's unit 2^(emin - 25) (3-bit)
@@ -412,7 +417,7 @@ __device__ __forceinline__ void wave_lds_sync() {
 // INT_SCALES: also stage the K scales in integer form (the 32-row kernel's
 // epilogue); the 16-row kernel, whose unpack sits between two barriers on
 // its critical path, uses the fp16 scales only.
-template <int D, int NT, bool INT_SCALES, bool KROT = false>
+template <int D, int NT, bool INT_SCALES, bool S16 = false>
 struct TileIo {
     static constexpr int NB = D / 32;
     static constexpr int KI = kKeyTile * NB;           // K items per tile
@@ -466,8 +471,8 @@ struct TileIo {
     // the tile's first key, written to t.wide_kb when a key of the tile has
     // no exact integer scale form (the NB items of a key sit on NB
     // consecutive lanes, all present or all absent)
-    __device__ __forceinline__ void store(TileLds<D, KROT> &t, int tid, int nk, int kb) const {
-        using L = TileLds<D, KROT>;
+    __device__ __forceinline__ void store(TileLds<D, S16> &t, int tid, int nk, int kb) const {
+        using L = TileLds<D, S16>;
 #pragma unroll
         for (int i = 0; i < KPT; ++i) {
             const int item = tid + i * NT;
@@ -475,7 +480,7 @@ struct TileIo {
                 const int kk = item / NB, b = item % NB;
                 uint32_t o[8];
                 unpack_bytes(k[i].w[0], k[i].w[1], k[i].w[2], o);
-                if constexpr (KROT) {
+                if constexpr (S16) {
                     // 8-byte pieces: the row shift keeps them 8-byte aligned only
                     int8_t *row = t.kq + kk * L::KQS + 8 * (kk & 3) + 32 * b;
 #pragma unroll
@@ -533,9 +538,10 @@ struct TileIo {
                     row[2 * qq + 1] = __builtin_bit_cast(uint32_t, v23);
                 }
                 u32x4 *dst = reinterpret_cast<u32x4 *>(t.vt + d * L::VTS + (d / 32) * L::VBPAD);
+                const int sw = S16 ? (d >> 1) & 3 : 0;      // chunk swizzle of the S16 layout
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    dst[j] = u32x4{row[4 * j], row[4 * j + 1], row[4 * j + 2], row[4 * j + 3]};
+                    dst[j ^ sw] = u32x4{row[4 * j], row[4 * j + 1], row[4 * j + 2], row[4 * j + 3]};
             }
         }
     }
@@ -1296,7 +1302,8 @@ __global__ __launch_bounds__(256) void attn_split16_kernel(const AttnArgs a) {
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt) {
                 const int d = 16 * dt + i16;
-                const f16x8 vop = *reinterpret_cast<const f16x8 *>(lds.vt + d * L::VTS + (d / 32) * L::VBPAD + 8 * qc);
+                // (d >> 1) & 3 = (i16 >> 1) & 3: the layout's chunk swizzle
+                const f16x8 vop = *reinterpret_cast<const f16x8 *>(lds.vt + d * L::VTS + 8 * (qc ^ ((i16 >> 1) & 3)));
                 if constexpr (PV16) {
                     const f32x4 tp = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop, pk, f32x4{}, 0, 0, 0);
                     oh[dt][0] += __builtin_convertvector(f32x2{tp[0], tp[1]}, f16x2);
