@@ -200,6 +200,12 @@ size_t stv_workspace_bytes(int32_t T, int32_t n_q_heads, int32_t head_dim, int32
  * q8 = clamp(rint(q * inv), -127, 127); sq = amax / 127; a zero row gives
  * sq = 0 and zero codes.  Logit of key j: softmax_scale * sq *
  * sum_b k_scale[j][b] * S_b[j] with S_b the int32 block sums.
+ * Value range: P.V takes fp16 operands (elpis-lossless, "Trust base": the
+ * m16n8k16 fp16 shape).  Calls of more than 16 rows per kv head (3-bit
+ * format) and the 4-bit format above 64 rows dequantize V to fp16 s (c - 4)
+ * (4-bit: s (c - 8)), so V scales must stay at or below 16,376 (4-bit:
+ * 8,188); beyond that the result is undefined.  Calls of up to 16 rows per
+ * kv head (4-bit: 64) accept every finite V scale.
  * Errors: STV_EINVAL, STV_EMASK, STV_ECAPACITY, STV_EWORKSPACE, STV_EHIP.
  */
 int stv_verify_attention(const float *q, int32_t T, int32_t n_q_heads,

@@ -674,50 +674,83 @@ using TileIoOf = typename std::conditional<FMT == 0, TileIo<D, NT, true>, TileIo
 // 32-key tile's P.V product still comes out of an fp32 MFMA, but it is
 // rounded to fp16 and added into fp16 accumulators, and the running max
 // follows every increase (so P <= 1 and the fp16 sums stay in range).
-template <int D, int NW, bool CAUSAL, bool DEBUG, int FMT, bool PV16>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D == 256 && NW > 1 && !DEBUG ? 2 : 1)))
+//
+// NG groups of NW waves per work-group.  Each group owns one (kv head, row
+// group of NW x 32 rows, context split) item, its own Q and tile in LDS, and
+// walks its tiles in three phases: U (store the held tile to LDS, fetch the
+// next), C (Q.K^T, block-scale epilogue, mask, online softmax) and P (P.V).
+// Every phase ends at a work-group barrier.  With NG = 2 the second group
+// runs one phase behind the first, and wave w of each group sits on SIMD
+// w, so the two waves a SIMD holds are always in different phases: the
+// VALU-heavy C of one beside the MFMA-only P or the lighter U of the other.
+// (Two independent work-groups per CU would drift into the same phase,
+// since each is held together by its own barriers.)  With NG = 1 the
+// phases C and P fuse and a tile takes two barriers.
+template <int D, int NW, int NG, bool CAUSAL, bool DEBUG, int FMT, bool PV16>
+__global__ __launch_bounds__(NG * NW * 64) __attribute__((amdgpu_waves_per_eu(D == 256 && NG * NW > 1 && !DEBUG ? 2 : 1)))
 void attn_split_kernel(const AttnArgs a) {
     constexpr int NB = D / 32;
     constexpr int KT = kKeyTile;
     constexpr int NT = NW * 64;
     using L = TileLds<D>;
-    __shared__ __attribute__((aligned(16))) L lds;
-    // int8 Q of each wave's 32 rows, [NW][32 rows][D + 16] bytes: read back as
-    // the B operand of every Q.K^T MFMA, which keeps 32 VGPRs free for
-    // double-buffering the MFMA results.
-    __shared__ __attribute__((aligned(16))) int8_t qlds[NW * kRowTile * L::KQS];
+    __shared__ __attribute__((aligned(16))) L lds_g[NG];
+    // int8 Q of each wave's 32 rows, [NG][NW][32 rows][D + 16] bytes: read
+    // back as the B operand of every Q.K^T MFMA, which keeps 32 VGPRs free
+    // for double-buffering the MFMA results.
+    __shared__ __attribute__((aligned(16))) int8_t qlds_g[NG * NW * kRowTile * L::KQS];
 
-    // ---- work-group -> (kv head, split, row group).  Row groups of one
-    // (head, split) get ids 8 apart so they share an XCD and its L2.
-    const int id = blockIdx.x;
-    const int chunk = id / (8 * a.NRG);
-    const int within = id - chunk * 8 * a.NRG;
-    const int rg = within >> 3;
-    const int hs = chunk * 8 + (within & 7);
-    if (hs >= a.Hkv * a.S) return;
-    const int head = hs / a.S;
-    const int split = hs - head * a.S;
-
-    const int tid = threadIdx.x;
+    const int grp = NG == 2 ? __builtin_amdgcn_readfirstlane((int)threadIdx.x / NT) : 0;
+    const int tid = threadIdx.x - grp * NT;
+    L &lds = lds_g[grp];
+    int8_t *qlds = qlds_g + grp * NW * kRowTile * L::KQS;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int hl = lane >> 5;
     const int l32 = lane & 31;
 
+    // ---- work item of each group.  Items ("virtual work-groups") map to
+    // (kv head, split, row group) so that the row groups of one (head,
+    // split) get ids 8 apart; a work-group takes items v and v + 8 (NG = 2),
+    // so both sit on one XCD (work-group i runs on XCD i mod 8) and they
+    // usually share a key range, hence a tile count.
+    // An item with no visible key (a causal row group whose rows end before
+    // its split) still writes its empty partial: zeros with lse = -inf.
+    struct Item {
+        int head, split, rg, k0, k1, n_tiles;
+        bool valid;
+    };
+    auto item_of = [&](int g) {
+        Item it{0, 0, 0, 0, 0, 0, false};
+        const int v = NG == 2 ? 16 * ((int)blockIdx.x >> 3) + ((int)blockIdx.x & 7) + 8 * g
+                              : (int)blockIdx.x;
+        const int chunk = v / (8 * a.NRG);
+        const int within = v - chunk * 8 * a.NRG;
+        const int hs = chunk * 8 + (within & 7);
+        if (hs >= a.Hkv * a.S) return it;
+        it.valid = true;
+        it.rg = within >> 3;
+        it.head = hs / a.S;
+        it.split = hs - it.head * a.S;
+        it.k0 = it.split * a.split_len;
+        int k1 = min(a.N, it.k0 + a.split_len);
+        if (CAUSAL) {
+            const int rho_last = min(a.R, (it.rg + 1) * NW * kRowTile) - 1;
+            k1 = min(k1, a.L + rho_last / a.G + 1);
+        }
+        it.k1 = max(k1, it.k0);
+        it.n_tiles = (it.k1 - it.k0 + KT - 1) / KT;
+        return it;
+    };
+    const Item me = item_of(grp);
+    const int n_other = NG == 2 ? item_of(1 - grp).n_tiles : 0;
+    const int head = me.head, split = me.split, rg = me.rg, k0 = me.k0, k1 = me.k1;
+
     const int rho = (rg * NW + wave) * kRowTile + l32;
-    const bool row_ok = rho < a.R;
+    const bool row_ok = me.valid && rho < a.R;
     const int t = row_ok ? rho / a.G : 0;
     const int g = row_ok ? rho - t * a.G : 0;
     const int flat = t * a.Hq + head * a.G + g;
-    const bool wave_active = (rg * NW + wave) * kRowTile < a.R;
-
-    // ---- key range of this work-group
-    const int k0 = split * a.split_len;
-    int k1 = min(a.N, k0 + a.split_len);
-    if (CAUSAL) {
-        const int rho_last = min(a.R, (rg + 1) * NW * kRowTile) - 1;
-        k1 = min(k1, a.L + rho_last / a.G + 1);
-    }
+    const bool wave_active = me.valid && (rg * NW + wave) * kRowTile < a.R;
     const int vis_from = min(k1, a.L);   // keys below this need no mask test
 
     // ---- prologue: per-row int8 quantization of Q.  Lane (l32, hl) holds
@@ -815,234 +848,237 @@ void attn_split_kernel(const AttnArgs a) {
     constexpr float kLazy = PV16 ? 0.0f : 8.0f;
     float m_run = -INFINITY;
     float l_run = 0.0f;
+    f16x8 pk[2];                          // the tile's P, from phase C to phase P
 
-    // Tile data is prefetched into registers AHEAD tiles ahead: with two
-    // register sets, tile i is stored to LDS from one while the other's loads
-    // (tile i + 1) are outstanding, and the freed set is refilled with tile
-    // i + 2 right after the store.  The 4-bit format, with fewer VALU
-    // operations per tile, gains from the deeper prefetch; the 3-bit format
-    // keeps one set (measured no faster with two, and its causal variant
-    // needs the registers).
-    constexpr int AHEAD = FMT == 1 ? 2 : 1;
-    TileIoOf<D, NT, FMT> io0, io1;
-    io0.load(a, head, k0, k0, k1, tid);
-    if constexpr (AHEAD == 2) io1.load(a, head, k0 + KT, k0, k1, tid);
-    if constexpr (FMT == 0) {
-        if (tid == 0) lds.wide_kb = -1;
-        __syncthreads();
-    }
+    // Tile data is prefetched into registers one tile ahead: phase U stores
+    // the held tile to LDS and issues the next tile's loads, which then have
+    // the rest of the tile's phases to arrive.
+    TileIoOf<D, NT, FMT> io;
+    io.load(a, head, k0, k0, k1, tid);
 
-    auto tile = [&](TileIoOf<D, NT, FMT> &io, int kb) {
-        io.store(lds, tid, min(KT, k1 - kb), kb);
-        __syncthreads();
-        io.load(a, head, kb + AHEAD * KT, k0, k1, tid);
-
-        if (wave_active) {
-            f32x16 acc = f32x16{};
-            const bool exact_int = FMT == 0 && __builtin_amdgcn_readfirstlane(lds.wide_kb) != kb;
-            if (exact_int) {
-                // ---- Q.K^T: one int8 MFMA per 32-element block; the block
-                // scales in integer form, so the key's logit is one int32
-                // sum (one v_mad_i32_i16 per block), converted and scaled
-                // once.  The MFMA of block b + 1 is issued before block b's
-                // sums read its results.
-                i32x16 iacc = i32x16{};
-                i32x16 s_cur = __builtin_amdgcn_mfma_i32_32x32x32_i8(
-                    *reinterpret_cast<const i32x4 *>(kq_lane),
-                    *reinterpret_cast<const i32x4 *>(q_lane), i32x16{}, 0, 0, 0);
+    // ---- phase C: Q.K^T, mask, online softmax of tile kb (P left in pk)
+    auto phase_c = [&](int kb) {
+        f32x16 acc = f32x16{};
+        const bool exact_int = FMT == 0 && __builtin_amdgcn_readfirstlane(lds.wide_kb) != kb;
+        if (exact_int) {
+            // ---- Q.K^T: one int8 MFMA per 32-element block; the block
+            // scales in integer form, so the key's logit is one int32
+            // sum (one v_mad_i32_i16 per block), converted and scaled
+            // once.  The MFMA of block b + 1 is issued before block b's
+            // sums read its results.
+            i32x16 iacc = i32x16{};
+            i32x16 s_cur = __builtin_amdgcn_mfma_i32_32x32x32_i8(
+                *reinterpret_cast<const i32x4 *>(kq_lane),
+                *reinterpret_cast<const i32x4 *>(q_lane), i32x16{}, 0, 0, 0);
 #pragma unroll
-                for (int b = 0; b < NB; ++b) {
-                    i32x16 s_next;
-                    if (b + 1 < NB)
-                        s_next = __builtin_amdgcn_mfma_i32_32x32x32_i8(
-                            *reinterpret_cast<const i32x4 *>(kq_lane + 32 * (b + 1)),
-                            *reinterpret_cast<const i32x4 *>(q_lane + 32 * (b + 1)), i32x16{}, 0, 0, 0);
-                    // M of keys 8hl + [0, 8) and 16 + 8hl + [0, 8), two per word
-                    const u32x4 m0 = *reinterpret_cast<const u32x4 *>(lds.skm + b * KT + 8 * hl);
-                    const u32x4 m1 = *reinterpret_cast<const u32x4 *>(lds.skm + b * KT + 16 + 8 * hl);
-                    const int32_t ready = mfma_ready(s_cur[0]);
+            for (int b = 0; b < NB; ++b) {
+                i32x16 s_next;
+                if (b + 1 < NB)
+                    s_next = __builtin_amdgcn_mfma_i32_32x32x32_i8(
+                        *reinterpret_cast<const i32x4 *>(kq_lane + 32 * (b + 1)),
+                        *reinterpret_cast<const i32x4 *>(q_lane + 32 * (b + 1)), i32x16{}, 0, 0, 0);
+                // M of keys 8hl + [0, 8) and 16 + 8hl + [0, 8), two per word
+                const u32x4 m0 = *reinterpret_cast<const u32x4 *>(lds.skm + b * KT + 8 * hl);
+                const u32x4 m1 = *reinterpret_cast<const u32x4 *>(lds.skm + b * KT + 16 + 8 * hl);
+                const int32_t ready = mfma_ready(s_cur[0]);
 #pragma unroll
-                    for (int r = 0; r < 8; r += 2) {
-                        iacc[r] = mad_i16<0>(s_cur[r], m0[r >> 1], iacc[r], ready);
-                        iacc[r + 1] = mad_i16<1>(s_cur[r + 1], m0[r >> 1], iacc[r + 1], ready);
-                        iacc[8 + r] = mad_i16<0>(s_cur[8 + r], m1[r >> 1], iacc[8 + r], ready);
-                        iacc[9 + r] = mad_i16<1>(s_cur[9 + r], m1[r >> 1], iacc[9 + r], ready);
-                    }
-                    if (DEBUG && a.dbg_logits && row_ok) {
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            const int key = kb + (r < 8 ? 8 * hl + r : 16 + 8 * hl + (r - 8));
-                            if (key < k1)
-                                a.dbg_logits[((size_t)flat * a.N + key) * NB + b] = s_cur[r];
-                        }
-                    }
-                    if (b + 1 < NB) s_cur = s_next;
+                for (int r = 0; r < 8; r += 2) {
+                    iacc[r] = mad_i16<0>(s_cur[r], m0[r >> 1], iacc[r], ready);
+                    iacc[r + 1] = mad_i16<1>(s_cur[r + 1], m0[r >> 1], iacc[r + 1], ready);
+                    iacc[8 + r] = mad_i16<0>(s_cur[8 + r], m1[r >> 1], iacc[8 + r], ready);
+                    iacc[9 + r] = mad_i16<1>(s_cur[9 + r], m1[r >> 1], iacc[9 + r], ready);
                 }
-                const f32x4 u0 = *reinterpret_cast<const f32x4 *>(lds.skf + 8 * hl);
-                const f32x4 u1 = *reinterpret_cast<const f32x4 *>(lds.skf + 8 * hl + 4);
-                const f32x4 u2 = *reinterpret_cast<const f32x4 *>(lds.skf + 16 + 8 * hl);
-                const f32x4 u3 = *reinterpret_cast<const f32x4 *>(lds.skf + 16 + 8 * hl + 4);
-                const float unit[16] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w,
-                                        u2.x, u2.y, u2.z, u2.w, u3.x, u3.y, u3.z, u3.w};
-#pragma unroll
-                for (int r = 0; r < 16; ++r) acc[r] = unit[r] * (float)iacc[r];
-            } else if constexpr (FMT == 0) {
-                // ---- the per-block fp32 epilogue, for tiles with a key
-                // whose scales have no exact integer form (rare: kept short,
-                // without the MFMA pipelining, to spare registers)
-#pragma unroll
-                for (int b = 0; b < NB; ++b) {
-                    const i32x16 s_cur = __builtin_amdgcn_mfma_i32_32x32x32_i8(
-                        *reinterpret_cast<const i32x4 *>(kq_lane + 32 * b),
-                        *reinterpret_cast<const i32x4 *>(q_lane + 32 * b), i32x16{}, 0, 0, 0);
-                    // fp16 scales of keys 8hl + [0, 8) and 16 + 8hl + [0, 8); the FMA
-                    // widens them in the instruction (v_fma_mix_f32)
-                    const f16x8 h0 = *reinterpret_cast<const f16x8 *>(lds.skh + b * KT + 8 * hl);
-                    const f16x8 h1 = *reinterpret_cast<const f16x8 *>(lds.skh + b * KT + 16 + 8 * hl);
-#pragma unroll
-                    for (int r = 0; r < 8; ++r) {
-                        acc[r] = fmaf((float)h0[r], (float)s_cur[r], acc[r]);
-                        acc[8 + r] = fmaf((float)h1[r], (float)s_cur[8 + r], acc[8 + r]);
-                    }
-                    if (DEBUG && a.dbg_logits && row_ok) {
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            const int key = kb + (r < 8 ? 8 * hl + r : 16 + 8 * hl + (r - 8));
-                            if (key < k1)
-                                a.dbg_logits[((size_t)flat * a.N + key) * NB + b] = s_cur[r];
-                        }
-                    }
-                }
-            } else {
-                // ---- 4-bit per-token-head: the int8 MFMAs of all blocks
-                // accumulate one int32 sum per (row, key), scaled once.
-                i32x16 s_acc = i32x16{};
-#pragma unroll
-                for (int b = 0; b < NB; ++b)
-                    s_acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(
-                        *reinterpret_cast<const i32x4 *>(kq_lane + 32 * b),
-                        *reinterpret_cast<const i32x4 *>(q_lane + 32 * b), s_acc, 0, 0, 0);
-                const f32x4 s0 = *reinterpret_cast<const f32x4 *>(lds.skf + 8 * hl);
-                const f32x4 s1 = *reinterpret_cast<const f32x4 *>(lds.skf + 8 * hl + 4);
-                const f32x4 s2 = *reinterpret_cast<const f32x4 *>(lds.skf + 16 + 8 * hl);
-                const f32x4 s3 = *reinterpret_cast<const f32x4 *>(lds.skf + 16 + 8 * hl + 4);
-                const float skr[16] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w,
-                                       s2.x, s2.y, s2.z, s2.w, s3.x, s3.y, s3.z, s3.w};
-#pragma unroll
-                for (int r = 0; r < 16; ++r) acc[r] = skr[r] * (float)s_acc[r];
                 if (DEBUG && a.dbg_logits && row_ok) {
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const int key = kb + (r < 8 ? 8 * hl + r : 16 + 8 * hl + (r - 8));
-                        if (key < k1) a.dbg_logits[(size_t)flat * a.N + key] = s_acc[r] >> 4;
+                        if (key < k1)
+                            a.dbg_logits[((size_t)flat * a.N + key) * NB + b] = s_cur[r];
+                    }
+                }
+                if (b + 1 < NB) s_cur = s_next;
+            }
+            const f32x4 u0 = *reinterpret_cast<const f32x4 *>(lds.skf + 8 * hl);
+            const f32x4 u1 = *reinterpret_cast<const f32x4 *>(lds.skf + 8 * hl + 4);
+            const f32x4 u2 = *reinterpret_cast<const f32x4 *>(lds.skf + 16 + 8 * hl);
+            const f32x4 u3 = *reinterpret_cast<const f32x4 *>(lds.skf + 16 + 8 * hl + 4);
+            const float unit[16] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w,
+                                    u2.x, u2.y, u2.z, u2.w, u3.x, u3.y, u3.z, u3.w};
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[r] = unit[r] * (float)iacc[r];
+        } else if constexpr (FMT == 0) {
+            // ---- the per-block fp32 epilogue, for tiles with a key
+            // whose scales have no exact integer form (rare: kept short,
+            // without the MFMA pipelining, to spare registers)
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                const i32x16 s_cur = __builtin_amdgcn_mfma_i32_32x32x32_i8(
+                    *reinterpret_cast<const i32x4 *>(kq_lane + 32 * b),
+                    *reinterpret_cast<const i32x4 *>(q_lane + 32 * b), i32x16{}, 0, 0, 0);
+                // fp16 scales of keys 8hl + [0, 8) and 16 + 8hl + [0, 8); the FMA
+                // widens them in the instruction (v_fma_mix_f32)
+                const f16x8 h0 = *reinterpret_cast<const f16x8 *>(lds.skh + b * KT + 8 * hl);
+                const f16x8 h1 = *reinterpret_cast<const f16x8 *>(lds.skh + b * KT + 16 + 8 * hl);
+#pragma unroll
+                for (int r = 0; r < 8; ++r) {
+                    acc[r] = fmaf((float)h0[r], (float)s_cur[r], acc[r]);
+                    acc[8 + r] = fmaf((float)h1[r], (float)s_cur[8 + r], acc[8 + r]);
+                }
+                if (DEBUG && a.dbg_logits && row_ok) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int key = kb + (r < 8 ? 8 * hl + r : 16 + 8 * hl + (r - 8));
+                        if (key < k1)
+                            a.dbg_logits[((size_t)flat * a.N + key) * NB + b] = s_cur[r];
                     }
                 }
             }
-
-            // ---- mask, online softmax in base 2.  c_row >= 0, so the row max
-            // of the scaled logits is c_row times the max of acc.
-            const bool masked = kb + KT > vis_from;
-            if (masked) {
+        } else {
+            // ---- 4-bit per-token-head: the int8 MFMAs of all blocks
+            // accumulate one int32 sum per (row, key), scaled once.
+            i32x16 s_acc = i32x16{};
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+                s_acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(
+                    *reinterpret_cast<const i32x4 *>(kq_lane + 32 * b),
+                    *reinterpret_cast<const i32x4 *>(q_lane + 32 * b), s_acc, 0, 0, 0);
+            const f32x4 s0 = *reinterpret_cast<const f32x4 *>(lds.skf + 8 * hl);
+            const f32x4 s1 = *reinterpret_cast<const f32x4 *>(lds.skf + 8 * hl + 4);
+            const f32x4 s2 = *reinterpret_cast<const f32x4 *>(lds.skf + 16 + 8 * hl);
+            const f32x4 s3 = *reinterpret_cast<const f32x4 *>(lds.skf + 16 + 8 * hl + 4);
+            const float skr[16] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w,
+                                   s2.x, s2.y, s2.z, s2.w, s3.x, s3.y, s3.z, s3.w};
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[r] = skr[r] * (float)s_acc[r];
+            if (DEBUG && a.dbg_logits && row_ok) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int key = kb + (r < 8 ? 8 * hl + r : 16 + 8 * hl + (r - 8));
-                    bool vis = key < k1;
-                    if (vis && key >= a.L) {
-                        const int u = key - a.L;
-                        vis = CAUSAL ? (u <= t) : (((mrow >> u) & 1ull) != 0ull);
-                    }
-                    if (!vis) acc[r] = -INFINITY;
+                    if (key < k1) a.dbg_logits[(size_t)flat * a.N + key] = s_acc[r] >> 4;
                 }
             }
-            float amax = acc[0];
+        }
+
+        // ---- mask, online softmax in base 2.  c_row >= 0, so the row max
+        // of the scaled logits is c_row times the max of acc.
+        const bool masked = kb + KT > vis_from;
+        if (masked) {
 #pragma unroll
-            for (int r = 1; r < 16; ++r) amax = fmaxf(amax, acc[r]);
-            amax = max_halves(amax);
-            // a row with c_row == 0 has all visible logits 0
-            const float tmax = amax == -INFINITY ? -INFINITY : amax * c_row;
-            const float m_new = tmax > m_run + kLazy ? tmax : m_run;
-            if (__any(m_new != m_run)) {
-                const float alpha = m_new != m_run ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
-                l_run *= alpha;
-                if constexpr (PV16) {
-#pragma unroll
-                    for (int dt = 0; dt < NB; ++dt)
-#pragma unroll
-                        for (int j = 0; j < 8; ++j)
-                            oh[dt][j] = __builtin_convertvector(
-                                __builtin_convertvector(oh[dt][j], f32x2) * alpha, f16x2);
-                } else {
-#pragma unroll
-                    for (int dt = 0; dt < NB; ++dt)
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+            for (int r = 0; r < 16; ++r) {
+                const int key = kb + (r < 8 ? 8 * hl + r : 16 + 8 * hl + (r - 8));
+                bool vis = key < k1;
+                if (vis && key >= a.L) {
+                    const int u = key - a.L;
+                    vis = CAUSAL ? (u <= t) : (((mrow >> u) & 1ull) != 0ull);
                 }
-                m_run = m_new;
+                if (!vis) acc[r] = -INFINITY;
             }
-            const float mm = m_run == -INFINITY ? 0.0f : m_run;
-            float p[16];
-            if (masked) {
+        }
+        float amax = acc[0];
 #pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    p[r] = acc[r] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(fmaf(acc[r], c_row, -mm));
-            } else {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(fmaf(acc[r], c_row, -mm));
-            }
-            // ---- P.V: B operand = P (lane = row, 8 keys), A operand = V^T rows.
-            // The row sum adds the same fp16 values the MFMA multiplies.
-            f16x8 pk[2];
-            float psum = 0.0f;
-            const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-                for (int e = 0; e < 8; e += 2) {
-                    const f16x2 h2 = __builtin_convertvector(f32x2{p[8 * ks + e], p[8 * ks + e + 1]}, f16x2);
-                    pk[ks][e] = h2.x;
-                    pk[ks][e + 1] = h2.y;
-                    psum = __builtin_amdgcn_fdot2(h2, ones, psum, false);
-                }
-            l_run += psum;
-            __builtin_amdgcn_s_setprio(1);
+        for (int r = 1; r < 16; ++r) amax = fmaxf(amax, acc[r]);
+        amax = max_halves(amax);
+        // a row with c_row == 0 has all visible logits 0
+        const float tmax = amax == -INFINITY ? -INFINITY : amax * c_row;
+        const float m_new = tmax > m_run + kLazy ? tmax : m_run;
+        if (__any(m_new != m_run)) {
+            const float alpha = m_new != m_run ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+            l_run *= alpha;
             if constexpr (PV16) {
-                // the tile's 32 keys in one fp32 product, then one fp16
-                // rounding and one fp16 add per accumulator
 #pragma unroll
-                for (int dt = 0; dt < NB; ++dt) {
-                    const _Float16 *vrow = vt_lane + (dt * 32) * L::VTS + dt * L::VBPAD;
-                    f32x16 tp = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                        *reinterpret_cast<const f16x8 *>(vrow), pk[0], f32x16{}, 0, 0, 0);
-                    tp = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                        *reinterpret_cast<const f16x8 *>(vrow + 16), pk[1], tp, 0, 0, 0);
+                for (int dt = 0; dt < NB; ++dt)
 #pragma unroll
                     for (int j = 0; j < 8; ++j)
-                        oh[dt][j] += __builtin_convertvector(f32x2{tp[2 * j], tp[2 * j + 1]}, f16x2);
-                }
+                        oh[dt][j] = __builtin_convertvector(
+                            __builtin_convertvector(oh[dt][j], f32x2) * alpha, f16x2);
             } else {
 #pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
+                for (int dt = 0; dt < NB; ++dt)
 #pragma unroll
-                    for (int dt = 0; dt < NB; ++dt) {
-                        const f16x8 vop = *reinterpret_cast<const f16x8 *>(
-                            vt_lane + (dt * 32) * L::VTS + dt * L::VBPAD + 16 * ks);
-                        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vop, pk[ks], oacc[dt], 0, 0, 0);
-                    }
+                    for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+            }
+            m_run = m_new;
+        }
+        const float mm = m_run == -INFINITY ? 0.0f : m_run;
+        float p[16];
+        if (masked) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                p[r] = acc[r] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(fmaf(acc[r], c_row, -mm));
+        } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(fmaf(acc[r], c_row, -mm));
+        }
+        // P for the B operand of P.V (lane = row, 8 keys per k-step); the
+        // row sum adds the same fp16 values the MFMA multiplies.
+        float psum = 0.0f;
+        const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) {
+                const f16x2 h2 = __builtin_convertvector(f32x2{p[8 * ks + e], p[8 * ks + e + 1]}, f16x2);
+                pk[ks][e] = h2.x;
+                pk[ks][e + 1] = h2.y;
+                psum = __builtin_amdgcn_fdot2(h2, ones, psum, false);
+            }
+        l_run += psum;
+    };
+
+    // ---- phase P: O += P.V over the tile (A operand = V^T rows)
+    auto phase_p = [&]() {
+        __builtin_amdgcn_s_setprio(1);
+        if constexpr (PV16) {
+            // the tile's 32 keys in one fp32 product, then one fp16
+            // rounding and one fp16 add per accumulator
+#pragma unroll
+            for (int dt = 0; dt < NB; ++dt) {
+                const _Float16 *vrow = vt_lane + (dt * 32) * L::VTS + dt * L::VBPAD;
+                f32x16 tp = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                    *reinterpret_cast<const f16x8 *>(vrow), pk[0], f32x16{}, 0, 0, 0);
+                tp = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                    *reinterpret_cast<const f16x8 *>(vrow + 16), pk[1], tp, 0, 0, 0);
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    oh[dt][j] += __builtin_convertvector(f32x2{tp[2 * j], tp[2 * j + 1]}, f16x2);
+            }
+        } else {
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+                for (int dt = 0; dt < NB; ++dt) {
+                    const f16x8 vop = *reinterpret_cast<const f16x8 *>(
+                        vt_lane + (dt * 32) * L::VTS + dt * L::VBPAD + 16 * ks);
+                    oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vop, pk[ks], oacc[dt], 0, 0, 0);
                 }
             }
-            __builtin_amdgcn_s_setprio(0);
         }
-        __syncthreads();
+        __builtin_amdgcn_s_setprio(0);
     };
-    if constexpr (AHEAD == 2) {
-        for (int kb = k0; kb < k1; kb += 2 * KT) {
-            tile(io0, kb);
-            if (kb + KT >= k1) break;
-            tile(io1, kb + KT);
-        }
-    } else {
-        for (int kb = k0; kb < k1; kb += KT) tile(io0, kb);
+
+    // ---- the tile loop: U, barrier, C, barrier (NG = 2 only), P, barrier.
+    // A barrier pairs with whichever barrier the other waves reach next, so
+    // group 1 takes one extra barrier before its first tile and runs one
+    // phase behind group 0 from then on; at the end each group takes the
+    // barriers the other group's remaining tiles still need, so every wave
+    // takes NPH * max(n) + NG - 1 barriers after the first.
+    constexpr int NPH = NG == 2 ? 3 : 2;
+    if constexpr (FMT == 0) {
+        if (tid == 0) lds.wide_kb = -1;
     }
+    __syncthreads();
+    if (NG == 2 && grp == 1) __syncthreads();
+    for (int kb = k0; kb < k1; kb += KT) {
+        io.store(lds, tid, min(KT, k1 - kb), kb);
+        io.load(a, head, kb + KT, k0, k1, tid);
+        __syncthreads();
+        if (wave_active) phase_c(kb);
+        if constexpr (NG == 2) __syncthreads();
+        if (wave_active) phase_p();
+        __syncthreads();
+    }
+    const int rest = NPH * (max(me.n_tiles, n_other) - me.n_tiles) + (NG == 2 && grp == 0 ? 1 : 0);
+    for (int i = 0; i < rest; ++i) __syncthreads();
 
     // ---- epilogue
     if (!wave_active) return;
@@ -1587,6 +1623,17 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_dec_kernel(const AttnArgs
     auto process = [&](TileRegs &r, int kb) {
         // ---- unpack the held tile into this wave's LDS region
         const int nk = min(KT, k1 - kb);
+        // P.V multiplies P by the V scales in fp16 (below).  With the lazy
+        // max, P reaches 2^kLazy = 256, so a V scale of 256 or more (fp16
+        // bits >= 0x5C00; sign-bit patterns count as large too) could carry
+        // the product past 65504.  A tile holding such a scale moves the
+        // running max to its own max, which bounds P by 1 and the product by
+        // the scale itself.  (Read here: the registers are refilled with a
+        // later tile right after the unpack.)
+        bool big_sv = false;
+#pragma unroll
+        for (int i = 0; i < (FMT == 1 ? 1 : PER); ++i) big_sv |= r.vs[i] >= (uint16_t)0x5C00u;
+        const float lazy = __any(big_sv) ? 0.0f : kLazy;
         wave_lds_sync();
         if constexpr (FMT == 1) {
 #pragma unroll
@@ -1712,7 +1759,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_dec_kernel(const AttnArgs
         amax = fmaxf(amax, __shfl_xor(amax, 16));
         amax = max_halves(amax);
         const float tmax = amax == -INFINITY ? -INFINITY : amax * c_row;
-        const float m_new = tmax > m_run + kLazy ? tmax : m_run;
+        const float m_new = tmax > m_run + lazy ? tmax : m_run;
         if (__any(m_new != m_run)) {
             const float alpha = m_new != m_run ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
             l_run *= alpha;
@@ -2077,11 +2124,22 @@ __global__ __launch_bounds__(kMergeMaxThreads) void merge_kernel(
     }
 }
 
+// Row groups per work-group.  Paired four-wave groups (NG = 2, items v and
+// v + 8 of each block of 16) measured slower than two independent
+// work-groups per CU on the 64-node tree over 262K (645 against 610 us; the
+// extra barrier per tile and each phase waiting for the slower group cost
+// more than the overlap of complementary phases gains), so every variant
+// runs one group; NG = 2 stays available to the template.
+template <int NW, bool DEBUG>
+constexpr int kGroups = 1;
+
 template <int D, int NW, bool CAUSAL, bool DEBUG, int FMT, bool PV16 = false>
 hipError_t launch_t(const AttnArgs &a, hipStream_t stream) {
-    const int grid = a.n_hs_pad * a.NRG;
-    hipLaunchKernelGGL((attn_split_kernel<D, NW, CAUSAL, DEBUG, FMT, PV16>), dim3(grid),
-                       dim3(NW * 64), 0, stream, a);
+    constexpr int NG = kGroups<NW, DEBUG>;
+    const int items = a.n_hs_pad * a.NRG;
+    const int grid = NG == 2 ? 8 * ((items + 15) / 16) : items;
+    hipLaunchKernelGGL((attn_split_kernel<D, NW, NG, CAUSAL, DEBUG, FMT, PV16>), dim3(grid),
+                       dim3(NG * NW * 64), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -2109,14 +2167,16 @@ hipError_t launch_nw(const AttnArgs &a, int NW, bool causal, bool debug, bool pv
     }
 }
 
+// Resident items (row groups of NW waves) per CU.
 template <int D, int NW, bool CAUSAL, int FMT>
 int occupancy_t() {
+    constexpr int NG = kGroups<NW, false>;
     int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &n, reinterpret_cast<const void *>(&attn_split_kernel<D, NW, CAUSAL, false, FMT, false>),
-            NW * 64, 0) != hipSuccess)
+            &n, reinterpret_cast<const void *>(&attn_split_kernel<D, NW, NG, CAUSAL, false, FMT, false>),
+            NG * NW * 64, 0) != hipSuccess)
         return 0;
-    return n;
+    return n * NG;
 }
 
 template <int D, int FMT>
