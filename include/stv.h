@@ -106,7 +106,7 @@ typedef struct stv_kv_layer {
 /* Description of the last failure on the calling thread ("" after success). */
 const char *stv_last_error(void);
 
-/* ABI version; bumped on any change of the interface.  Currently 4. */
+/* ABI version; bumped on any change of the interface.  Currently 5. */
 int32_t stv_abi_version(void);
 
 /*
@@ -213,6 +213,30 @@ int stv_verify_attention(const float *q, int32_t T, int32_t n_q_heads,
                          float softmax_scale, float *out, float *out_lse, void *workspace,
                          size_t workspace_bytes, int32_t n_splits, int32_t *dbg_logits,
                          int8_t *dbg_q, float *dbg_qscale, void *stream);
+
+/*
+ * stv_verify_attention_noalloc -- stv_verify_attention for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  The split partials go to a
+ * file-scope device array of the library, STV_NOALLOC_SCRATCH_BYTES (64 MiB)
+ * per GPU, held from the library's first such call on that GPU until the
+ * process ends; the call allocates nothing.  Every call on a GPU shares that
+ * GPU's array, which keeps the last call's contents: calls that overlap on
+ * one GPU (on different streams, or from different threads) race and give
+ * undefined results.  The caller still passes q, out and out_lse.
+ *   n_splits  0 = automatic, capped at the splits whose partials
+ *             (n_splits * T * n_q_heads * (head_dim + 1) * 4 bytes) fit the
+ *             array; an explicit count that does not fit is STV_EWORKSPACE
+ * Other arguments, results (bit for bit, at the same split count) and
+ * errors as for stv_verify_attention, without the debug outputs.
+ */
+#define STV_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int stv_verify_attention_noalloc(const float *q, int32_t T, int32_t n_q_heads,
+                                 const stv_kv_layer *kv, int32_t ctx_len,
+                                 const uint64_t *anc_mask, float softmax_scale, float *out,
+                                 float *out_lse, int32_t n_splits, void *stream);
+/* Bytes of the array above (STV_NOALLOC_SCRATCH_BYTES).  No HIP call. */
+size_t stv_noalloc_scratch_bytes(void);
 
 /*
  * stv_verify_attention_fp16acc -- stv_verify_attention with P.V accumulated

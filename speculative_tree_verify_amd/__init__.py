@@ -29,7 +29,8 @@ STV_EHIP = -5
 
 __all__ = [
     "StvError", "KVCache", "load_library", "kv_quant_pack", "attention_plan", "workspace_bytes",
-    "verify_attention", "verify_attention_fp16acc", "prefill_attention",
+    "verify_attention", "verify_attention_fp16acc", "verify_attention_noalloc",
+    "noalloc_scratch_bytes", "prefill_attention",
     "attention_partials", "context_plan", "context_partials", "split_merge", "tree_accept", "kv_commit", "lookup_plan",
     "lookup_draft", "STV_OK", "STV_EINVAL", "STV_EMASK", "STV_ECAPACITY", "STV_EWORKSPACE",
     "STV_EHIP", "STV_KV_3BIT", "STV_KV_4BIT_TOKEN",
@@ -55,7 +56,7 @@ _FORMATS = {"b3": STV_KV_3BIT, "i4": STV_KV_4BIT_TOKEN}
 
 
 _lib = None
-ABI_VERSION = 4      # the argument lists below follow this version of include/stv.h
+ABI_VERSION = 5      # the argument lists below follow this version of include/stv.h
 
 
 def load_library():
@@ -90,6 +91,11 @@ def load_library():
         lib.stv_verify_attention_fp16acc.argtypes = [P, i32, i32, ctypes.POINTER(_KVLayer), i32,
                                                      P, ctypes.c_float, P, P, P, ctypes.c_size_t,
                                                      i32, P]
+        lib.stv_verify_attention_noalloc.restype = ctypes.c_int
+        lib.stv_verify_attention_noalloc.argtypes = [P, i32, i32, ctypes.POINTER(_KVLayer), i32,
+                                                     P, ctypes.c_float, P, P, i32, P]
+        lib.stv_noalloc_scratch_bytes.restype = ctypes.c_size_t
+        lib.stv_noalloc_scratch_bytes.argtypes = []
         lib.stv_context_plan.restype = ctypes.c_int
         lib.stv_context_plan.argtypes = [i32, i32, i32, i32, i32, i32, i32,
                                          ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_size_t)]
@@ -338,6 +344,34 @@ def verify_attention_fp16acc(q, kv: KVCache, ctx_len: int, anc_mask, softmax_sca
     """verify_attention with P.V accumulated in fp16 (3-bit caches only)."""
     return _attention(q, kv, ctx_len, anc_mask, softmax_scale, out, out_lse, workspace,
                       n_splits, False, causal=False, fp16acc=True)
+
+
+def verify_attention_noalloc(q, kv: KVCache, ctx_len: int, anc_mask, softmax_scale=None,
+                             out=None, out_lse=None, n_splits: int = 0):
+    """verify_attention whose split partials go to the library's fixed
+    per-GPU scratch array (the call allocates nothing on the device; `out`
+    is allocated here only when the caller passes none).  Calls that overlap
+    on one GPU race on that array."""
+    torch = _torch()
+    T, hq, d = q.shape
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((T, hq, d), dtype=torch.float32, device=q.device)
+    m = np.ascontiguousarray(np.asarray(anc_mask, dtype=np.uint64))
+    if m.shape != (T,):
+        raise ValueError(f"anc_mask must have shape ({T},)")
+    layer = kv._layer()
+    _check(load_library().stv_verify_attention_noalloc(
+        _dev_ptr(q, torch.float32, "q"), T, hq, ctypes.byref(layer), ctx_len, m.ctypes.data,
+        float(softmax_scale), _dev_ptr(out, torch.float32, "out", (T, hq, d)),
+        _dev_ptr(out_lse, torch.float32, "out_lse", (T, hq)), n_splits, _stream(q.device)))
+    return out
+
+
+def noalloc_scratch_bytes() -> int:
+    """Bytes of the per-GPU array verify_attention_noalloc uses."""
+    return int(load_library().stv_noalloc_scratch_bytes())
 
 
 def prefill_attention(q, kv: KVCache, ctx_len: int, softmax_scale=None, out=None,

@@ -89,7 +89,8 @@ int attention_common(const float *q, int T, int Hq, const stv_kv_layer *kv, int 
                      const uint64_t *mask, bool causal, float scale, float *out, float *out_lse,
                      void *ws, size_t ws_bytes, int n_splits, int32_t *dbg_logits, int8_t *dbg_q,
                      float *dbg_qscale, void *stream, float *partials_o = nullptr,
-                     float *partials_lse = nullptr, bool pv16 = false, bool ctx_only = false) {
+                     float *partials_lse = nullptr, bool pv16 = false, bool ctx_only = false,
+                     bool noalloc = false) {
     const bool partials_only = partials_o != nullptr;
     if (!q || (!out && !partials_only)) return fail(STV_EINVAL, "q and out must not be NULL");
     if (partials_only && !partials_lse) return fail(STV_EINVAL, "part_lse must not be NULL");
@@ -116,8 +117,25 @@ int attention_common(const float *q, int T, int Hq, const stv_kv_layer *kv, int 
     const int fmt = kv->kv_format;
     if (pv16 && fmt != STV_KV_3BIT)
         return fail(STV_EINVAL, "fp16-accumulated P.V reads the 3-bit format only");
-    const stv::Plan plan =
-        stv::make_plan_keys(T, Hq, Hkv, D, L, causal, n_splits, fmt, ctx_only ? 0 : T);
+    stv::Plan plan = stv::make_plan_keys(T, Hq, Hkv, D, L, causal, n_splits, fmt, ctx_only ? 0 : T);
+    if (noalloc && plan.S > 1 && plan.ws_bytes > stv::kNoAllocScratchBytes) {
+        // the partials go to the library's fixed scratch: the automatic plan
+        // takes as many splits as it holds; an explicit count beyond that fails
+        const size_t per_split = (size_t)T * Hq * ((size_t)D + 1) * sizeof(float);
+        const long long fit = (long long)(stv::kNoAllocScratchBytes / per_split);
+        if (n_splits > 0)
+            return fail(STV_EWORKSPACE,
+                        "the no-alloc scratch (%zu bytes) holds at most %lld splits of this call "
+                        "(%d requested)", stv::kNoAllocScratchBytes, fit, n_splits);
+        plan = stv::make_plan_keys(T, Hq, Hkv, D, L, causal, fit > 1 ? (int)fit : 1, fmt,
+                                   ctx_only ? 0 : T);
+    }
+    if (noalloc && plan.S > 1) {
+        hipError_t e = hipSuccess;
+        ws = stv::noalloc_scratch(&e);
+        if (!ws) return fail(STV_EHIP, "no-alloc scratch unavailable: %s", hipGetErrorString(e));
+        ws_bytes = stv::kNoAllocScratchBytes;
+    }
     if (!partials_only && plan.S > 1 && (!ws || ws_bytes < plan.ws_bytes))
         return fail(STV_EWORKSPACE, "workspace of %zu bytes needed for %d splits (got %zu)",
                     plan.ws_bytes, plan.S, ws ? ws_bytes : (size_t)0);
@@ -288,7 +306,7 @@ extern "C" {
 
 const char *stv_last_error(void) { return g_err; }
 
-int32_t stv_abi_version(void) { return 4; }
+int32_t stv_abi_version(void) { return 5; }
 
 int stv_kv_quant_pack(const float *x, int32_t n_tok, int32_t pos0, int32_t which,
                       uint32_t *codes, uint16_t *scales, int32_t n_kv_heads, int32_t head_dim,
@@ -357,6 +375,17 @@ int stv_verify_attention(const float *q, int32_t T, int32_t n_q_heads, const stv
                             out_lse, workspace, workspace_bytes, n_splits, dbg_logits, dbg_q,
                             dbg_qscale, stream);
 }
+
+int stv_verify_attention_noalloc(const float *q, int32_t T, int32_t n_q_heads,
+                                 const stv_kv_layer *kv, int32_t ctx_len,
+                                 const uint64_t *anc_mask, float softmax_scale, float *out,
+                                 float *out_lse, int32_t n_splits, void *stream) {
+    return attention_common(q, T, n_q_heads, kv, ctx_len, anc_mask, false, softmax_scale, out,
+                            out_lse, nullptr, 0, n_splits, nullptr, nullptr, nullptr, stream,
+                            nullptr, nullptr, false, false, true);
+}
+
+size_t stv_noalloc_scratch_bytes(void) { return stv::kNoAllocScratchBytes; }
 
 int stv_verify_attention_fp16acc(const float *q, int32_t T, int32_t n_q_heads,
                                  const stv_kv_layer *kv, int32_t ctx_len,

@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "stv.h"
+
 namespace stv {
 
 constexpr int kKeyTile = 32;     // keys per tile: the M side of one 32x32 MFMA
@@ -80,6 +82,13 @@ hipError_t launch_attention_dec(const AttnArgs &a, int D, bool causal, bool debu
                                 int fmt, hipStream_t stream);
 hipError_t launch_attention_s16(const AttnArgs &a, int D, bool causal, bool debug, bool pv16,
                                 hipStream_t stream);   // 3-bit format
+// Bytes of the device array that holds the split partials of
+// stv_verify_attention_noalloc (one per device), and its device address for
+// the current device (resolved once per device; NULL with *err set when the
+// runtime cannot resolve it).
+constexpr size_t kNoAllocScratchBytes = STV_NOALLOC_SCRATCH_BYTES;
+void *noalloc_scratch(hipError_t *err);
+
 hipError_t launch_merge(const float *part_o, const float *part_lse, int S, int rows, int D,
                         float *out, float *out_lse, hipStream_t stream);
 hipError_t launch_kv_pack(const float *x, int n_tok, int pos0, uint32_t *codes,

@@ -25,6 +25,7 @@
 
 #include <math.h>
 
+#include <mutex>
 #include <type_traits>
 
 namespace stv {
@@ -2405,6 +2406,39 @@ hipError_t launch_kv_pack4(const float *x, int n_tok, int pos0, uint32_t *codes,
                        dim3(threads), 0, stream, x, n_tok, pos0, codes, scales, Hkv, D, cap, ng,
                        grp0, n_grp);
     return hipGetLastError();
+}
+
+// ------------------------------------------- scratch of the no-alloc entry
+
+// Split partials of stv_verify_attention_noalloc: a file-scope device array,
+// one per GPU the library runs on, held until the process ends.  In host
+// code `scratch` names a host-side stand-in, not device memory: its device
+// address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+void *noalloc_scratch(hipError_t *err) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void *ptr[kMaxDevices];
+    *err = hipSuccess;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        *err = e != hipSuccess ? e : hipErrorInvalidDevice;
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(mu);
+    if (!ptr[dev]) {
+        // with device `dev` current (hipGetDevice above): its own copy
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) {
+            *err = e != hipSuccess ? e : hipErrorInvalidSymbol;
+            return nullptr;
+        }
+        ptr[dev] = p;
+    }
+    return ptr[dev];
 }
 
 }  // namespace stv

@@ -46,7 +46,8 @@ def test_header_declares_the_four_operations():
                "stv_split_merge", "stv_attention_plan", "stv_last_error", "stv_abi_version",
                "stv_tree_accept", "stv_kv_commit", "stv_lookup_plan", "stv_lookup_draft",
                "stv_verify_attention_fp16acc", "stv_context_plan", "stv_context_partials",
-               "stv_workspace_bytes"):
+               "stv_workspace_bytes", "stv_verify_attention_noalloc",
+               "stv_noalloc_scratch_bytes"):
         assert op in names
 
 
@@ -57,10 +58,10 @@ def test_library_exports_every_declared_symbol(lib, stvmod):
     for name in _declared():
         assert name in exported, name
         assert hasattr(lib, name)
-    assert lib.stv_abi_version() == 4 == stvmod.ABI_VERSION
+    assert lib.stv_abi_version() == 5 == stvmod.ABI_VERSION
     # the header states the same version
     with open(os.path.join(ROOT, "include", "stv.h")) as f:
-        assert re.search(r"Currently 4\b", f.read())
+        assert re.search(r"Currently 5\b", f.read())
 
 
 def _layer(stvmod, hkv=4, d=256, cap=1000):
@@ -353,3 +354,22 @@ def test_product_path_refuses_to_run_without_the_library(stvmod, monkeypatch, tm
     monkeypatch.setattr(stvmod, "_lib", None)
     with pytest.raises(RuntimeError, match="not built"):
         stvmod.load_library()
+
+
+def test_noalloc_rejects_split_counts_beyond_its_scratch(lib, stvmod):
+    """The no-alloc entry point: an explicit split count whose partials do not
+    fit the library's scratch array fails with STV_EWORKSPACE on the host."""
+    assert lib.stv_noalloc_scratch_bytes() == 64 << 20
+    T, hq, d, L = 64, 24, 256, 262144
+    layer = _layer(stvmod, hkv=4, d=d, cap=L + T)
+    m = np.ascontiguousarray(synth.ancestor_masks(synth.chain_parents(T)))
+    per_split = T * hq * (d + 1) * 4
+    fit = (64 << 20) // per_split
+    rc = lib.stv_verify_attention_noalloc(FAKE, T, hq, ctypes.byref(layer), L, m.ctypes.data,
+                                          0.0625, FAKE, None, fit + 1, None)
+    assert rc == stvmod.STV_EWORKSPACE
+    assert b"no-alloc scratch" in lib.stv_last_error()
+    # the usual argument checks come first
+    rc = lib.stv_verify_attention_noalloc(FAKE, 65, hq, ctypes.byref(layer), L, None, 0.0625,
+                                          FAKE, None, 0, None)
+    assert rc == stvmod.STV_EINVAL
