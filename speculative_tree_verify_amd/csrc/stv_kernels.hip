@@ -1095,25 +1095,62 @@ void attn_split_kernel(const AttnArgs a) {
     const float l_tot = sum_halves(l_run);
     const float inv_l = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
     const float lse = l_tot > 0.0f ? (m_run + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
-    if (!row_ok) return;
     const size_t rows_total = (size_t)a.T * a.Hq;
     const bool partial = a.part_o != nullptr;
-    float *dst = partial ? a.part_o + (size_t)split * rows_total * D : a.out;
-    dst += (size_t)flat * D;
-#pragma unroll
-    for (int dt = 0; dt < NB; ++dt)
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-            const int d0 = dt * 32 + 8 * r4 + 4 * hl;
-            f32x4 v = {oacc[dt][4 * r4 + 0] * inv_l, oacc[dt][4 * r4 + 1] * inv_l,
-                       oacc[dt][4 * r4 + 2] * inv_l, oacc[dt][4 * r4 + 3] * inv_l};
-            *reinterpret_cast<f32x4 *>(dst + d0) = v;
-        }
-    if (hl == 0) {
+    float *const out_base = partial ? a.part_o + (size_t)split * rows_total * D : a.out;
+    if (row_ok && hl == 0) {
         if (partial)
             a.part_lse[(size_t)split * rows_total + flat] = lse;
         else if (a.out_lse)
             a.out_lse[flat] = lse;
+    }
+    // The output goes out through the wave's own Q slot in LDS (no longer
+    // read), one 32-column tile at a time: the MFMA layout gives a lane 16
+    // bytes of a row per store, while read back row-major, eight lanes write
+    // a row's whole 128-byte segment in one store instruction.  (head_dim
+    // 64, whose Q slot is too small, stores from the MFMA layout.)
+    constexpr int SS = 36;                     // staging row stride in floats (144 bytes)
+    if constexpr (SS * 4 <= L::KQS) {
+        float *stage = reinterpret_cast<float *>(qlds_g + (grp * NW + wave) * kRowTile * L::KQS);
+        const int rr = lane >> 3, cq = lane & 7;    // read-back: rows rr + 8j, columns 4cq..4cq+3
+        float *dst_row[4];
+        bool ok_row[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int rho_j = (rg * NW + wave) * kRowTile + rr + 8 * j;
+            ok_row[j] = rho_j < a.R;
+            const int t_j = ok_row[j] ? rho_j / a.G : 0;
+            const int g_j = ok_row[j] ? rho_j - t_j * a.G : 0;
+            dst_row[j] = out_base + (size_t)(t_j * a.Hq + head * a.G + g_j) * D + 4 * cq;
+        }
+#pragma unroll
+        for (int dt = 0; dt < NB; ++dt) {
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const f32x4 v = {oacc[dt][4 * r4 + 0] * inv_l, oacc[dt][4 * r4 + 1] * inv_l,
+                                 oacc[dt][4 * r4 + 2] * inv_l, oacc[dt][4 * r4 + 3] * inv_l};
+                *reinterpret_cast<f32x4 *>(stage + l32 * SS + 8 * r4 + 4 * hl) = v;
+            }
+            wave_lds_sync();
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const f32x4 v = *reinterpret_cast<const f32x4 *>(stage + (rr + 8 * j) * SS + 4 * cq);
+                if (ok_row[j]) *reinterpret_cast<f32x4 *>(dst_row[j] + dt * 32) = v;
+            }
+            wave_lds_sync();
+        }
+    } else {
+        if (!row_ok) return;
+        float *dst = out_base + (size_t)flat * D;
+#pragma unroll
+        for (int dt = 0; dt < NB; ++dt)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const int d0 = dt * 32 + 8 * r4 + 4 * hl;
+                const f32x4 v = {oacc[dt][4 * r4 + 0] * inv_l, oacc[dt][4 * r4 + 1] * inv_l,
+                                 oacc[dt][4 * r4 + 2] * inv_l, oacc[dt][4 * r4 + 3] * inv_l};
+                *reinterpret_cast<f32x4 *>(dst + d0) = v;
+            }
     }
 }
 
@@ -1955,15 +1992,18 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_dec_kernel(const AttnArgs
 
 // ---------------------------------------------------------------- merge
 
-// One work-group per output row.  The weights exp(lse_s - M) come from a
-// block-wide max and sum; then thread (g, c) accumulates column c over the
-// splits s = g, g + G, g + 2G, ... (four loads in flight), and the G partial
-// sums are added in order g = 0, 1, ... through LDS, so the result does not
+// One work-group per output row, or per (row, chunk of CC column groups of
+// four) when rows are few: then the row's partials stream through D / 4CC
+// CUs instead of one.  The weights exp(lse_s - M) come from a block-wide max
+// and sum; then thread (g, c) accumulates column group c over the splits
+// s = g, g + G, g + 2G, ... (four loads in flight), and the G partial sums
+// are added in order g = 0, 1, ... through LDS, so the result does not
 // depend on timing.  G grows with S so that few rows with many splits still
 // keep many loads in flight.
 constexpr int kMergeMaxThreads = 1024;
 constexpr int kMergeWeights = 1024;      // weights cached in LDS for s < this
 constexpr int kMergePre = 8;             // partial vectors a thread loads up front
+constexpr int kMergeChunkRows = 1024;    // fewer rows: a row's columns split over work-groups
 
 __device__ __forceinline__ float block_reduce(float v, float *red, bool is_max) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -2036,7 +2076,7 @@ __global__ __launch_bounds__(kMergeSmallThreads) void merge_small_kernel(
 
 __global__ __launch_bounds__(kMergeMaxThreads) void merge_kernel(
     const float *__restrict__ part_o, const float *__restrict__ part_lse, int S, int rows, int D,
-    int G, float *__restrict__ out, float *__restrict__ out_lse) {
+    int G, int CC, float *__restrict__ out, float *__restrict__ out_lse) {
     __shared__ float red[kMergeMaxThreads / 64];
     __shared__ float wgt[kMergeWeights];
     __shared__ f32x4 acc_lds[kMergeMaxThreads];
@@ -2047,11 +2087,12 @@ __global__ __launch_bounds__(kMergeMaxThreads) void merge_kernel(
     // Its first kMergePre partial vectors are loaded before the weights are
     // known, so their latency overlaps the two block reductions.
     const bool vec = (D & 3) == 0;
-    const int C = vec ? D / 4 : 1;
+    const int C = vec ? CC : 1;
     const int g = tid / C, c = tid - (tid / C) * C;
     const bool gv = vec && g < G;
+    const int c0 = vec ? (int)blockIdx.y * CC : 0;      // first column group of the chunk
     const size_t split_stride = (size_t)rows * D;
-    const float *col = part_o + (size_t)row * D + 4 * c;
+    const float *col = part_o + (size_t)row * D + 4 * (c0 + c);
     f32x4 pre[kMergePre];
 #pragma unroll
     for (int u = 0; u < kMergePre; ++u) {
@@ -2075,10 +2116,11 @@ __global__ __launch_bounds__(kMergeMaxThreads) void merge_kernel(
         }
     W = block_reduce(W, red, false);
     const float invW = W > 0.0f ? 1.0f / W : 0.0f;
-    if (out_lse && tid == 0) out_lse[row] = M == -INFINITY ? -INFINITY : M + logf(W);
+    if (out_lse && tid == 0 && blockIdx.y == 0) out_lse[row] = M == -INFINITY ? -INFINITY : M + logf(W);
     __syncthreads();
     if (M == -INFINITY) {
-        for (int d = tid; d < D; d += nt) out[(size_t)row * D + d] = 0.0f;
+        const int d_end = vec ? 4 * (c0 + CC) : D;
+        for (int d = 4 * c0 + tid; d < d_end; d += nt) out[(size_t)row * D + d] = 0.0f;
         return;
     }
     if (vec) {
@@ -2112,7 +2154,7 @@ __global__ __launch_bounds__(kMergeMaxThreads) void merge_kernel(
         if (g == 0) {
             f32x4 sum = acc_lds[c];
             for (int k = 1; k < G; ++k) sum += acc_lds[k * C + c];
-            *reinterpret_cast<f32x4 *>(out + (size_t)row * D + 4 * c) = sum * invW;
+            *reinterpret_cast<f32x4 *>(out + (size_t)row * D + 4 * (c0 + c)) = sum * invW;
         }
     } else {
         for (int d = tid; d < D; d += nt) {
@@ -2346,19 +2388,25 @@ hipError_t launch_merge(const float *part_o, const float *part_lse, int S, int r
                            out_lse);
         return hipGetLastError();
     }
-    // Vector path: C = D / 4 columns times G split groups, about eight
-    // splits per group (so many rows keep blocks small), at most 1024
-    // threads.  Scalar path (D % 4 != 0): 256 threads over the columns.
-    int G = 1, threads = 256;
+    // Vector path: C = D / 4 column groups times G split groups, about
+    // eight splits per group (so many rows keep blocks small), at most 1024
+    // threads.  Fewer rows than kMergeChunkRows: the columns split into
+    // chunks of 16 groups, one work-group each, with the same G (so the same
+    // order of the sums).  Scalar path (D % 4 != 0): 256 threads over the
+    // columns.
+    int G = 1, threads = 256, CC = 1, chunks = 1;
     if ((D & 3) == 0) {
         const int C = D / 4;
         G = (S + 7) / 8;
         if (G > kMergeMaxThreads / C) G = kMergeMaxThreads / C;
         if (G < 1) G = 1;
-        threads = ((C * G + 63) / 64) * 64;
+        CC = C;
+        if (rows < kMergeChunkRows && C % 16 == 0) CC = 16;
+        chunks = C / CC;
+        threads = ((CC * G + 63) / 64) * 64;
     }
-    hipLaunchKernelGGL(merge_kernel, dim3(rows), dim3(threads), 0, stream, part_o, part_lse, S,
-                       rows, D, G, out, out_lse);
+    hipLaunchKernelGGL(merge_kernel, dim3(rows, chunks), dim3(threads), 0, stream, part_o, part_lse,
+                       S, rows, D, G, CC, out, out_lse);
     return hipGetLastError();
 }
 
