@@ -142,7 +142,18 @@ int stv_kv_quant_pack(const float *x, int32_t n_tok, int32_t pos0, int32_t which
  *                 of context splits (the effective count may be lower: each
  *                 split covers a whole number of 32-key tiles)
  *   n_splits_out  [host] effective split count S
- *   workspace_bytes_out [host] bytes of workspace the call needs (0 when S = 1)
+ *   workspace_bytes_out [host] bytes of workspace the call needs (0 when S = 1):
+ *                 stv_workspace_bytes(T, n_q_heads, head_dim, S), except for
+ *                 a prefill call on the 3-bit format with eight or more groups
+ *                 of 128 query rows per KV head (T * n_q_heads / n_kv_heads >
+ *                 896).  There it adds, after the partials rounded up to 256
+ *                 bytes, one unpacked image of every 32-key tile per KV head
+ *                 (ceil((ctx_len + T) / 32) * n_kv_heads images, a whole number
+ *                 of KiB each: about 31 KiB at head_dim 256): the call then
+ *                 unpacks each tile once instead of once per row group.  A
+ *                 workspace that holds the partials only still works (every
+ *                 row group unpacks the tiles itself); the results are the
+ *                 same bit for bit.
  * Errors: STV_EINVAL, STV_ECAPACITY is not checked here (no capacity given).
  */
 int stv_attention_plan(int32_t T, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
@@ -156,8 +167,9 @@ int stv_attention_plan(int32_t T, int32_t n_q_heads, int32_t n_kv_heads, int32_t
  * i.e. S * T * n_q_heads * (head_dim + 1) * 4 bytes, or 0 when S = 1 (one
  * split writes the output directly).  Split-K with a merge of the partials:
  * elpis-lossless, "Trust base" (the split-K barrier); elpis, "Why fast" (the
- * prefill merge).  stv_attention_plan gives S (and this same size) for a
- * call whose split count the library chooses.
+ * prefill merge).  stv_attention_plan gives S (and this same size, plus
+ * tile images for a large 3-bit prefill chunk) for a call whose split count
+ * the library chooses.
  *   T, n_q_heads  query rows and heads of the call (T >= 1, n_q_heads >= 1)
  *   head_dim      64, 128 or 256
  *   n_splits      the call's effective split count S >= 1
@@ -260,7 +272,9 @@ int stv_verify_attention_fp16acc(const float *q, int32_t T, int32_t n_q_heads,
  * prefill int8 Q.K^T, the K/V double-buffered ring, the prefill merge): T
  * new rows, row t sees keys 0 .. ctx_len+t.  Arguments as for
  * stv_verify_attention without anc_mask; T may be any positive count with
- * T * n_q_heads < 2^31.
+ * T * n_q_heads < 2^31.  The workspace must hold the partials
+ * (stv_workspace_bytes); with the plan's full size (stv_attention_plan) a
+ * chunk of many row groups per KV head unpacks each tile once into it.
  * Errors: STV_EINVAL, STV_ECAPACITY, STV_EWORKSPACE, STV_EHIP.
  */
 int stv_prefill_attention(const float *q, int32_t T, int32_t n_q_heads,

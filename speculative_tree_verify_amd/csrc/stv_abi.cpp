@@ -118,7 +118,7 @@ int attention_common(const float *q, int T, int Hq, const stv_kv_layer *kv, int 
     if (pv16 && fmt != STV_KV_3BIT)
         return fail(STV_EINVAL, "fp16-accumulated P.V reads the 3-bit format only");
     stv::Plan plan = stv::make_plan_keys(T, Hq, Hkv, D, L, causal, n_splits, fmt, ctx_only ? 0 : T);
-    if (noalloc && plan.S > 1 && plan.ws_bytes > stv::kNoAllocScratchBytes) {
+    if (noalloc && plan.S > 1 && plan.part_bytes > stv::kNoAllocScratchBytes) {
         // the partials go to the library's fixed scratch: the automatic plan
         // takes as many splits as it holds; an explicit count beyond that fails
         const size_t per_split = (size_t)T * Hq * ((size_t)D + 1) * sizeof(float);
@@ -136,9 +136,9 @@ int attention_common(const float *q, int T, int Hq, const stv_kv_layer *kv, int 
         if (!ws) return fail(STV_EHIP, "no-alloc scratch unavailable: %s", hipGetErrorString(e));
         ws_bytes = stv::kNoAllocScratchBytes;
     }
-    if (!partials_only && plan.S > 1 && (!ws || ws_bytes < plan.ws_bytes))
+    if (!partials_only && plan.S > 1 && (!ws || ws_bytes < plan.part_bytes))
         return fail(STV_EWORKSPACE, "workspace of %zu bytes needed for %d splits (got %zu)",
-                    plan.ws_bytes, plan.S, ws ? ws_bytes : (size_t)0);
+                    plan.part_bytes, plan.S, ws ? ws_bytes : (size_t)0);
 
     stv::AttnArgs a;
     memset(&a, 0, sizeof a);
@@ -179,6 +179,15 @@ int attention_common(const float *q, int T, int Hq, const stv_kv_layer *kv, int 
 
     hipStream_t st = static_cast<hipStream_t>(stream);
     const bool debug = dbg_logits || dbg_q || dbg_qscale;
+    // tile images when the plan asks for them and the workspace holds them
+    // (otherwise every row group unpacks the tiles itself)
+    if (plan.pre && !debug && !partials_only && !noalloc && ws && ws_bytes >= plan.ws_bytes) {
+        unsigned char *img = static_cast<unsigned char *>(ws) + plan.img_offset;
+        a.img = img;
+        a.img_tiles = (a.N + kKeyTileC - 1) / kKeyTileC;
+        hipError_t e = stv::launch_tile_images(a, D, fmt, img, st);
+        if (e != hipSuccess) return fail(STV_EHIP, "tile image launch failed: %s", hipGetErrorString(e));
+    }
     hipError_t e = plan.dec   ? stv::launch_attention_dec(a, D, causal, debug, pv16, fmt, st)
                    : plan.s16 ? stv::launch_attention_s16(a, D, causal, debug, pv16, st)
                               : stv::launch_attention(a, D, plan.NW, causal, debug, fmt, pv16, st);
@@ -291,8 +300,15 @@ Plan make_plan_keys(int T, int Hq, int Hkv, int D, int L, bool causal, int n_spl
     p.split_len = (int)(tiles_per_split * kKeyTile);
     p.S = (int)S;
     const size_t rows = (size_t)T * Hq;
-    p.ws_bytes = p.S > 1 ? (size_t)p.S * rows * ((size_t)D + 1) * sizeof(float) : 0;
-    (void)D;
+    p.part_bytes = p.S > 1 ? (size_t)p.S * rows * ((size_t)D + 1) * sizeof(float) : 0;
+    // the causal chunk with many row groups: each tile unpacked once, into
+    // images after the partials (256-byte aligned)
+    // (3-bit format only: the 4-bit unpack is cheap enough that images
+    // measured no faster)
+    p.pre = causal && fmt == 0 && !p.dec && !p.s16 && p.NW == 4 && p.NRG >= kPreMinRowGroups;
+    p.img_offset = (p.part_bytes + 255) / 256 * 256;
+    p.ws_bytes = p.pre ? p.img_offset + (size_t)Hkv * (size_t)n_tiles * tile_image_bytes(D)
+                       : p.part_bytes;
     return p;
 }
 

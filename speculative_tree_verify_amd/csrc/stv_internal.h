@@ -32,6 +32,8 @@ struct AttnArgs {
     int32_t T, Hq, Hkv, G, cap, ngroups, L, N, R;
     int32_t S, split_len, NRG, n_hs_pad;
     float scale_log2;    // softmax_scale * log2(e)
+    const unsigned char *img;  // unpacked tile images [Hkv][img_tiles] (causal chunk), or NULL
+    int32_t img_tiles;         // ceil(N / 32): images per KV head
     uint64_t mask[64];   // verify only: ancestor masks of the tree rows
 };
 
@@ -55,8 +57,16 @@ struct Plan {
     int NRG;         // row groups per kv head
     int S;           // context splits
     int split_len;   // keys per split, a multiple of kKeyTile
-    size_t ws_bytes; // workspace for the partials
+    size_t ws_bytes; // workspace of the call: the partials, then the tile images when pre is set
+    size_t part_bytes;   // the partials alone (the least workspace the call accepts)
+    bool pre;            // the causal chunk with many row groups: unpack each tile once into
+                         // images in the workspace (used when the workspace holds them)
+    size_t img_offset;   // where the images start in the workspace
 };
+
+// Row groups per KV head from which a causal chunk unpacks its tiles once, in
+// a pre-pass, instead of in every row group.
+constexpr int kPreMinRowGroups = 8;
 
 // Work-groups of the attention kernels that fit on one CU at once, from the
 // runtime's occupancy calculator; 0 when no device answers.
@@ -89,6 +99,9 @@ hipError_t launch_attention_s16(const AttnArgs &a, int D, bool causal, bool debu
 constexpr size_t kNoAllocScratchBytes = STV_NOALLOC_SCRATCH_BYTES;
 void *noalloc_scratch(hipError_t *err);
 
+// The pre-pass: images of tiles 0 .. a.img_tiles - 1 of every KV head into img.
+hipError_t launch_tile_images(const AttnArgs &a, int D, int fmt, unsigned char *img, hipStream_t s);
+size_t tile_image_bytes(int D);
 hipError_t launch_merge(const float *part_o, const float *part_lse, int S, int rows, int D,
                         float *out, float *out_lse, hipStream_t stream);
 hipError_t launch_kv_pack(const float *x, int n_tok, int pos0, uint32_t *codes,

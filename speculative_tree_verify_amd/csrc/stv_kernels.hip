@@ -671,6 +671,79 @@ struct TileIo4 {
 template <int D, int NT, int FMT>
 using TileIoOf = typename std::conditional<FMT == 0, TileIo<D, NT, true>, TileIo4<D, NT>>::type;
 
+// ---- unpacked tile images (the causal chunk with many row groups).
+//
+// Every row group of a KV head unpacks the same tiles; with hundreds of row
+// groups per head (a prefill chunk) a pre-pass unpacks each tile once into
+// the workspace, laid out exactly as the 32-row kernel's LDS tile, and the
+// kernel copies images into LDS with direct buffer-to-LDS loads (no VGPRs,
+// no VALU).  An image is a K part (int8 K rows, K scales in fp32 unit, fp16
+// and integer form, the fp32-epilogue flag) and a V part (fp16 V^T), each
+// padded to whole 1 KiB chunks: one 16-byte load per lane moves one chunk.
+template <int D>
+struct PreLayout {
+    using L = TileLds<D>;
+    static constexpr int NB = D / 32;
+    static constexpr int KQ = 0;
+    static constexpr int SKF = kKeyTile * L::KQS;
+    static constexpr int SKH = SKF + 4 * kKeyTile;
+    static constexpr int SKM = SKH + 2 * NB * kKeyTile;
+    static constexpr int WIDE = SKM + 2 * NB * kKeyTile;
+    static constexpr int KP = (WIDE + 16 + 1023) / 1024 * 1024;
+    static constexpr int VT = KP;
+    static constexpr int VP = (2 * (D * L::VTS + NB * L::VBPAD) + 1023) / 1024 * 1024;
+    static constexpr int BYTES = KP + VP;
+    static_assert(L::KQS % 16 == 0 && (2 * NB * kKeyTile) % 16 == 0, "16-byte pieces");
+};
+
+template <int N>
+__device__ __forceinline__ void copy16(unsigned char *dst, const void *src, int tid, int nt) {
+    static_assert(N % 16 == 0, "whole 16-byte pieces");
+    const u32x4 *s = reinterpret_cast<const u32x4 *>(src);
+    u32x4 *d = reinterpret_cast<u32x4 *>(dst);
+    for (int i = tid; i < N / 16; i += nt) d[i] = s[i];
+}
+
+// Chunks wave, wave + NW, ... of NC 1 KiB chunks of an image from src into
+// LDS at dst, one 16-byte direct buffer-to-LDS load per lane and chunk.
+template <int NC, int NW>
+__device__ __forceinline__ void image_to_lds(const unsigned char *src, unsigned char *dst, int wave,
+                                             int lane) {
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<unsigned char *>(src), (short)0, NC * 1024, kBufWord3);
+    for (int c = wave; c < NC; c += NW)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            r, (__attribute__((address_space(3))) void *)(dst + 1024 * c), 16, 16 * lane, 1024 * c, 0, 0);
+}
+
+// A lane's direct-to-LDS loads have written LDS once its vector-memory count is 0.
+__device__ __forceinline__ void vmem_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// One work-group per (tile, KV head): the 32-row kernel's unpack into LDS,
+// then the tile's image out to img.  Keys at or past N read as zero.
+template <int D, int FMT>
+__global__ __launch_bounds__(256) void tile_image_kernel(const AttnArgs a, unsigned char *img) {
+    using L = TileLds<D>;
+    using PL = PreLayout<D>;
+    __shared__ __attribute__((aligned(16))) L t;
+    const int tid = threadIdx.x;
+    const int tile = blockIdx.x, head = blockIdx.y;
+    const int kb = tile * kKeyTile;
+    TileIoOf<D, 256, FMT> io;
+    io.load(a, head, kb, 0, a.N, tid);
+    if (tid == 0) t.wide_kb = -1;
+    __syncthreads();
+    io.store(t, tid, min(kKeyTile, a.N - kb), kb);
+    __syncthreads();
+    unsigned char *dst = img + ((size_t)head * a.img_tiles + tile) * PL::BYTES;
+    copy16<kKeyTile * L::KQS>(dst + PL::KQ, t.kq, tid, 256);
+    copy16<4 * kKeyTile>(dst + PL::SKF, t.skf, tid, 256);
+    copy16<2 * PL::NB * kKeyTile>(dst + PL::SKH, t.skh, tid, 256);
+    copy16<2 * PL::NB * kKeyTile>(dst + PL::SKM, t.skm, tid, 256);
+    copy16<2 * (D * L::VTS + PL::NB * L::VBPAD)>(dst + PL::VT, t.vt, tid, 256);
+    if (tid == 0) *reinterpret_cast<int *>(dst + PL::WIDE) = t.wide_kb;
+}
+
 // PV16 selects the fp16-accumulated P.V variant (3-bit, verify only): each
 // 32-key tile's P.V product still comes out of an fp32 MFMA, but it is
 // rounded to fp16 and added into fp16 accumulators, and the running max
@@ -687,14 +760,22 @@ using TileIoOf = typename std::conditional<FMT == 0, TileIo<D, NT, true>, TileIo
 // (Two independent work-groups per CU would drift into the same phase,
 // since each is held together by its own barriers.)  With NG = 1 the
 // phases C and P fuse and a tile takes two barriers.
-template <int D, int NW, int NG, bool CAUSAL, bool DEBUG, int FMT, bool PV16>
+template <int D, int NW, int NG, bool CAUSAL, bool DEBUG, int FMT, bool PV16, bool PRE = false>
 __global__ __launch_bounds__(NG * NW * 64) __attribute__((amdgpu_waves_per_eu(D == 256 && NG * NW > 1 && !DEBUG ? 2 : 1)))
 void attn_split_kernel(const AttnArgs a) {
     constexpr int NB = D / 32;
     constexpr int KT = kKeyTile;
     constexpr int NT = NW * 64;
     using L = TileLds<D>;
-    __shared__ __attribute__((aligned(16))) L lds_g[NG];
+    using PL = PreLayout<D>;
+    // the tile: TileLds, or with PRE the image layout in two arrays, the K
+    // part and the V part (distinct objects, so the compiler can tell the
+    // image loads into one from the reads of the other and does not wait
+    // for them)
+    constexpr int TSZ = PRE ? 16 : ((int)sizeof(L) + 15) / 16 * 16;
+    __shared__ __attribute__((aligned(16))) unsigned char tile_raw[NG * TSZ];
+    __shared__ __attribute__((aligned(16))) unsigned char kimg[PRE ? PL::KP : 16];
+    __shared__ __attribute__((aligned(16))) unsigned char vimg[PRE ? PL::VP : 16];
     // int8 Q of each wave's 32 rows, [NG][NW][32 rows][D + 16] bytes: read
     // back as the B operand of every Q.K^T MFMA, which keeps 32 VGPRs free
     // for double-buffering the MFMA results.
@@ -702,7 +783,14 @@ void attn_split_kernel(const AttnArgs a) {
 
     const int grp = NG == 2 ? __builtin_amdgcn_readfirstlane((int)threadIdx.x / NT) : 0;
     const int tid = threadIdx.x - grp * NT;
-    L &lds = lds_g[grp];
+    unsigned char *const tbase = tile_raw + grp * TSZ;
+    L &lds = *reinterpret_cast<L *>(tbase);
+    int8_t *const t_kq = PRE ? reinterpret_cast<int8_t *>(kimg + PL::KQ) : lds.kq;
+    _Float16 *const t_vt = PRE ? reinterpret_cast<_Float16 *>(vimg) : lds.vt;
+    float *const t_skf = PRE ? reinterpret_cast<float *>(kimg + PL::SKF) : lds.skf;
+    _Float16 *const t_skh = PRE ? reinterpret_cast<_Float16 *>(kimg + PL::SKH) : lds.skh;
+    uint16_t *const t_skm = PRE ? reinterpret_cast<uint16_t *>(kimg + PL::SKM) : lds.skm;
+    int *const t_wide = PRE ? reinterpret_cast<int *>(kimg + PL::WIDE) : &lds.wide_kb;
     int8_t *qlds = qlds_g + grp * NW * kRowTile * L::KQS;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -832,8 +920,8 @@ void attn_split_kernel(const AttnArgs a) {
     // are exactly the key runs the P.V MFMA wants from that lane.
     const int ai = l32 >> 3;
     const int krow = 16 * (ai >> 1) + 8 * ((l32 >> 2) & 1) + 4 * (ai & 1) + (l32 & 3);
-    const int8_t *kq_lane = lds.kq + krow * L::KQS + 16 * hl;
-    const _Float16 *vt_lane = lds.vt + l32 * L::VTS + 8 * hl;
+    const int8_t *kq_lane = t_kq + krow * L::KQS + 16 * hl;
+    const _Float16 *vt_lane = t_vt + l32 * L::VTS + 8 * hl;
 
     f32x16 oacc[NB];
 #pragma unroll
@@ -855,12 +943,12 @@ void attn_split_kernel(const AttnArgs a) {
     // the held tile to LDS and issues the next tile's loads, which then have
     // the rest of the tile's phases to arrive.
     TileIoOf<D, NT, FMT> io;
-    io.load(a, head, k0, k0, k1, tid);
+    if constexpr (!PRE) io.load(a, head, k0, k0, k1, tid);
 
     // ---- phase C: Q.K^T, mask, online softmax of tile kb (P left in pk)
     auto phase_c = [&](int kb) {
         f32x16 acc = f32x16{};
-        const bool exact_int = FMT == 0 && __builtin_amdgcn_readfirstlane(lds.wide_kb) != kb;
+        const bool exact_int = FMT == 0 && __builtin_amdgcn_readfirstlane(*t_wide) != kb;
         if (exact_int) {
             // ---- Q.K^T: one int8 MFMA per 32-element block; the block
             // scales in integer form, so the key's logit is one int32
@@ -879,8 +967,8 @@ void attn_split_kernel(const AttnArgs a) {
                         *reinterpret_cast<const i32x4 *>(kq_lane + 32 * (b + 1)),
                         *reinterpret_cast<const i32x4 *>(q_lane + 32 * (b + 1)), i32x16{}, 0, 0, 0);
                 // M of keys 8hl + [0, 8) and 16 + 8hl + [0, 8), two per word
-                const u32x4 m0 = *reinterpret_cast<const u32x4 *>(lds.skm + b * KT + 8 * hl);
-                const u32x4 m1 = *reinterpret_cast<const u32x4 *>(lds.skm + b * KT + 16 + 8 * hl);
+                const u32x4 m0 = *reinterpret_cast<const u32x4 *>(t_skm + b * KT + 8 * hl);
+                const u32x4 m1 = *reinterpret_cast<const u32x4 *>(t_skm + b * KT + 16 + 8 * hl);
                 const int32_t ready = mfma_ready(s_cur[0]);
 #pragma unroll
                 for (int r = 0; r < 8; r += 2) {
@@ -899,10 +987,10 @@ void attn_split_kernel(const AttnArgs a) {
                 }
                 if (b + 1 < NB) s_cur = s_next;
             }
-            const f32x4 u0 = *reinterpret_cast<const f32x4 *>(lds.skf + 8 * hl);
-            const f32x4 u1 = *reinterpret_cast<const f32x4 *>(lds.skf + 8 * hl + 4);
-            const f32x4 u2 = *reinterpret_cast<const f32x4 *>(lds.skf + 16 + 8 * hl);
-            const f32x4 u3 = *reinterpret_cast<const f32x4 *>(lds.skf + 16 + 8 * hl + 4);
+            const f32x4 u0 = *reinterpret_cast<const f32x4 *>(t_skf + 8 * hl);
+            const f32x4 u1 = *reinterpret_cast<const f32x4 *>(t_skf + 8 * hl + 4);
+            const f32x4 u2 = *reinterpret_cast<const f32x4 *>(t_skf + 16 + 8 * hl);
+            const f32x4 u3 = *reinterpret_cast<const f32x4 *>(t_skf + 16 + 8 * hl + 4);
             const float unit[16] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w,
                                     u2.x, u2.y, u2.z, u2.w, u3.x, u3.y, u3.z, u3.w};
 #pragma unroll
@@ -918,8 +1006,8 @@ void attn_split_kernel(const AttnArgs a) {
                     *reinterpret_cast<const i32x4 *>(q_lane + 32 * b), i32x16{}, 0, 0, 0);
                 // fp16 scales of keys 8hl + [0, 8) and 16 + 8hl + [0, 8); the FMA
                 // widens them in the instruction (v_fma_mix_f32)
-                const f16x8 h0 = *reinterpret_cast<const f16x8 *>(lds.skh + b * KT + 8 * hl);
-                const f16x8 h1 = *reinterpret_cast<const f16x8 *>(lds.skh + b * KT + 16 + 8 * hl);
+                const f16x8 h0 = *reinterpret_cast<const f16x8 *>(t_skh + b * KT + 8 * hl);
+                const f16x8 h1 = *reinterpret_cast<const f16x8 *>(t_skh + b * KT + 16 + 8 * hl);
 #pragma unroll
                 for (int r = 0; r < 8; ++r) {
                     acc[r] = fmaf((float)h0[r], (float)s_cur[r], acc[r]);
@@ -943,10 +1031,10 @@ void attn_split_kernel(const AttnArgs a) {
                 s_acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(
                     *reinterpret_cast<const i32x4 *>(kq_lane + 32 * b),
                     *reinterpret_cast<const i32x4 *>(q_lane + 32 * b), s_acc, 0, 0, 0);
-            const f32x4 s0 = *reinterpret_cast<const f32x4 *>(lds.skf + 8 * hl);
-            const f32x4 s1 = *reinterpret_cast<const f32x4 *>(lds.skf + 8 * hl + 4);
-            const f32x4 s2 = *reinterpret_cast<const f32x4 *>(lds.skf + 16 + 8 * hl);
-            const f32x4 s3 = *reinterpret_cast<const f32x4 *>(lds.skf + 16 + 8 * hl + 4);
+            const f32x4 s0 = *reinterpret_cast<const f32x4 *>(t_skf + 8 * hl);
+            const f32x4 s1 = *reinterpret_cast<const f32x4 *>(t_skf + 8 * hl + 4);
+            const f32x4 s2 = *reinterpret_cast<const f32x4 *>(t_skf + 16 + 8 * hl);
+            const f32x4 s3 = *reinterpret_cast<const f32x4 *>(t_skf + 16 + 8 * hl + 4);
             const float skr[16] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w,
                                    s2.x, s2.y, s2.z, s2.w, s3.x, s3.y, s3.z, s3.w};
 #pragma unroll
@@ -1063,23 +1151,51 @@ void attn_split_kernel(const AttnArgs a) {
     // phase behind group 0 from then on; at the end each group takes the
     // barriers the other group's remaining tiles still need, so every wave
     // takes NPH * max(n) + NG - 1 barriers after the first.
-    constexpr int NPH = NG == 2 ? 3 : 2;
-    if constexpr (FMT == 0) {
-        if (tid == 0) lds.wide_kb = -1;
-    }
-    __syncthreads();
-    if (NG == 2 && grp == 1) __syncthreads();
-    for (int kb = k0; kb < k1; kb += KT) {
-        io.store(lds, tid, min(KT, k1 - kb), kb);
-        io.load(a, head, kb + KT, k0, k1, tid);
+    if constexpr (PRE) {
+        // ---- tiles from their images: the K part of tile i + 1 streams into
+        // LDS during tile i's P.V, the V part during tile i + 1's Q.K^T; each
+        // wave moves every NW-th 1 KiB chunk (one 16-byte load per lane).
+        static_assert(NG == 1, "images feed one group per work-group");
+        const int wv = __builtin_amdgcn_readfirstlane(wave);
+        auto copy_img = [&](int kb, bool kpart, bool vpart) {
+            const unsigned char *src =
+                a.img + ((size_t)head * a.img_tiles + (size_t)(kb / KT)) * PL::BYTES;
+            if (kpart) image_to_lds<PL::KP / 1024, NW>(src, kimg, wv, lane);
+            if (vpart) image_to_lds<PL::VP / 1024, NW>(src + PL::KP, vimg, wv, lane);
+        };
+        if (me.n_tiles > 0) copy_img(k0, true, true);
+        vmem_wait();
         __syncthreads();
-        if (wave_active) phase_c(kb);
-        if constexpr (NG == 2) __syncthreads();
-        if (wave_active) phase_p();
+        for (int kb = k0; kb < k1; kb += KT) {
+            const bool more = kb + KT < k1;
+            if (wave_active) phase_c(kb);
+            vmem_wait();
+            __syncthreads();
+            if (more) copy_img(kb + KT, true, false);
+            if (wave_active) phase_p();
+            vmem_wait();
+            __syncthreads();
+            if (more) copy_img(kb + KT, false, true);
+        }
+    } else {
+        constexpr int NPH = NG == 2 ? 3 : 2;
+        if constexpr (FMT == 0) {
+            if (tid == 0) lds.wide_kb = -1;
+        }
         __syncthreads();
+        if (NG == 2 && grp == 1) __syncthreads();
+        for (int kb = k0; kb < k1; kb += KT) {
+            io.store(lds, tid, min(KT, k1 - kb), kb);
+            io.load(a, head, kb + KT, k0, k1, tid);
+            __syncthreads();
+            if (wave_active) phase_c(kb);
+            if constexpr (NG == 2) __syncthreads();
+            if (wave_active) phase_p();
+            __syncthreads();
+        }
+        const int rest = NPH * (max(me.n_tiles, n_other) - me.n_tiles) + (NG == 2 && grp == 0 ? 1 : 0);
+        for (int i = 0; i < rest; ++i) __syncthreads();
     }
-    const int rest = NPH * (max(me.n_tiles, n_other) - me.n_tiles) + (NG == 2 && grp == 0 ? 1 : 0);
-    for (int i = 0; i < rest; ++i) __syncthreads();
 
     // ---- epilogue
     if (!wave_active) return;
@@ -2176,12 +2292,12 @@ __global__ __launch_bounds__(kMergeMaxThreads) void merge_kernel(
 template <int NW, bool DEBUG>
 constexpr int kGroups = 1;
 
-template <int D, int NW, bool CAUSAL, bool DEBUG, int FMT, bool PV16 = false>
+template <int D, int NW, bool CAUSAL, bool DEBUG, int FMT, bool PV16 = false, bool PRE = false>
 hipError_t launch_t(const AttnArgs &a, hipStream_t stream) {
     constexpr int NG = kGroups<NW, DEBUG>;
     const int items = a.n_hs_pad * a.NRG;
     const int grid = NG == 2 ? 8 * ((items + 15) / 16) : items;
-    hipLaunchKernelGGL((attn_split_kernel<D, NW, NG, CAUSAL, DEBUG, FMT, PV16>), dim3(grid),
+    hipLaunchKernelGGL((attn_split_kernel<D, NW, NG, CAUSAL, DEBUG, FMT, PV16, PRE>), dim3(grid),
                        dim3(NG * NW * 64), 0, stream, a);
     return hipGetLastError();
 }
@@ -2195,8 +2311,14 @@ hipError_t launch_d(const AttnArgs &a, bool causal, bool debug, bool pv16, hipSt
         }
         return hipErrorInvalidValue;
     }
-    if (causal)
+    if (causal) {
+        if constexpr (NW == 4 && FMT == 0) {
+            // the causal chunk reading tile images (a.img set by the caller)
+            if (a.img && !debug) return launch_t<D, NW, true, false, FMT, false, true>(a, s);
+        }
         return debug ? launch_t<D, NW, true, true, FMT>(a, s) : launch_t<D, NW, true, false, FMT>(a, s);
+    }
+    if (a.img) return hipErrorInvalidValue;
     return debug ? launch_t<D, NW, false, true, FMT>(a, s) : launch_t<D, NW, false, false, FMT>(a, s);
 }
 
@@ -2357,6 +2479,33 @@ int attention_wgs_per_cu(int D, int NW, bool causal, int fmt) {
         case 128: return occupancy_d<128, 0>(NW, causal);
         case 256: return occupancy_d<256, 0>(NW, causal);
         default: return 0;
+    }
+}
+
+size_t tile_image_bytes(int D) {
+    switch (D) {
+        case 64: return PreLayout<64>::BYTES;
+        case 128: return PreLayout<128>::BYTES;
+        case 256: return PreLayout<256>::BYTES;
+        default: return 0;
+    }
+}
+
+template <int D, int FMT>
+hipError_t launch_img_t(const AttnArgs &a, unsigned char *img, hipStream_t s) {
+    hipLaunchKernelGGL((tile_image_kernel<D, FMT>), dim3(a.img_tiles, a.Hkv), dim3(256), 0, s, a, img);
+    return hipGetLastError();
+}
+
+// (3-bit format only)
+hipError_t launch_tile_images(const AttnArgs &a, int D, int fmt, unsigned char *img, hipStream_t s) {
+    if (a.img_tiles <= 0) return hipSuccess;
+    if (fmt != 0) return hipErrorInvalidValue;
+    switch (D) {
+        case 64: return launch_img_t<64, 0>(a, img, s);
+        case 128: return launch_img_t<128, 0>(a, img, s);
+        case 256: return launch_img_t<256, 0>(a, img, s);
+        default: return hipErrorInvalidValue;
     }
 }
 

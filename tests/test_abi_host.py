@@ -326,8 +326,16 @@ def test_plan_is_consistent(stvmod, T, hq, hkv, d, L, causal, fmt):
         assert 1 <= S <= n_tiles
         if req:
             assert S <= req
-        assert ws == (S * T * hq * (d + 1) * 4 if S > 1 else 0)
-        assert ws == stvmod.workspace_bytes(T, hq, d, S)
+        part = S * T * hq * (d + 1) * 4 if S > 1 else 0
+        assert part == stvmod.workspace_bytes(T, hq, d, S)
+        if causal and fmt == "b3" and -(-T * (hq // hkv) // 32) > 28:
+            # eight or more groups of 128 rows per KV head: the workspace also
+            # holds one unpacked image per tile and KV head, after the partials
+            img = ws - -(-part // 256) * 256
+            assert img > 0 and img % (hkv * n_tiles) == 0
+            assert (img // (hkv * n_tiles)) % 1024 == 0
+        else:
+            assert ws == part
         # the documented split layout covers every key, each split non-empty
         P = 32 * -(-n_tiles // S)
         assert (S - 1) * P < L + T <= S * P

@@ -163,7 +163,7 @@ def _f16_bits(x):
     return np.asarray(x, dtype=np.float16).view(np.uint16)
 
 
-@pytest.mark.parametrize("kind,T", [("tree", 64), ("prefill", 40)])
+@pytest.mark.parametrize("kind,T", [("tree", 64), ("prefill", 40), ("prefill", 200)])
 def test_k_scale_exponent_spread(gpu, orc, kind, T):
     """Keys whose fp16 block scales span more than three binades, or hold
     zeros and subnormals, next to ordinary keys in one call.  For more than
@@ -197,7 +197,7 @@ def test_k_scale_exponent_spread(gpu, orc, kind, T):
     run_case(gpu, orc, hq, hkv, d, L, T, kind, 153, host=host, scale_mul=16.0)
 
 
-@pytest.mark.parametrize("kind,T", [("tree", 64), ("prefill", 40)])
+@pytest.mark.parametrize("kind,T", [("tree", 64), ("prefill", 40), ("prefill", 200)])
 def test_k_scale_integer_sum_bound(gpu, orc, kind, T):
     """The largest sums the integer-scale path can meet.  Rows whose Q
     elements are all equal quantize to int8 +-127; keys with every code 0
@@ -221,6 +221,51 @@ def test_k_scale_integer_sum_bound(gpu, orc, kind, T):
         host.k_scales[:, j] = scales
     # logits of the heavy keys near +-6 for the equal-element rows
     run_case(gpu, orc, hq, hkv, d, L, T, kind, 156, host=host, q=q, scale_mul=1.6e-6)
+
+
+IMAGE_CASES = [
+    # Hq, Hkv, D, L, T, fmt, n_splits: eight or more groups of 128 rows per
+    # KV head, where the causal chunk unpacks each tile once into images
+    (24, 4, 256, 1500, 200, "b3", 0),
+    (24, 4, 256, 333, 180, "b3", 3),
+    (8, 1, 128, 700, 130, "b3", 0),
+    (8, 2, 64, 901, 260, "b3", 2),
+]
+
+
+@pytest.mark.parametrize("hq,hkv,d,L,T,fmt,ns", IMAGE_CASES,
+                         ids=[f"d{c[2]}_{c[5]}_T{c[4]}_S{c[6]}" for c in IMAGE_CASES])
+def test_prefill_tile_images(gpu, orc, hq, hkv, d, L, T, fmt, ns):
+    """The causal chunk with many row groups: a pre-pass unpacks each tile
+    once into the workspace and the kernel copies the images into LDS.  The
+    result equals, bit for bit, the same call whose workspace holds only the
+    partials (each row group unpacking the tiles itself), and matches the
+    oracle on sampled rows, at every head_dim.  (The 4-bit format unpacks
+    in the kernel: its plan asks for no image space.)"""
+    stv, torch = gpu
+    rng = np.random.default_rng(170 + d + T)
+    host = synth.make_kv(rng, hkv, d, L + T, L + T + 5)
+    S4, ws4 = stv.attention_plan(T, hq, hkv, d, L, True, ns, "i4")
+    assert ws4 == stv.workspace_bytes(T, hq, d, S4)
+    q = synth.make_q(rng, T, hq, d)
+    S, ws_full = stv.attention_plan(T, hq, hkv, d, L, True, ns, fmt)
+    part = stv.workspace_bytes(T, hq, d, S)
+    assert ws_full > part, "the plan asks for image space"
+    kv = stv.KVCache.from_host(host)
+    qd = torch.from_numpy(q).cuda()
+    lse_a = torch.empty((T, hq), dtype=torch.float32, device="cuda")
+    lse_b = torch.empty((T, hq), dtype=torch.float32, device="cuda")
+    out_a = stv.prefill_attention(qd, kv, L, out_lse=lse_a, n_splits=ns)
+    small = torch.empty(max(part, 16), dtype=torch.uint8, device="cuda")
+    out_b = stv.prefill_attention(qd, kv, L, out_lse=lse_b, n_splits=ns, workspace=small)
+    torch.cuda.synchronize()
+    assert torch.equal(out_a, out_b) and torch.equal(lse_a, lse_b)
+    rows = np.unique(np.concatenate([[0, T * hq - 1], rng.integers(0, T * hq, 40)]))
+    ref = orc.attention(q, host, L, None, 1.0 / math.sqrt(d), rows=rows)
+    got = out_a.reshape(T * hq, d)[torch.from_numpy(rows).cuda()].cpu().numpy()
+    assert _row_err(got, ref["out"]).max() <= TOL
+    lg = lse_a.reshape(-1)[torch.from_numpy(rows).cuda()].cpu().numpy()
+    assert np.max(np.abs(lg - ref["lse"])) <= TOL
 
 
 def test_residue_sweep(gpu, orc):
