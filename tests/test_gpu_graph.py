@@ -82,3 +82,44 @@ def test_graph_replays_match_eager(gpu, name, hq, hkv, d, L, T, fmt):
         again = eager(qs[(i + 1) % 3])
         torch.cuda.synchronize()
         assert torch.equal(again[0], ref[(i + 1) % 3][0])
+
+
+def test_graph_replays_prefill_with_tile_images(gpu):
+    """A prefill chunk large enough for tile images (the pre-pass, the
+    attention kernel reading images, the merge) captured and replayed."""
+    stv, torch = gpu
+    hq, hkv, d, L, T = 24, 4, 256, 1000, 200
+    rng = np.random.default_rng(410)
+    kv = stv.KVCache.from_host(synth.make_kv(rng, hkv, d, L + T))
+    scale = 1.0 / math.sqrt(d)
+    qs = [torch.from_numpy(synth.make_q(rng, T, hq, d)).cuda() for _ in range(3)]
+    S, ws_bytes = stv.attention_plan(T, hq, hkv, d, L, True, 0, "b3")
+    assert ws_bytes > stv.workspace_bytes(T, hq, d, S), "the plan uses tile images"
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    q_static = qs[0].clone()
+    out_static = torch.empty((T, hq, d), dtype=torch.float32, device="cuda")
+    lse_static = torch.empty((T, hq), dtype=torch.float32, device="cuda")
+
+    def eager(q):
+        lse = torch.empty((T, hq), dtype=torch.float32, device="cuda")
+        o = stv.prefill_attention(q, kv, L, scale, out_lse=lse, workspace=ws)
+        return o.clone(), lse.clone()
+
+    ref = [eager(q) for q in qs]
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            stv.prefill_attention(q_static, kv, L, scale, out=out_static, out_lse=lse_static,
+                                  workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for rep in range(6):
+        i = rep % 3
+        q_static.copy_(qs[i])
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out_static, ref[i][0]), f"replay {rep} differs from eager"
+        assert torch.equal(lse_static, ref[i][1])

@@ -230,11 +230,12 @@ IMAGE_CASES = [
     (24, 4, 256, 333, 180, "b3", 3),
     (8, 1, 128, 700, 130, "b3", 0),
     (8, 2, 64, 901, 260, "b3", 2),
+    (24, 4, 256, 0, 200, "b3", 0),          # no context keys: early row groups see few tiles
 ]
 
 
 @pytest.mark.parametrize("hq,hkv,d,L,T,fmt,ns", IMAGE_CASES,
-                         ids=[f"d{c[2]}_{c[5]}_T{c[4]}_S{c[6]}" for c in IMAGE_CASES])
+                         ids=[f"d{c[2]}_L{c[3]}_T{c[4]}_S{c[6]}" for c in IMAGE_CASES])
 def test_prefill_tile_images(gpu, orc, hq, hkv, d, L, T, fmt, ns):
     """The causal chunk with many row groups: a pre-pass unpacks each tile
     once into the workspace and the kernel copies the images into LDS.  The
