@@ -72,6 +72,20 @@ def measured_traffic(kernel: str, workload: str):
         return None
 
 
+def attention_kernel_of(geom: synth.Geometry, fmt: str, causal: bool) -> str:
+    """The attention kernel the library's plan runs for a workload (the same
+    row-count thresholds as the plan)."""
+    rows = geom.n_rows * (geom.n_q_heads // geom.n_kv_heads)
+    if rows <= (64 if fmt == "i4" else 16):
+        return "attn_dec_kernel"
+    if fmt == "b3" and rows <= 64:
+        return "attn_split16_kernel"
+    row_tiles = (rows + 31) // 32
+    if fmt == "b3" and not causal and geom.head_dim == 256 and row_tiles >= 4:
+        return "attn_ws_kernel"
+    return "attn_split_kernel"
+
+
 def work_of(geom: synth.Geometry, masks, fmt: str = "b3"):
     """Algorithmic bytes and operations of one step (see the design notes)."""
     T, hq, hkv, d, L = geom.n_rows, geom.n_q_heads, geom.n_kv_heads, geom.head_dim, geom.ctx_len
@@ -420,9 +434,7 @@ def main():
     total_ops = w["qk_ops"] + w["pv_ops"]
     blended_peak = total_ops / (w["qk_ops"] / INT8_PEAK_TOPS + w["pv_ops"] / FP16_PEAK_TFLOPS)
     achieved = total_ops / (s["attn_kernel_us"] * 1e-6) / 1e12
-    rows_per_kv_head = g.n_rows * (g.n_q_heads // g.n_kv_heads)
-    kernel_name = ("attn_dec_kernel" if rows_per_kv_head <= 16 and wl.fmt == "b3"
-                   else "attn_split_kernel")
+    kernel_name = attention_kernel_of(g, wl.fmt, wl.causal)
     line = {
         "metric": METRIC,
         "value": round(w["step_bytes"] / (s["ms_per_step"] * 1e-3) / 1e9, 2),

@@ -204,8 +204,9 @@ int attention_common(const float *q, int T, int Hq, const stv_kv_layer *kv, int 
 namespace stv {
 
 long long attention_slots(int D, int NW, bool causal, int kind, int fmt) {
-    // MI355X: 256 CUs; the D = 256 four-wave kernels hold two work-groups per CU.
-    constexpr long long kFallback = 256LL * 2;
+    // MI355X: 256 CUs; the D = 256 four-wave kernels hold two work-groups per
+    // CU, the wave-specialized kernel one.
+    const long long kFallback = kind == 3 ? 256LL : 256LL * 2;
     struct Entry {
         int dev, D, NW;
         bool causal;
@@ -232,6 +233,7 @@ long long attention_slots(int D, int NW, bool causal, int kind, int fmt) {
     }
     const int per_cu = kind == 1   ? attention_dec_wgs_per_cu(D, causal, fmt)
                        : kind == 2 ? attention_s16_wgs_per_cu(D, causal)
+                       : kind == 3 ? attention_ws_wgs_per_cu(D)
                                    : attention_wgs_per_cu(D, NW, causal, fmt);
     const long long slots = per_cu > 0 ? (long long)cus * per_cu : kFallback;
     cache.push_back({dev, D, NW, causal, kind, fmt, slots});
@@ -248,6 +250,7 @@ Plan make_plan_keys(int T, int Hq, int Hkv, int D, int L, bool causal, int n_spl
     // the few-row kernel: up to 16 rows per KV head (3-bit), 64 (4-bit)
     p.dec = R <= (fmt == 1 ? kDecMaxRows4 : kDecMaxRows);
     p.s16 = !p.dec && R <= kS16MaxRows && fmt == 0;
+    p.ws = false;
     if (p.dec) {
         p.NW = 4;
         p.NRG = (int)((R + 15) / 16);
@@ -258,12 +261,39 @@ Plan make_plan_keys(int T, int Hq, int Hkv, int D, int L, bool causal, int n_spl
         const long long row_tiles = (R + kRowTile - 1) / kRowTile;
         p.NW = row_tiles >= 4 ? 4 : (row_tiles >= 2 ? 2 : 1);
         p.NRG = (int)((row_tiles + p.NW - 1) / p.NW);
+        p.ws = !causal && fmt == 0 && p.NW == 4 && D == 256;
     }
     const long long N = (long long)L + n_after;
     const long long n_tiles = (N + kKeyTile - 1) / kKeyTile;
     long long S;
     if (n_splits_req > 0) {
         S = n_splits_req;
+    } else if (p.ws) {
+        // The wave-specialized kernel holds one work-group per CU, and
+        // work-group i runs on XCD i mod 8 with the row groups of one (head,
+        // split) on one XCD: the fullest XCD sets the number of rounds.  Pick
+        // the split count (up to three rounds' worth) that keeps the largest
+        // share of the slots busy over those rounds; a larger count must gain
+        // more than 2% (each split adds partials for the merge to read).
+        const long long slots = attention_slots(D, p.NW, causal, 3, fmt);
+        const long long groups = (long long)Hkv * p.NRG;
+        const long long xcds = slots % 8 == 0 ? 8 : 1;
+        const long long per_xcd = slots / xcds;
+        const long long max_s = n_tiles / 4 > 0 ? n_tiles / 4 : 1;
+        long long s_hi = 3 * slots / groups;
+        if (s_hi > max_s) s_hi = max_s;
+        if (s_hi < 1) s_hi = 1;
+        S = 1;
+        double best = -1.0;
+        for (long long s = 1; s <= s_hi; ++s) {
+            const long long fullest = p.NRG * ((Hkv * s + xcds - 1) / xcds);
+            const long long rounds = (fullest + per_xcd - 1) / per_xcd;
+            const double busy = (double)(groups * s) / (double)(rounds * slots);
+            if (busy > best * 1.02) {
+                best = busy;
+                S = s;
+            }
+        }
     } else {
         // Fill the device's resident work-group slots exactly once: one
         // round of equal work-groups, no straggling partial round.  Splits

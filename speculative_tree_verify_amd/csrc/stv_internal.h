@@ -50,9 +50,14 @@ constexpr int kDecMaxRows4 = 64;
 // 4-bit format above kDecMaxRows4, the 32-row tile kernel.
 constexpr int kS16MaxRows = 64;
 
+// The wave-specialized 32-row kernel (3-bit verify rows at head_dim 256, four
+// row tiles per work-group): twelve waves, one work-group per CU.
+constexpr int kWsThreads = 768;
+
 struct Plan {
     bool dec;        // few-row kernel (then NW = 4 waves and NRG groups of 16 rows)
     bool s16;        // 16-row shared-tile kernel (then NW = 4 waves and NRG groups of 64 rows)
+    bool ws;         // wave-specialized 32-row kernel (3-bit, head_dim 256, NW = 4, verify rows)
     int NW;          // waves (32-row tiles) per work-group
     int NRG;         // row groups per kv head
     int S;           // context splits
@@ -75,10 +80,12 @@ constexpr int kPreMinRowGroups = 8;
 int attention_wgs_per_cu(int D, int NW, bool causal, int fmt);
 int attention_dec_wgs_per_cu(int D, bool causal, int fmt);
 int attention_s16_wgs_per_cu(int D, bool causal);     // 3-bit format
+int attention_ws_wgs_per_cu(int D);                   // 3-bit format, verify rows
 
 // Resident work-group slots of the current device for a kernel variant
 // (CUs x work-groups per CU); a fixed MI355X figure when no device answers.
-// kind: 0 = 32-row tile kernel, 1 = few-row kernel, 2 = 16-row shared-tile kernel.
+// kind: 0 = 32-row tile kernel, 1 = few-row kernel, 2 = 16-row shared-tile kernel,
+// 3 = wave-specialized 32-row kernel.
 long long attention_slots(int D, int NW, bool causal, int kind, int fmt);
 
 Plan make_plan(int T, int Hq, int Hkv, int D, int L, bool causal, int n_splits_req, int fmt);

@@ -415,6 +415,73 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// One K item (key kk, block b) of a tile into LDS: the int8 values c - 4 of
+// its 32 codes (row stride KQS bytes; S16: the 16-row kernel's shifted rows),
+// its fp16 scale, and with INT_SCALES the integer form of the key's scales
+// (M of the block; the key's unit, from the item with b == 0).  kb: the
+// tile's first key, written to *wide when the key has no exact integer scale
+// form.  The NB items of a key sit on NB consecutive lanes, all present or all
+// absent (min_over_blocks).
+template <int NB, int KQS, bool INT_SCALES, bool S16>
+__device__ __forceinline__ void unpack_k_item(const KItem &it, int kk, int b, int8_t *kq,
+                                              _Float16 *skh, uint16_t *skm, float *skf, int *wide,
+                                              int kb) {
+    uint32_t o[8];
+    unpack_bytes(it.w[0], it.w[1], it.w[2], o);
+    if constexpr (S16) {
+        // 8-byte pieces: the row shift keeps them 8-byte aligned only
+        int8_t *row = kq + kk * KQS + 8 * (kk & 3) + 32 * b;
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            *reinterpret_cast<u32x2 *>(row + 8 * c) =
+                u32x2{codes_to_i8(o[2 * c]), codes_to_i8(o[2 * c + 1])};
+    } else {
+        const u32x4 lo = {codes_to_i8(o[0]), codes_to_i8(o[1]), codes_to_i8(o[2]), codes_to_i8(o[3])};
+        const u32x4 hi = {codes_to_i8(o[4]), codes_to_i8(o[5]), codes_to_i8(o[6]), codes_to_i8(o[7])};
+        *reinterpret_cast<u32x4 *>(kq + kk * KQS + 32 * b) = lo;
+        *reinterpret_cast<u32x4 *>(kq + kk * KQS + 32 * b + 16) = hi;
+    }
+    skh[b * kKeyTile + kk] = __builtin_bit_cast(_Float16, it.s);
+    if constexpr (INT_SCALES) {
+        const ScaleInt si = scale_int(it.s);
+        const uint32_t emin = min_over_blocks<NB>(si.e);
+        const uint32_t shift = si.e - emin;      // 0 .. 30 (zero scales: M = 0)
+        skm[b * kKeyTile + kk] = (uint16_t)(shift <= kScaleMaxShift ? si.m << shift : 0u);
+        if (b == 0) skf[kk] = scale_unit(emin);
+        if (si.special || (si.m != 0u && shift > kScaleMaxShift)) *wide = kb;
+    }
+}
+
+// Element row d of a tile's V side into LDS as fp16 V^ = s * (c - 4), keys in
+// order (row stride VTS halves, plus VBPAD per 32-row block; S16: 16-byte
+// chunks swizzled by row).  svs: the tile's V scales [D/32][32 keys], written
+// by the same wave and made visible by a wave-local sync.
+template <int VTS, int VBPAD, bool S16>
+__device__ __forceinline__ void unpack_v_row(const VItem &it, int d, _Float16 *vt,
+                                             const uint16_t *svs) {
+    uint32_t o[8];
+    unpack_bytes(it.w[0], it.w[1], it.w[2], o);   // keys 4qq..4qq+3 in o[qq]
+    const uint32_t *sv32 = reinterpret_cast<const uint32_t *>(svs + (d & ~31));
+    uint32_t row[16];
+#pragma unroll
+    for (int qq = 0; qq < 8; ++qq) {
+        // Byte-select table lookup: code c -> high byte of the binary16
+        // value c - 4 (whose low byte is zero).
+        const uint32_t tt = __builtin_amdgcn_perm(kC4Hi, kC4Lo, o[qq]);
+        const uint32_t p01 = __builtin_amdgcn_perm(tt, tt, 0x010C000Cu);
+        const uint32_t p23 = __builtin_amdgcn_perm(tt, tt, 0x030C020Cu);
+        const f16x2 v01 = __builtin_bit_cast(f16x2, p01) * __builtin_bit_cast(f16x2, sv32[2 * qq]);
+        const f16x2 v23 = __builtin_bit_cast(f16x2, p23) * __builtin_bit_cast(f16x2, sv32[2 * qq + 1]);
+        row[2 * qq] = __builtin_bit_cast(uint32_t, v01);
+        row[2 * qq + 1] = __builtin_bit_cast(uint32_t, v23);
+    }
+    u32x4 *dst = reinterpret_cast<u32x4 *>(vt + d * VTS + (d / 32) * VBPAD);
+    const int sw = S16 ? (d >> 1) & 3 : 0;      // chunk swizzle of the S16 layout
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        dst[j ^ sw] = u32x4{row[4 * j], row[4 * j + 1], row[4 * j + 2], row[4 * j + 3]};
+}
+
 // INT_SCALES: also stage the K scales in integer form (the 32-row kernel's
 // epilogue); the 16-row kernel, whose unpack sits between two barriers on
 // its critical path, uses the fp16 scales only.
@@ -477,35 +544,9 @@ struct TileIo {
 #pragma unroll
         for (int i = 0; i < KPT; ++i) {
             const int item = tid + i * NT;
-            if (item < KI) {
-                const int kk = item / NB, b = item % NB;
-                uint32_t o[8];
-                unpack_bytes(k[i].w[0], k[i].w[1], k[i].w[2], o);
-                if constexpr (S16) {
-                    // 8-byte pieces: the row shift keeps them 8-byte aligned only
-                    int8_t *row = t.kq + kk * L::KQS + 8 * (kk & 3) + 32 * b;
-#pragma unroll
-                    for (int c = 0; c < 4; ++c)
-                        *reinterpret_cast<u32x2 *>(row + 8 * c) =
-                            u32x2{codes_to_i8(o[2 * c]), codes_to_i8(o[2 * c + 1])};
-                } else {
-                    const u32x4 lo = {codes_to_i8(o[0]), codes_to_i8(o[1]), codes_to_i8(o[2]),
-                                      codes_to_i8(o[3])};
-                    const u32x4 hi = {codes_to_i8(o[4]), codes_to_i8(o[5]), codes_to_i8(o[6]),
-                                      codes_to_i8(o[7])};
-                    *reinterpret_cast<u32x4 *>(t.kq + kk * L::KQS + 32 * b) = lo;
-                    *reinterpret_cast<u32x4 *>(t.kq + kk * L::KQS + 32 * b + 16) = hi;
-                }
-                t.skh[b * kKeyTile + kk] = __builtin_bit_cast(_Float16, k[i].s);
-                if constexpr (INT_SCALES) {
-                    const ScaleInt si = scale_int(k[i].s);
-                    const uint32_t emin = min_over_blocks<NB>(si.e);
-                    const uint32_t shift = si.e - emin;      // 0 .. 30 (zero scales: M = 0)
-                    t.skm[b * kKeyTile + kk] = (uint16_t)(shift <= kScaleMaxShift ? si.m << shift : 0u);
-                    if (b == 0) t.skf[kk] = scale_unit(emin);
-                    if (si.special || (si.m != 0u && shift > kScaleMaxShift)) t.wide_kb = kb;
-                }
-            }
+            if (item < KI)
+                unpack_k_item<NB, L::KQS, INT_SCALES, S16>(k[i], item / NB, item % NB, t.kq, t.skh,
+                                                           t.skm, t.skf, &t.wide_kb, kb);
         }
         // V scales: every wave stages the entries its own rows need; keys
         // past the range get scale 0, so their V^ is exactly 0.
@@ -518,32 +559,7 @@ struct TileIo {
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
             const int d = tid + i * NT;
-            if (d < VI) {
-                const VItem &it = v[i];
-                uint32_t o[8];
-                unpack_bytes(it.w[0], it.w[1], it.w[2], o);   // keys 4qq..4qq+3 in o[qq]
-                const uint32_t *sv32 = reinterpret_cast<const uint32_t *>(t.svs + (d & ~31));
-                uint32_t row[16];
-#pragma unroll
-                for (int qq = 0; qq < 8; ++qq) {
-                    // Byte-select table lookup: code c -> high byte of the
-                    // binary16 value c - 4 (whose low byte is zero).
-                    const uint32_t tt = __builtin_amdgcn_perm(kC4Hi, kC4Lo, o[qq]);
-                    const uint32_t p01 = __builtin_amdgcn_perm(tt, tt, 0x010C000Cu);
-                    const uint32_t p23 = __builtin_amdgcn_perm(tt, tt, 0x030C020Cu);
-                    const f16x2 v01 = __builtin_bit_cast(f16x2, p01) *
-                                      __builtin_bit_cast(f16x2, sv32[2 * qq]);
-                    const f16x2 v23 = __builtin_bit_cast(f16x2, p23) *
-                                      __builtin_bit_cast(f16x2, sv32[2 * qq + 1]);
-                    row[2 * qq] = __builtin_bit_cast(uint32_t, v01);
-                    row[2 * qq + 1] = __builtin_bit_cast(uint32_t, v23);
-                }
-                u32x4 *dst = reinterpret_cast<u32x4 *>(t.vt + d * L::VTS + (d / 32) * L::VBPAD);
-                const int sw = S16 ? (d >> 1) & 3 : 0;      // chunk swizzle of the S16 layout
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    dst[j ^ sw] = u32x4{row[4 * j], row[4 * j + 1], row[4 * j + 2], row[4 * j + 3]};
-            }
+            if (d < VI) unpack_v_row<L::VTS, L::VBPAD, S16>(v[i], d, t.vt, t.svs);
         }
     }
 };
@@ -1267,6 +1283,499 @@ void attn_split_kernel(const AttnArgs a) {
                                  oacc[dt][4 * r4 + 2] * inv_l, oacc[dt][4 * r4 + 3] * inv_l};
                 *reinterpret_cast<f32x4 *>(dst + d0) = v;
             }
+    }
+}
+
+// ------------------------------------------ attention, 32-row tiles, wave-specialized
+//
+// The 32-row tile kernel's work for the 3-bit format at head_dim 256, split by
+// role over three waves per row tile (four row tiles, 128 rows, per work-group of
+// twelve waves):
+//   score waves 0-3 (row tile w): Q in registers, Q.K^T with the integer
+//     block-scale epilogue, the mask and the online softmax; they hand P (fp16,
+//     in the P.V operand layout) and the step's row rescale to the output waves
+//     through LDS;
+//   output waves 4-11 (row tile (w - 4) mod 4, half (w - 4) / 4 of D): P.V into
+//     32 rows x D/2 fp32 accumulators, and the unpack -- waves 4-7 the K items of
+//     the next tile, waves 8-11 the V rows of the current one.
+// K, V and P are double-buffered in LDS, so one step (Q.K^T of tile j, P.V of
+// tile j - 1, the unpack of K of tile j + 1 and of V of tile j) ends at one
+// barrier.  The score waves' chain is the step's critical path; the output
+// waves' MFMAs and unpack run beside it (wave w sits on SIMD w mod 4, so a SIMD
+// holds one row tile's three waves).  No wave holds both Q and accumulators, or
+// more than 32 x D/2 accumulators, so three waves fit per SIMD.  Raw code words
+// are fetched three tiles ahead into registers.
+template <int D>
+struct WsLds {
+    using L = TileLds<D>;
+    static constexpr int NB = D / 32;
+    static constexpr int NRT = 4;        // row tiles per work-group
+    struct KBuf {
+        int8_t kq[kKeyTile * L::KQS];
+        float skf[kKeyTile];
+        alignas(16) _Float16 skh[NB * kKeyTile];
+        alignas(16) uint16_t skm[NB * kKeyTile];
+        int wide_kb;
+    };
+    struct VBuf {
+        _Float16 vt[D * L::VTS + NB * L::VBPAD];
+        alignas(16) uint16_t svs[D];
+    };
+    struct PBuf {
+        f16x8 p[2][64];          // [k-step][lane]: the score wave's P.V operand registers
+        float alpha[kRowTile];   // the step's row rescale (when rescale is set)
+        int rescale;
+    };
+    alignas(16) KBuf k[2];
+    alignas(16) VBuf v[2];
+    alignas(16) PBuf p[2][NRT];  // [buffer][row tile]
+};
+
+template <int D, bool CAUSAL, bool DEBUG>
+__global__ __launch_bounds__(kWsThreads) __attribute__((amdgpu_waves_per_eu(3, 3)))
+void attn_ws_kernel(const AttnArgs a) {
+    constexpr int NB = D / 32;
+    constexpr int KT = kKeyTile;
+    using L = TileLds<D>;
+    using W = WsLds<D>;
+    constexpr int NRT = W::NRT;
+    constexpr int NH = NB / 2;               // 32-column d-tiles of an output wave
+    __shared__ __attribute__((aligned(16))) W sh;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int hl = lane >> 5;
+    const int l32 = lane & 31;
+    const bool score = wave < NRT;
+    const int rt = score ? wave : (wave - NRT) % NRT;
+    const int dh = score ? 0 : (wave - NRT) / NRT;
+
+    // ---- work item (kv head, split, row group), mapped as in the 32-row kernel
+    const int vid = blockIdx.x;
+    const int chunk = vid / (8 * a.NRG);
+    const int within = vid - chunk * 8 * a.NRG;
+    const int hs = chunk * 8 + (within & 7);
+    if (hs >= a.Hkv * a.S) return;
+    const int rg = within >> 3;
+    const int head = hs / a.S;
+    const int split = hs - head * a.S;
+    const int k0 = split * a.split_len;
+    int k1 = min(a.N, k0 + a.split_len);
+    if (CAUSAL) {
+        const int rho_last = min(a.R, (rg + 1) * NRT * kRowTile) - 1;
+        k1 = min(k1, a.L + rho_last / a.G + 1);
+    }
+    k1 = max(k1, k0);
+    const int n_tiles = (k1 - k0 + KT - 1) / KT;
+
+    const int rho = (rg * NRT + rt) * kRowTile + l32;
+    const bool row_ok = rho < a.R;
+    const int t = row_ok ? rho / a.G : 0;
+    const int g = row_ok ? rho - t * a.G : 0;
+    const int flat = t * a.Hq + head * a.G + g;
+    const bool tile_active = (rg * NRT + rt) * kRowTile < a.R;
+    const size_t rows_total = (size_t)a.T * a.Hq;
+    const bool partial = a.part_o != nullptr;
+
+    if (score) {
+        __builtin_amdgcn_s_setprio(1);
+        // ---- Q row l32 of the row tile to int8 with one fp32 scale; lane
+        // (l32, hl) holds elements 32b + 16hl + [0, 16) of every block b (the B
+        // operand of the 32x32x32 int8 MFMA)
+        i32x4 qreg[NB];
+        float sq = 0.0f;
+        {
+            const float *qrow = a.q + (size_t)flat * D + 16 * hl;
+            float amax = 0.0f;
+            if (row_ok) {
+#pragma unroll
+                for (int b = 0; b < NB; ++b)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const f32x4 v = *reinterpret_cast<const f32x4 *>(qrow + 32 * b + 4 * j);
+                        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+                    }
+            }
+            amax = fmaxf(amax, __shfl_xor(amax, 32));
+            const float inv = amax > 0.0f ? 127.0f / amax : 0.0f;
+            sq = amax / 127.0f;
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    uint32_t word = 0;
+                    if (row_ok) {
+                        const f32x4 v = *reinterpret_cast<const f32x4 *>(qrow + 32 * b + 4 * j);
+                        const float e[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            float r = rintf(e[i] * inv);
+                            r = fminf(fmaxf(r, -127.0f), 127.0f);
+                            word |= ((uint32_t)(int)r & 0xFFu) << (8 * i);
+                        }
+                    }
+                    qreg[b][j] = (int32_t)word;
+                }
+            }
+            if (DEBUG && split == 0 && row_ok) {
+                if (a.dbg_q) {
+#pragma unroll
+                    for (int b = 0; b < NB; ++b)
+                        *reinterpret_cast<i32x4 *>(a.dbg_q + (size_t)flat * D + 32 * b + 16 * hl) = qreg[b];
+                }
+                if (a.dbg_qscale && hl == 0) a.dbg_qscale[flat] = sq;
+            }
+        }
+        const float c_row = sq * a.scale_log2;
+        uint64_t mrow = 0;
+        if (!CAUSAL) {
+            for (int tt = 0; tt < a.T; ++tt)
+                if (tt == t) mrow = a.mask[tt];
+        }
+        const int vis_from = min(k1, a.L);
+        // MFMA row i of Q.K^T reads key krow(i): output registers r = 0..7 of
+        // lane half hl hold keys 8hl + r, registers 8..15 keys 16 + 8hl + r - 8,
+        // the key runs of the P.V operand
+        const int ai = l32 >> 3;
+        const int krow = 16 * (ai >> 1) + 8 * ((l32 >> 2) & 1) + 4 * (ai & 1) + (l32 & 3);
+        constexpr float kLazy = 8.0f;
+        float m_run = -INFINITY;
+        float l_run = 0.0f;
+
+        if (tid == 0) {
+            sh.k[0].wide_kb = -1;
+            sh.k[1].wide_kb = -1;
+        }
+        __syncthreads();     // the flags are set before any unpack
+        __syncthreads();     // K of the first tile is in LDS
+        for (int j = 0; j <= n_tiles; ++j) {
+            if (j < n_tiles && tile_active) {
+                const int kb = k0 + j * KT;
+                const typename W::KBuf &kt = sh.k[j & 1];
+                typename W::PBuf &pb = sh.p[j & 1][rt];
+                const int8_t *kq_lane = kt.kq + krow * L::KQS + 16 * hl;
+                f32x16 acc = f32x16{};
+                // the first operands go out with the read of the tile's flag
+                // (LDS returns in order: the flag's wait leaves them in flight)
+                const int wide_kb = kt.wide_kb;
+                i32x4 kop[3];
+                u32x4 mop[2][2];
+                kop[0] = *reinterpret_cast<const i32x4 *>(kq_lane);
+                kop[1] = *reinterpret_cast<const i32x4 *>(kq_lane + 32);
+                mop[0][0] = *reinterpret_cast<const u32x4 *>(kt.skm + 8 * hl);
+                mop[0][1] = *reinterpret_cast<const u32x4 *>(kt.skm + 16 + 8 * hl);
+                if (__builtin_amdgcn_readfirstlane(wide_kb) != kb) {
+                    // Q.K^T, one int8 MFMA per block; the block scales in
+                    // integer form make the logit one exact int32 sum (one
+                    // v_mad_i32_i16 per block), converted and scaled once.  The
+                    // MFMA of block b + 1 is issued before block b's sums, and
+                    // the LDS operands run ahead of their use (K two blocks, M
+                    // one), so no read waits right before its MFMA or sums.
+                    i32x16 iacc = i32x16{};
+                    i32x16 s_cur = __builtin_amdgcn_mfma_i32_32x32x32_i8(kop[0], qreg[0], i32x16{}, 0, 0, 0);
+#pragma unroll
+                    for (int b = 0; b < NB; ++b) {
+                        if (b + 2 < NB) kop[(b + 2) % 3] = *reinterpret_cast<const i32x4 *>(kq_lane + 32 * (b + 2));
+                        if (b + 1 < NB) {
+                            mop[(b + 1) & 1][0] = *reinterpret_cast<const u32x4 *>(kt.skm + (b + 1) * KT + 8 * hl);
+                            mop[(b + 1) & 1][1] = *reinterpret_cast<const u32x4 *>(kt.skm + (b + 1) * KT + 16 + 8 * hl);
+                        }
+                        i32x16 s_next;
+                        if (b + 1 < NB)
+                            s_next = __builtin_amdgcn_mfma_i32_32x32x32_i8(kop[(b + 1) % 3], qreg[b + 1], i32x16{}, 0, 0, 0);
+                        // M of keys 8hl + [0, 8) and 16 + 8hl + [0, 8), two per word
+                        const u32x4 m0 = mop[b & 1][0];
+                        const u32x4 m1 = mop[b & 1][1];
+                        const int32_t ready = mfma_ready(s_cur[0]);
+#pragma unroll
+                        for (int r = 0; r < 8; r += 2) {
+                            iacc[r] = mad_i16<0>(s_cur[r], m0[r >> 1], iacc[r], ready);
+                            iacc[r + 1] = mad_i16<1>(s_cur[r + 1], m0[r >> 1], iacc[r + 1], ready);
+                            iacc[8 + r] = mad_i16<0>(s_cur[8 + r], m1[r >> 1], iacc[8 + r], ready);
+                            iacc[9 + r] = mad_i16<1>(s_cur[9 + r], m1[r >> 1], iacc[9 + r], ready);
+                        }
+                        if (DEBUG && a.dbg_logits && row_ok) {
+#pragma unroll
+                            for (int r = 0; r < 16; ++r) {
+                                const int key = kb + (r < 8 ? 8 * hl + r : 16 + 8 * hl + (r - 8));
+                                if (key < k1) a.dbg_logits[((size_t)flat * a.N + key) * NB + b] = s_cur[r];
+                            }
+                        }
+                        if (b + 1 < NB) s_cur = s_next;
+                    }
+                    const f32x4 u0 = *reinterpret_cast<const f32x4 *>(kt.skf + 8 * hl);
+                    const f32x4 u1 = *reinterpret_cast<const f32x4 *>(kt.skf + 8 * hl + 4);
+                    const f32x4 u2 = *reinterpret_cast<const f32x4 *>(kt.skf + 16 + 8 * hl);
+                    const f32x4 u3 = *reinterpret_cast<const f32x4 *>(kt.skf + 16 + 8 * hl + 4);
+                    const float unit[16] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w,
+                                            u2.x, u2.y, u2.z, u2.w, u3.x, u3.y, u3.z, u3.w};
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[r] = unit[r] * (float)iacc[r];
+                } else {
+                    // the per-block fp32 epilogue, for a tile with a key whose
+                    // scales have no exact integer form
+#pragma unroll
+                    for (int b = 0; b < NB; ++b) {
+                        const i32x16 s_cur = __builtin_amdgcn_mfma_i32_32x32x32_i8(
+                            *reinterpret_cast<const i32x4 *>(kq_lane + 32 * b), qreg[b], i32x16{}, 0, 0, 0);
+                        const f16x8 h0 = *reinterpret_cast<const f16x8 *>(kt.skh + b * KT + 8 * hl);
+                        const f16x8 h1 = *reinterpret_cast<const f16x8 *>(kt.skh + b * KT + 16 + 8 * hl);
+#pragma unroll
+                        for (int r = 0; r < 8; ++r) {
+                            acc[r] = fmaf((float)h0[r], (float)s_cur[r], acc[r]);
+                            acc[8 + r] = fmaf((float)h1[r], (float)s_cur[8 + r], acc[8 + r]);
+                        }
+                        if (DEBUG && a.dbg_logits && row_ok) {
+#pragma unroll
+                            for (int r = 0; r < 16; ++r) {
+                                const int key = kb + (r < 8 ? 8 * hl + r : 16 + 8 * hl + (r - 8));
+                                if (key < k1) a.dbg_logits[((size_t)flat * a.N + key) * NB + b] = s_cur[r];
+                            }
+                        }
+                    }
+                }
+
+                // ---- mask, online softmax in base 2 (c_row >= 0: the row max of
+                // the scaled logits is c_row times the max of acc)
+                const bool masked = kb + KT > vis_from;
+                if (masked) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int key = kb + (r < 8 ? 8 * hl + r : 16 + 8 * hl + (r - 8));
+                        bool vis = key < k1;
+                        if (vis && key >= a.L) {
+                            const int u = key - a.L;
+                            vis = CAUSAL ? (u <= t) : (((mrow >> u) & 1ull) != 0ull);
+                        }
+                        if (!vis) acc[r] = -INFINITY;
+                    }
+                }
+                // the row max as a tree of three-way maxima (short dependency chain)
+                float m3[6];
+#pragma unroll
+                for (int i = 0; i < 5; ++i) m3[i] = fmaxf(fmaxf(acc[3 * i], acc[3 * i + 1]), acc[3 * i + 2]);
+                m3[5] = acc[15];
+                float amax = fmaxf(fmaxf(fmaxf(m3[0], m3[1]), m3[2]), fmaxf(fmaxf(m3[3], m3[4]), m3[5]));
+                amax = max_halves(amax);
+                const float tmax = amax == -INFINITY ? -INFINITY : amax * c_row;
+                const float m_new = tmax > m_run + kLazy ? tmax : m_run;
+                // the running max moves (rarely): the output waves scale their
+                // accumulators by alpha before adding this tile's P.V
+                const bool moved = __any(m_new != m_run);
+                if (moved) {
+                    const float alpha = m_new != m_run ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+                    l_run *= alpha;
+                    m_run = m_new;
+                    if (hl == 0) pb.alpha[l32] = alpha;
+                }
+                if (lane == 0) pb.rescale = moved ? 1 : 0;
+                const float mm = m_run == -INFINITY ? 0.0f : m_run;
+                float p[16];
+                if (masked) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        p[r] = acc[r] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(fmaf(acc[r], c_row, -mm));
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(fmaf(acc[r], c_row, -mm));
+                }
+                // P for the B operand of P.V (lane = row, 8 keys per k-step); the
+                // row sum adds the same fp16 values the MFMA multiplies
+                // (four independent pair sums, then a tree: a short chain)
+                const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+                f16x8 pk[2];
+                float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                    for (int e = 0; e < 8; e += 2) {
+                        const f16x2 h2 = __builtin_convertvector(f32x2{p[8 * ks + e], p[8 * ks + e + 1]}, f16x2);
+                        pk[ks][e] = h2.x;
+                        pk[ks][e + 1] = h2.y;
+                        const int c = (4 * ks + e / 2) & 3;
+                        ps[c] = __builtin_amdgcn_fdot2(h2, ones, ps[c], false);
+                    }
+                l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+                pb.p[0][lane] = pk[0];
+                pb.p[1][lane] = pk[1];
+            }
+            __syncthreads();
+        }
+        // ---- epilogue: 1 / (row sum) to the output waves, the lse out
+        const float l_tot = sum_halves(l_run);
+        if (tile_active && hl == 0) sh.p[0][rt].alpha[l32] = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+        if (tile_active && row_ok && hl == 0) {
+            const float lse = l_tot > 0.0f ? (m_run + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
+            if (partial)
+                a.part_lse[(size_t)split * rows_total + flat] = lse;
+            else if (a.out_lse)
+                a.out_lse[flat] = lse;
+        }
+        __syncthreads();
+        return;
+    }
+
+    // ---- output waves
+    const int item = (tid - NRT * 64) & 255;     // K item (waves 4-7) or V row d (waves 8-11)
+    const bool kthr = dh == 0;
+    f32x16 oacc[NH];
+#pragma unroll
+    for (int dt = 0; dt < NH; ++dt) oacc[dt] = f32x16{};
+
+    // Buffer-descriptor loads as in TileIo: entries past k1 read as zero, a
+    // tile at or past k1 reads nothing (zero-size descriptors based at k0).
+    auto load_k = [&](KItem &r, int kb) {
+        const bool valid = kb < k1;
+        const int kt = valid ? kb : k0;
+        const int nk = valid ? min(KT, k1 - kb) : 0;
+        const size_t head_base = (size_t)head * a.cap;
+        const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint32_t *>(a.kc + (head_base + kt) * NB * 3), (short)0, nk * NB * 12, kBufWord3);
+        const __amdgpu_buffer_rsrc_t rks = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t *>(a.ks + (head_base + kt) * NB), (short)0, nk * NB * 2, kBufWord3);
+        const u32x3 w = __builtin_amdgcn_raw_buffer_load_b96(rk, item * 12, 0, 0);
+        r.w[0] = w[0];
+        r.w[1] = w[1];
+        r.w[2] = w[2];
+        r.s = __builtin_amdgcn_raw_buffer_load_b16(rks, item * 2, 0, 0);
+    };
+    auto load_v = [&](VItem &r, int kb) {
+        const bool valid = kb < k1;
+        const int kt = valid ? kb : k0;
+        const size_t grp = (size_t)head * a.ngroups + (size_t)(kt / KT);
+        const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint32_t *>(a.vc + grp * D * 3), (short)0, valid ? D * 12 : 0, kBufWord3);
+        const __amdgpu_buffer_rsrc_t rvs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t *>(a.vs + grp * D), (short)0, valid ? D * 2 : 0, kBufWord3);
+        const u32x3 w = __builtin_amdgcn_raw_buffer_load_b96(rv, item * 12, 0, 0);
+        r.w[0] = w[0];
+        r.w[1] = w[1];
+        r.w[2] = w[2];
+        r.s = __builtin_amdgcn_raw_buffer_load_b16(rvs, item * 2, 0, 0);
+    };
+    // V scales of keys past the range become 0, so their V^ is exactly 0
+    auto store_v = [&](const VItem &r, typename W::VBuf &vb, int kb) {
+        const int nk = min(KT, k1 - kb);
+        vb.svs[item] = (item & 31) < nk ? r.s : (uint16_t)0;
+        wave_lds_sync();
+        unpack_v_row<L::VTS, L::VBPAD, false>(r, item, vb.vt, vb.svs);
+    };
+    auto store_k = [&](const KItem &r, typename W::KBuf &kbuf, int kb) {
+        unpack_k_item<NB, L::KQS, true, false>(r, item / NB, item % NB, kbuf.kq, kbuf.skh, kbuf.skm,
+                                               kbuf.skf, &kbuf.wide_kb, kb);
+    };
+    // P.V of a tile: this wave's d-tiles dh * NH + [0, NH)
+    auto phase_p = [&](const typename W::VBuf &vb, const typename W::PBuf &pb) {
+        if (__builtin_amdgcn_readfirstlane(pb.rescale)) {
+            const float al = pb.alpha[l32];
+#pragma unroll
+            for (int dt = 0; dt < NH; ++dt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[dt][r] *= al;
+        }
+        const f16x8 p0 = pb.p[0][lane];
+        const f16x8 p1 = pb.p[1][lane];
+        const _Float16 *vt_lane = vb.vt + l32 * L::VTS + 8 * hl;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+            for (int dt = 0; dt < NH; ++dt) {
+                const int gd = dh * NH + dt;
+                const f16x8 vop = *reinterpret_cast<const f16x8 *>(vt_lane + (gd * 32) * L::VTS +
+                                                                   gd * L::VBPAD + 16 * ks);
+                oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vop, ks ? p1 : p0, oacc[dt], 0, 0, 0);
+            }
+        }
+    };
+
+    // Step j: K of tile j + 1 (waves 4-7) or V of tile j (waves 8-11) into
+    // LDS from one of three register sets, which is then refilled with the
+    // tile three steps ahead (loads of tiles past the range read nothing), and
+    // P.V of tile j - 1.  Each role runs its own loop over triples of steps,
+    // so that the register sets stay put and every path into a step has that
+    // step's set loaded first: a step waits only for its own set's loads.
+    if (kthr) {
+        KItem r0, r1, r2;
+        load_k(r0, k0);
+        load_k(r1, k0 + KT);
+        load_k(r2, k0 + 2 * KT);
+        __syncthreads();     // the flags are set
+        if (n_tiles > 0) store_k(r0, sh.k[0], k0);
+        load_k(r0, k0 + 3 * KT);
+        __syncthreads();     // K of the first tile is in LDS
+        auto step = [&](int j, KItem &r) {
+            if (j + 1 < n_tiles) store_k(r, sh.k[(j + 1) & 1], k0 + (j + 1) * KT);
+            load_k(r, k0 + (j + 4) * KT);
+            if (j >= 1 && tile_active) phase_p(sh.v[(j - 1) & 1], sh.p[(j - 1) & 1][rt]);
+            __syncthreads();
+        };
+        int j = 0;
+        for (; j + 2 <= n_tiles; j += 3) {
+            step(j, r1);
+            step(j + 1, r2);
+            step(j + 2, r0);
+        }
+        if (j <= n_tiles) step(j, r1);
+        if (j + 1 <= n_tiles) step(j + 1, r2);
+    } else {
+        VItem r0, r1, r2;
+        load_v(r0, k0);
+        load_v(r1, k0 + KT);
+        load_v(r2, k0 + 2 * KT);
+        __syncthreads();
+        __syncthreads();
+        auto step = [&](int j, VItem &r) {
+            if (j < n_tiles) store_v(r, sh.v[j & 1], k0 + j * KT);
+            load_v(r, k0 + (j + 3) * KT);
+            if (j >= 1 && tile_active) phase_p(sh.v[(j - 1) & 1], sh.p[(j - 1) & 1][rt]);
+            __syncthreads();
+        };
+        int j = 0;
+        for (; j + 2 <= n_tiles; j += 3) {
+            step(j, r0);
+            step(j + 1, r1);
+            step(j + 2, r2);
+        }
+        if (j <= n_tiles) step(j, r0);
+        if (j + 1 <= n_tiles) step(j + 1, r1);
+    }
+    __syncthreads();     // the score waves' 1 / (row sum) is in LDS
+    if (!tile_active) return;
+    const float inv_l = sh.p[0][rt].alpha[l32];
+    float *const out_base = partial ? a.part_o + (size_t)split * rows_total * D : a.out;
+    // The output goes out through LDS (the V buffers, free after the last
+    // P.V), one 32-column tile at a time: read back row-major, eight lanes
+    // write a row's whole 128-byte segment in one store instruction.
+    constexpr int SS = 36;                       // staging row stride in floats
+    static_assert(8 * kRowTile * SS * 4 <= (int)sizeof(sh.v), "staging fits the V buffers");
+    float *stage = reinterpret_cast<float *>(&sh.v[0]) + (wave - NRT) * kRowTile * SS;
+    const int rr = lane >> 3, cq = lane & 7;     // read-back: rows rr + 8j, columns 4cq..4cq+3
+    float *dst_row[4];
+    bool ok_row[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int rho_j = (rg * NRT + rt) * kRowTile + rr + 8 * j;
+        ok_row[j] = rho_j < a.R;
+        const int t_j = ok_row[j] ? rho_j / a.G : 0;
+        const int g_j = ok_row[j] ? rho_j - t_j * a.G : 0;
+        dst_row[j] = out_base + (size_t)(t_j * a.Hq + head * a.G + g_j) * D + 4 * cq;
+    }
+#pragma unroll
+    for (int dt = 0; dt < NH; ++dt) {
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+            const f32x4 v = {oacc[dt][4 * r4 + 0] * inv_l, oacc[dt][4 * r4 + 1] * inv_l,
+                             oacc[dt][4 * r4 + 2] * inv_l, oacc[dt][4 * r4 + 3] * inv_l};
+            *reinterpret_cast<f32x4 *>(stage + l32 * SS + 8 * r4 + 4 * hl) = v;
+        }
+        wave_lds_sync();
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const f32x4 v = *reinterpret_cast<const f32x4 *>(stage + (rr + 8 * j) * SS + 4 * cq);
+            if (ok_row[j]) *reinterpret_cast<f32x4 *>(dst_row[j] + (dh * NH + dt) * 32) = v;
+        }
+        wave_lds_sync();
     }
 }
 
@@ -2292,8 +2801,20 @@ __global__ __launch_bounds__(kMergeMaxThreads) void merge_kernel(
 template <int NW, bool DEBUG>
 constexpr int kGroups = 1;
 
+// The wave-specialized kernel serves the 3-bit verify rows at head_dim 256 in
+// groups of four row tiles; the other shapes run attn_split_kernel.
+template <int D, int NW, bool CAUSAL, int FMT>
+constexpr bool kWaveSpecialized = D == 256 && NW == 4 && FMT == 0 && !CAUSAL;
+
+template <int D, bool CAUSAL, bool DEBUG>
+hipError_t launch_ws_t(const AttnArgs &a, hipStream_t stream) {
+    hipLaunchKernelGGL((attn_ws_kernel<D, CAUSAL, DEBUG>), dim3(a.n_hs_pad * a.NRG), dim3(kWsThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
 template <int D, int NW, bool CAUSAL, bool DEBUG, int FMT, bool PV16 = false, bool PRE = false>
 hipError_t launch_t(const AttnArgs &a, hipStream_t stream) {
+    if constexpr (kWaveSpecialized<D, NW, CAUSAL, FMT> && !PV16 && !PRE) return launch_ws_t<D, CAUSAL, DEBUG>(a, stream);
     constexpr int NG = kGroups<NW, DEBUG>;
     const int items = a.n_hs_pad * a.NRG;
     const int grid = NG == 2 ? 8 * ((items + 15) / 16) : items;
@@ -2414,6 +2935,15 @@ int occupancy_dec_t() {
 }
 
 }  // namespace
+
+int attention_ws_wgs_per_cu(int D) {
+    if (D != 256) return 0;
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &n, reinterpret_cast<const void *>(&attn_ws_kernel<256, false, false>), kWsThreads, 0) != hipSuccess)
+        return 0;
+    return n;
+}
 
 int attention_s16_wgs_per_cu(int D, bool causal) {
     switch (D) {
