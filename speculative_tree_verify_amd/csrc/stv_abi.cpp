@@ -271,26 +271,27 @@ Plan make_plan_keys(int T, int Hq, int Hkv, int D, int L, bool causal, int n_spl
     } else if (p.ws) {
         // The wave-specialized kernel holds one work-group per CU, and
         // work-group i runs on XCD i mod 8 with the row groups of one (head,
-        // split) on one XCD: the fullest XCD sets the number of rounds.  Pick
-        // the split count (up to three rounds' worth) that keeps the largest
-        // share of the slots busy over those rounds; a larger count must gain
-        // more than 2% (each split adds partials for the merge to read).
+        // split) on one XCD: the fullest XCD sets the number of rounds.  A
+        // round costs its work-groups' tiles plus a fixed part (prologue,
+        // prefetch fill, epilogue: about kWsRoundTiles tiles, measured), so
+        // pick the split count that minimises rounds x (tiles per split +
+        // that part), preferring fewer splits.
         const long long slots = attention_slots(D, p.NW, causal, 3, fmt);
-        const long long groups = (long long)Hkv * p.NRG;
         const long long xcds = slots % 8 == 0 ? 8 : 1;
         const long long per_xcd = slots / xcds;
         const long long max_s = n_tiles / 4 > 0 ? n_tiles / 4 : 1;
-        long long s_hi = 3 * slots / groups;
+        const long long groups = (long long)Hkv * p.NRG;
+        long long s_hi = 4 * ((slots + groups - 1) / groups);
         if (s_hi > max_s) s_hi = max_s;
         if (s_hi < 1) s_hi = 1;
         S = 1;
-        double best = -1.0;
+        long long best = -1;
         for (long long s = 1; s <= s_hi; ++s) {
             const long long fullest = p.NRG * ((Hkv * s + xcds - 1) / xcds);
             const long long rounds = (fullest + per_xcd - 1) / per_xcd;
-            const double busy = (double)(groups * s) / (double)(rounds * slots);
-            if (busy > best * 1.02) {
-                best = busy;
+            const long long cost = rounds * ((n_tiles + s - 1) / s + kWsRoundTiles);
+            if (best < 0 || cost < best) {
+                best = cost;
                 S = s;
             }
         }

@@ -53,6 +53,9 @@ constexpr int kS16MaxRows = 64;
 // The wave-specialized 32-row kernel (3-bit verify rows at head_dim 256, four
 // row tiles per work-group): twelve waves, one work-group per CU.
 constexpr int kWsThreads = 768;
+// Fixed cost of one round of its work-groups, in tile steps (measured: the
+// 64-node tree over 32K and 262K keys).
+constexpr int kWsRoundTiles = 12;
 
 struct Plan {
     bool dec;        // few-row kernel (then NW = 4 waves and NRG groups of 16 rows)
