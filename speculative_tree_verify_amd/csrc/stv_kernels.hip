@@ -68,6 +68,51 @@ __device__ __forceinline__ float sum_halves(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// A lane's part of one Q row for the int8 quantization in the attention
+// prologues: C four-element chunks of every 32-element block b, at
+// row + 32b + 4j.  All chunks load at once (one memory round trip, where a
+// load under a per-lane condition was issued and waited for one chunk at a
+// time), and the codes come from the same registers.  `row` must be readable
+// for every lane, also where the lane's row is past the last one (the kernels
+// point such lanes at a real row); valid = false gives a zero maximum and zero
+// codes for them.
+template <int NB, int C>
+struct QPart {
+    f32x4 v[NB][C];
+    __device__ __forceinline__ void load(const float *row) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int j = 0; j < C; ++j) v[b][j] = *reinterpret_cast<const f32x4 *>(row + 32 * b + 4 * j);
+    }
+    // largest magnitude of the lane's elements
+    __device__ __forceinline__ float absmax(bool valid) const {
+        float m = 0.0f;
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int j = 0; j < C; ++j) {
+                const f32x4 x = v[b][j];
+                m = fmaxf(m, fmaxf(fmaxf(fabsf(x.x), fabsf(x.y)), fmaxf(fabsf(x.z), fabsf(x.w))));
+            }
+        return valid ? m : 0.0f;
+    }
+    // int8 codes of chunk (b, j), element 4j + i in byte i: x * inv rounded
+    // to nearest even, clamped to [-127, 127]
+    __device__ __forceinline__ uint32_t codes(int b, int j, float inv, bool valid) const {
+        const f32x4 x = v[b][j];
+        const float e[4] = {x.x, x.y, x.z, x.w};
+        uint32_t word = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float r = rintf(e[i] * inv);
+            r = fminf(fmaxf(r, -127.0f), 127.0f);
+            word |= ((uint32_t)(int)r & 0xFFu) << (8 * i);
+        }
+        return valid ? word : 0u;
+    }
+};
+
 __device__ __forceinline__ float half_bits_to_float(uint16_t h) {
     return (float)__builtin_bit_cast(_Float16, h);
 }
@@ -865,39 +910,16 @@ void attn_split_kernel(const AttnArgs a) {
     int8_t *q_lane = qlds + (wave * kRowTile + l32) * L::KQS + 16 * hl;
     {
         i32x4 qreg[NB];
-        const float *qrow = a.q + (size_t)flat * D + 16 * hl;
-        float amax = 0.0f;
-        if (row_ok) {
-#pragma unroll
-            for (int b = 0; b < NB; ++b)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    f32x4 v = *reinterpret_cast<const f32x4 *>(qrow + 32 * b + 4 * j);
-                    amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)),
-                                             fmaxf(fabsf(v.z), fabsf(v.w))));
-                }
-        }
+        QPart<NB, 4> qp;
+        qp.load(a.q + (size_t)flat * D + 16 * hl);
+        float amax = qp.absmax(row_ok);
         amax = fmaxf(amax, __shfl_xor(amax, 32));
         const float inv = amax > 0.0f ? 127.0f / amax : 0.0f;
         sq = amax / 127.0f;
 #pragma unroll
-        for (int b = 0; b < NB; ++b) {
+        for (int b = 0; b < NB; ++b)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                uint32_t word = 0;
-                if (row_ok) {
-                    f32x4 v = *reinterpret_cast<const f32x4 *>(qrow + 32 * b + 4 * j);
-                    float e[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        float r = rintf(e[i] * inv);
-                        r = fminf(fmaxf(r, -127.0f), 127.0f);
-                        word |= ((uint32_t)(int)r & 0xFFu) << (8 * i);
-                    }
-                }
-                qreg[b][j] = (int32_t)word;
-            }
-        }
+            for (int j = 0; j < 4; ++j) qreg[b][j] = (int32_t)qp.codes(b, j, inv, row_ok);
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
             i32x4 w = qreg[b];
@@ -924,11 +946,8 @@ void attn_split_kernel(const AttnArgs a) {
     }
     const float c_row = sq * a.scale_log2;
 
-    uint64_t mrow = 0;
-    if (!CAUSAL) {
-        for (int tt = 0; tt < a.T; ++tt)
-            if (tt == t) mrow = a.mask[tt];
-    }
+    // the row's ancestor mask (t < T for every lane: rows past the end use row 0)
+    const uint64_t mrow = CAUSAL ? 0 : a.mask[t];
 
     // Key order inside a tile: MFMA row i of the Q.K^T product reads key
     // kperm(i), chosen so that output registers r = 0..7 of lane half hl hold
@@ -1386,38 +1405,16 @@ void attn_ws_kernel(const AttnArgs a) {
         i32x4 qreg[NB];
         float sq = 0.0f;
         {
-            const float *qrow = a.q + (size_t)flat * D + 16 * hl;
-            float amax = 0.0f;
-            if (row_ok) {
-#pragma unroll
-                for (int b = 0; b < NB; ++b)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const f32x4 v = *reinterpret_cast<const f32x4 *>(qrow + 32 * b + 4 * j);
-                        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
-                    }
-            }
+            QPart<NB, 4> qp;
+            qp.load(a.q + (size_t)flat * D + 16 * hl);
+            float amax = qp.absmax(row_ok);
             amax = fmaxf(amax, __shfl_xor(amax, 32));
             const float inv = amax > 0.0f ? 127.0f / amax : 0.0f;
             sq = amax / 127.0f;
 #pragma unroll
-            for (int b = 0; b < NB; ++b) {
+            for (int b = 0; b < NB; ++b)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    uint32_t word = 0;
-                    if (row_ok) {
-                        const f32x4 v = *reinterpret_cast<const f32x4 *>(qrow + 32 * b + 4 * j);
-                        const float e[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            float r = rintf(e[i] * inv);
-                            r = fminf(fmaxf(r, -127.0f), 127.0f);
-                            word |= ((uint32_t)(int)r & 0xFFu) << (8 * i);
-                        }
-                    }
-                    qreg[b][j] = (int32_t)word;
-                }
-            }
+                for (int j = 0; j < 4; ++j) qreg[b][j] = (int32_t)qp.codes(b, j, inv, row_ok);
             if (DEBUG && split == 0 && row_ok) {
                 if (a.dbg_q) {
 #pragma unroll
@@ -1428,11 +1425,8 @@ void attn_ws_kernel(const AttnArgs a) {
             }
         }
         const float c_row = sq * a.scale_log2;
-        uint64_t mrow = 0;
-        if (!CAUSAL) {
-            for (int tt = 0; tt < a.T; ++tt)
-                if (tt == t) mrow = a.mask[tt];
-        }
+        // the row's ancestor mask (t < T for every lane: rows past the end use row 0)
+        const uint64_t mrow = CAUSAL ? 0 : a.mask[t];
         const int vis_from = min(k1, a.L);
         // MFMA row i of Q.K^T reads key krow(i): output registers r = 0..7 of
         // lane half hl hold keys 8hl + r, registers 8..15 keys 16 + 8hl + r - 8,
@@ -1839,39 +1833,16 @@ __global__ __launch_bounds__(256) void attn_split16_kernel(const AttnArgs a) {
     i64_t qop[NB];
     float sq;
     {
-        const float *qrow = a.q + (size_t)flat * D + 8 * qc;
-        float amax = 0.0f;
-        if (row_ok) {
-#pragma unroll
-            for (int b = 0; b < NB; ++b)
-#pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    const f32x4 v = *reinterpret_cast<const f32x4 *>(qrow + 32 * b + 4 * j);
-                    amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
-                }
-        }
+        QPart<NB, 2> qp;
+        qp.load(a.q + (size_t)flat * D + 8 * qc);
+        float amax = qp.absmax(row_ok);
         amax = fmaxf(amax, __shfl_xor(amax, 16));
         amax = max_halves(amax);
         const float inv = amax > 0.0f ? 127.0f / amax : 0.0f;
         sq = amax / 127.0f;
 #pragma unroll
-        for (int b = 0; b < NB; ++b) {
-            uint32_t w2[2] = {0u, 0u};
-            if (row_ok) {
-#pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    const f32x4 v = *reinterpret_cast<const f32x4 *>(qrow + 32 * b + 4 * j);
-                    const float e[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        float r = rintf(e[i] * inv);
-                        r = fminf(fmaxf(r, -127.0f), 127.0f);
-                        w2[j] |= ((uint32_t)(int)r & 0xFFu) << (8 * i);
-                    }
-                }
-            }
-            qop[b] = (i64_t)((uint64_t)w2[0] | ((uint64_t)w2[1] << 32));
-        }
+        for (int b = 0; b < NB; ++b)
+            qop[b] = (i64_t)((uint64_t)qp.codes(b, 0, inv, row_ok) | ((uint64_t)qp.codes(b, 1, inv, row_ok) << 32));
         if (DEBUG && split == 0 && row_ok) {
             if (a.dbg_q) {
 #pragma unroll
@@ -1882,11 +1853,8 @@ __global__ __launch_bounds__(256) void attn_split16_kernel(const AttnArgs a) {
         }
     }
     const float c_row = sq * a.scale_log2;
-    uint64_t mrow = 0;
-    if (!CAUSAL) {
-        for (int tt = 0; tt < a.T; ++tt)
-            if (tt == t) mrow = a.mask[tt];
-    }
+    // the row's ancestor mask (t < T for every lane: rows past the end use row 0)
+    const uint64_t mrow = CAUSAL ? 0 : a.mask[t];
 
     // A operand row m of key half kh reads key 8(m / 4) + 4kh + m % 4, so the
     // result registers of lane (i16, qc) hold keys 8qc + 4kh + [0, 4): its
@@ -2125,39 +2093,16 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_dec_kernel(const AttnArgs
     i64_t qop[NB];
     float sq;
     {
-        const float *qrow = a.q + (size_t)flat * D + 8 * qc;
-        float amax = 0.0f;
-        if (row_ok) {
-#pragma unroll
-            for (int b = 0; b < NB; ++b)
-#pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    const f32x4 v = *reinterpret_cast<const f32x4 *>(qrow + 32 * b + 4 * j);
-                    amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
-                }
-        }
+        QPart<NB, 2> qp;
+        qp.load(a.q + (size_t)flat * D + 8 * qc);
+        float amax = qp.absmax(row_ok);
         amax = fmaxf(amax, __shfl_xor(amax, 16));
         amax = max_halves(amax);
         const float inv = amax > 0.0f ? 127.0f / amax : 0.0f;
         sq = amax / 127.0f;
 #pragma unroll
-        for (int b = 0; b < NB; ++b) {
-            uint32_t w2[2] = {0u, 0u};
-            if (row_ok) {
-#pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    const f32x4 v = *reinterpret_cast<const f32x4 *>(qrow + 32 * b + 4 * j);
-                    const float e[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        float r = rintf(e[i] * inv);
-                        r = fminf(fmaxf(r, -127.0f), 127.0f);
-                        w2[j] |= ((uint32_t)(int)r & 0xFFu) << (8 * i);
-                    }
-                }
-            }
-            qop[b] = (i64_t)((uint64_t)w2[0] | ((uint64_t)w2[1] << 32));
-        }
+        for (int b = 0; b < NB; ++b)
+            qop[b] = (i64_t)((uint64_t)qp.codes(b, 0, inv, row_ok) | ((uint64_t)qp.codes(b, 1, inv, row_ok) << 32));
         if (DEBUG && split == 0 && wave == 0 && row_ok) {
             if (a.dbg_q) {
 #pragma unroll
@@ -2179,11 +2124,8 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_dec_kernel(const AttnArgs
         }
     }
     const float c_row = sq * a.scale_log2;
-    uint64_t mrow = 0;
-    if (!CAUSAL) {
-        for (int tt = 0; tt < a.T; ++tt)
-            if (tt == t) mrow = a.mask[tt];
-    }
+    // the row's ancestor mask (t < T for every lane: rows past the end use row 0)
+    const uint64_t mrow = CAUSAL ? 0 : a.mask[t];
 
     f32x4 oacc[NDT];
 #pragma unroll
