@@ -270,8 +270,8 @@ Plan make_plan_keys(int T, int Hq, int Hkv, int D, int L, bool causal, int n_spl
         S = n_splits_req;
     } else if (p.ws) {
         // The wave-specialized kernel holds one work-group per CU, and
-        // work-group i runs on XCD i mod 8 with the row groups of one (head,
-        // split) on one XCD: the fullest XCD sets the number of rounds.  A
+        // work-group i runs on XCD i mod 8; each XCD takes a run of
+        // ceil(work-groups / 8) of them, which sets the number of rounds.  A
         // round costs its work-groups' tiles plus a fixed part (prologue,
         // prefetch fill, epilogue: about kWsRoundTiles tiles, measured), so
         // pick the split count that minimises rounds x (tiles per split +
@@ -287,7 +287,7 @@ Plan make_plan_keys(int T, int Hq, int Hkv, int D, int L, bool causal, int n_spl
         S = 1;
         long long best = -1;
         for (long long s = 1; s <= s_hi; ++s) {
-            const long long fullest = p.NRG * ((Hkv * s + xcds - 1) / xcds);
+            const long long fullest = (p.NRG * Hkv * s + xcds - 1) / xcds;
             const long long rounds = (fullest + per_xcd - 1) / per_xcd;
             const long long cost = rounds * ((n_tiles + s - 1) / s + kWsRoundTiles);
             if (best < 0 || cost < best) {

@@ -1370,13 +1370,16 @@ void attn_ws_kernel(const AttnArgs a) {
     const int rt = score ? wave : (wave - NRT) % NRT;
     const int dh = score ? 0 : (wave - NRT) / NRT;
 
-    // ---- work item (kv head, split, row group), mapped as in the 32-row kernel
-    const int vid = blockIdx.x;
-    const int chunk = vid / (8 * a.NRG);
-    const int within = vid - chunk * 8 * a.NRG;
-    const int hs = chunk * 8 + (within & 7);
-    if (hs >= a.Hkv * a.S) return;
-    const int rg = within >> 3;
+    // ---- work item w = (head * S + split) * NRG + row group.  Work-group i
+    // runs on XCD i mod 8; XCD x takes the run of items [x Q, x Q + Q), Q =
+    // ceil(items / 8), so the row groups of one (head, split) share an XCD's
+    // L2 (except where a run ends) and no XCD holds more than Q of them.
+    const int n_items = a.Hkv * a.S * a.NRG;
+    const int per_xcd = (n_items + 7) / 8;
+    const int w_item = ((int)blockIdx.x & 7) * per_xcd + ((int)blockIdx.x >> 3);
+    if (w_item >= n_items) return;
+    const int hs = w_item / a.NRG;
+    const int rg = w_item - hs * a.NRG;
     const int head = hs / a.S;
     const int split = hs - head * a.S;
     const int k0 = split * a.split_len;
@@ -2750,7 +2753,9 @@ constexpr bool kWaveSpecialized = D == 256 && NW == 4 && FMT == 0 && !CAUSAL;
 
 template <int D, bool CAUSAL, bool DEBUG>
 hipError_t launch_ws_t(const AttnArgs &a, hipStream_t stream) {
-    hipLaunchKernelGGL((attn_ws_kernel<D, CAUSAL, DEBUG>), dim3(a.n_hs_pad * a.NRG), dim3(kWsThreads), 0, stream, a);
+    // eight runs of ceil(items / 8) work-groups, one per XCD
+    const int per_xcd = (a.Hkv * a.S * a.NRG + 7) / 8;
+    hipLaunchKernelGGL((attn_ws_kernel<D, CAUSAL, DEBUG>), dim3(8 * per_xcd), dim3(kWsThreads), 0, stream, a);
     return hipGetLastError();
 }
 

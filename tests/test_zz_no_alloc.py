@@ -29,9 +29,9 @@ def _row_err(got, ref):
     return np.max(np.abs(got - ref), axis=-1) / np.max(np.abs(ref), axis=-1)
 
 
-def _case(stv, torch, orc, hq, hkv, d, L, T, seed, n_splits_ref=0):
+def _case(stv, torch, orc, hq, hkv, d, L, T, seed, n_splits_ref=0, fmt="b3"):
     rng = np.random.default_rng(seed)
-    host = synth.make_kv(rng, hkv, d, L + T)
+    host = (synth.make_kv4 if fmt == "i4" else synth.make_kv)(rng, hkv, d, L + T)
     q = torch.from_numpy(synth.make_q(rng, T, hq, d)).cuda()
     mask = synth.ancestor_masks(synth.make_tree_parents(rng, T, 8))
     kv = stv.KVCache.from_host(host)
@@ -49,7 +49,7 @@ def _case(stv, torch, orc, hq, hkv, d, L, T, seed, n_splits_ref=0):
 
 def test_noalloc_two_calls_then_smaller(gpu, orc):
     stv, torch = gpu
-    # 64-node tree over 20K keys: 42-odd splits of 1.6 MB partials in the scratch
+    # 64-node tree over 20K keys: some 20 splits of 1.6 MB partials in the scratch
     S1, ws1 = stv.attention_plan(64, 24, 4, 256, 20000, False, 0)
     assert S1 > 1 and ws1 <= stv.noalloc_scratch_bytes()
     _case(stv, torch, orc, 24, 4, 256, 20000, 64, 950)
@@ -62,20 +62,21 @@ def test_noalloc_caps_the_automatic_split_count(gpu, orc):
     the call takes as many splits as fit, and then equals the workspace entry
     point asked for that count.  The split count follows the device's
     occupancy, so the first of a few 64-node-tree shapes whose plan passes the
-    array is used (32 query / 4 KV heads did under the four-wave kernel's plan;
-    under the wave-specialized kernel's, many query heads on one KV head, whose
-    row groups share an XCD and so take several rounds of splits)."""
+    array is used: the 4-bit format's 32-row kernel fills two work-groups per
+    CU once (32 query / 4 KV heads: 32 splits of 2.1 MB), while the 3-bit
+    wave-specialized kernel's one round of one work-group per CU stays below
+    the array at 64 rows."""
     stv, torch = gpu
     T, d, L = 64, 256, 8000
-    for hq, hkv in ((32, 4), (96, 1), (128, 1)):
-        S_auto, ws_auto = stv.attention_plan(T, hq, hkv, d, L, False, 0)
+    for hq, hkv, fmt in ((32, 4, "i4"), (64, 4, "i4"), (32, 4, "b3"), (128, 1, "b3")):
+        S_auto, ws_auto = stv.attention_plan(T, hq, hkv, d, L, False, 0, fmt)
         if ws_auto > stv.noalloc_scratch_bytes():
             break
     else:
         pytest.skip("no candidate's automatic plan passes the scratch on this device")
     fit = stv.noalloc_scratch_bytes() // (T * hq * (d + 1) * 4)
     assert 1 < fit < S_auto
-    _case(stv, torch, orc, hq, hkv, d, L, T, 952, n_splits_ref=int(fit))
+    _case(stv, torch, orc, hq, hkv, d, L, T, 952, n_splits_ref=int(fit), fmt=fmt)
 
 
 def test_noalloc_rejects_too_many_splits(gpu):
