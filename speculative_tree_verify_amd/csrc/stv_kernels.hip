@@ -250,56 +250,54 @@ __global__ void k_pack_kernel(const float *__restrict__ x, int n_tok, int pos0,
     scales[pos * NB + b] = s16;
 }
 
-// V, first pass: one thread per (token, head, block) writes the scale into
-// the key-transposed scale layout [Hkv][ng][D/32][32].
-__global__ void v_scale_kernel(const float *__restrict__ x, int n_tok, int pos0,
-                               uint16_t *__restrict__ scales, int Hkv, int D, int ng) {
+// V: one work-group of D threads per (head, 32-key group that holds new
+// keys); the key-transposed layout puts the codes of 32 keys in each element
+// row's three words, so one thread owns a row's read-modify-write.  The
+// group's new rows are staged in LDS; thread i = (key e = i / NB, block
+// b = i % NB) computes that block's scale from its 32 elements and writes it
+// to the scale layout [Hkv][ng][D/32][32]; then thread d rewrites the three
+// words of element row d, changing only the new keys.  The old code words are
+// loaded first, so their latency overlaps the rows'.
+__global__ __launch_bounds__(256) void v_pack_kernel(const float *__restrict__ x, int n_tok, int pos0,
+                                                     uint32_t *__restrict__ codes,
+                                                     uint16_t *__restrict__ scales, int Hkv, int D,
+                                                     int ng, int grp0) {
+    __shared__ float xs[32][8][33];      // [key][block][element], one float of padding per block
+    __shared__ uint16_t ss[32][8];       // [key][block] scales
     const int NB = D / 32;
-    const long long total = (long long)n_tok * Hkv * NB;
-    const long long id = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-    if (id >= total) return;
-    const int b = (int)(id % NB);
-    const int g = (int)((id / NB) % Hkv);
-    const int t = (int)(id / ((long long)NB * Hkv));
-    float v[32];
-    load32(x + ((size_t)t * Hkv + g) * D + 32 * b, v);
-    const int pos = pos0 + t;
-    scales[(((size_t)g * ng + pos / 32) * NB + b) * 32 + (pos & 31)] = block_scale(v);
-}
-
-// V, second pass: one thread per (head, group, element d) rewrites the three
-// words holding that element of the group's 32 keys, changing only the keys
-// in [pos0, pos0 + n_tok).
-__global__ void v_code_kernel(const float *__restrict__ x, int n_tok, int pos0,
-                              uint32_t *__restrict__ codes, const uint16_t *__restrict__ scales,
-                              int Hkv, int D, int ng, int grp0, int n_grp) {
-    const int NB = D / 32;
-    const long long total = (long long)n_grp * Hkv * D;
-    const long long id = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-    if (id >= total) return;
-    const int d = (int)(id % D);
-    const int g = (int)((id / D) % Hkv);
-    const int grp = grp0 + (int)(id / ((long long)D * Hkv));
-    uint32_t *w = codes + (((size_t)g * ng + grp) * D + d) * 3;
-    const uint16_t *srow = scales + (((size_t)g * ng + grp) * NB + d / 32) * 32;
-    // All loads first (the new keys of this group are a contiguous run), so
-    // they are in flight together; then the read-modify-write of the row.
+    const int g = (int)blockIdx.x % Hkv;
+    const int grp = grp0 + (int)blockIdx.x / Hkv;
+    const int d = threadIdx.x;           // element row (and, for the scales, key d / NB, block d % NB)
     const int e0 = max(0, pos0 - grp * 32), e1 = min(32, pos0 + n_tok - grp * 32);
+    uint32_t *w = codes + (((size_t)g * ng + grp) * D + d) * 3;
+    uint32_t w0 = w[0], w1 = w[1], w2 = w[2];
+    // every key's row is loaded (keys outside the new ones read a real new row,
+    // unused), so all loads are issued before the first wait
     float xv[32];
-    uint16_t sv[32];
 #pragma unroll
     for (int e = 0; e < 32; ++e) {
-        xv[e] = 0.0f;
-        sv[e] = 0;
-        if (e >= e0 && e < e1) {
-            xv[e] = x[((size_t)(grp * 32 + e - pos0) * Hkv + g) * D + d];
-            sv[e] = srow[e];
-        }
+        const int r = min(max(grp * 32 + e - pos0, 0), n_tok - 1);
+        xv[e] = x[((size_t)r * Hkv + g) * D + d];
     }
-    uint32_t w0 = w[0], w1 = w[1], w2 = w[2];
 #pragma unroll
     for (int e = 0; e < 32; ++e)
-        if (e >= e0 && e < e1) set_code(w0, w1, w2, e, code_of(xv[e], half_bits_to_float(sv[e])));
+        if (e >= e0 && e < e1) xs[e][d >> 5][d & 31] = xv[e];
+    __syncthreads();
+    {
+        const int e = d / NB, b = d - (d / NB) * NB;
+        if (e >= e0 && e < e1) {
+            float v[32];
+#pragma unroll
+            for (int k = 0; k < 32; ++k) v[k] = xs[e][b][k];
+            const uint16_t s16 = block_scale(v);
+            ss[e][b] = s16;
+            scales[(((size_t)g * ng + grp) * NB + b) * 32 + e] = s16;
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < 32; ++e)
+        if (e >= e0 && e < e1) set_code(w0, w1, w2, e, code_of(xv[e], half_bits_to_float(ss[e][d >> 5])));
     w[0] = w0;
     w[1] = w1;
     w[2] = w2;
@@ -3046,16 +3044,11 @@ hipError_t launch_kv_pack(const float *x, int n_tok, int pos0, uint32_t *codes, 
                            dim3(threads), 0, stream, x, n_tok, pos0, codes, scales, Hkv, D, cap);
         return hipGetLastError();
     }
+    // V: one work-group of D (64, 128 or 256) threads per (head, touched group)
     const int ng = (cap + 31) / 32;
-    hipLaunchKernelGGL(v_scale_kernel, dim3((unsigned)((items + threads - 1) / threads)),
-                       dim3(threads), 0, stream, x, n_tok, pos0, scales, Hkv, D, ng);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
     const int grp0 = pos0 / 32, n_grp = (pos0 + n_tok - 1) / 32 - grp0 + 1;
-    const long long rows = (long long)n_grp * Hkv * D;
-    hipLaunchKernelGGL(v_code_kernel, dim3((unsigned)((rows + threads - 1) / threads)),
-                       dim3(threads), 0, stream, x, n_tok, pos0, codes, scales, Hkv, D, ng, grp0,
-                       n_grp);
+    hipLaunchKernelGGL(v_pack_kernel, dim3((unsigned)((long long)n_grp * Hkv)), dim3(D), 0, stream, x, n_tok,
+                       pos0, codes, scales, Hkv, D, ng, grp0);
     return hipGetLastError();
 }
 
