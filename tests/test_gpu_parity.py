@@ -543,3 +543,47 @@ def test_partials_then_merge_equals_verify(gpu, orc):
         assert _row_err(got, ref["out"]).max() <= TOL
         gl = pl[s].reshape(-1)[[0, 7, T * hq - 1]].cpu().numpy()
         assert np.max(np.abs(gl - ref["lse"])) <= TOL
+
+
+@pytest.mark.parametrize("hq,hkv,n_splits", [(24, 4, 5), (24, 4, 22), (6, 1, 1), (6, 1, 3),
+                                             (32, 4, 7), (8, 1, 43)])
+def test_wave_specialized_item_runs(gpu, orc, hq, hkv, n_splits):
+    """The wave-specialized kernel (3-bit, head_dim 256, 64 tree rows) sends
+    work item w = (head * S + split) * row groups + row group to the XCD run
+    w / ceil(items / 8).  Item counts that are not multiples of eight, runs
+    shorter than eight and more than one round: the partials go into
+    NaN-filled buffers, so an item that no work-group computes shows, and the
+    partials of sampled splits match the oracle's over the same key ranges on
+    rows of every row group, so one computed for the wrong split or written to
+    the wrong place shows too.  The merge matches the one-split call."""
+    stv, torch = gpu
+    T, d, L = 64, 256, 6000          # 190 tiles: 22 splits stay 22 (264 items, two rounds)
+    rng = np.random.default_rng(1200 + 100 * hq + n_splits)
+    host = synth.make_kv(rng, hkv, d, L + T)
+    kv = stv.KVCache.from_host(host)
+    q = torch.from_numpy(synth.make_q(rng, T, hq, d)).cuda()
+    mask = synth.ancestor_masks(synth.make_tree_parents(rng, T, 8))
+    S, _ = stv.attention_plan(T, hq, hkv, d, L, False, n_splits)
+    po = torch.full((S, T, hq, d), float("nan"), dtype=torch.float32, device="cuda")
+    pl = torch.full((S, T, hq), float("nan"), dtype=torch.float32, device="cuda")
+    stv.attention_partials(q, kv, L, mask, n_splits=n_splits, part_o=po, part_lse=pl)
+    torch.cuda.synchronize()
+    assert not torch.isnan(po).any() and not torch.isnan(pl).any()
+    n_keys = L + T
+    split_len = 32 * -(-(-(-n_keys // 32)) // S)        # 32 * ceil(ceil(N / 32) / S)
+    rows = np.unique(np.linspace(0, T * hq - 1, 16).round().astype(np.int64))
+    qh = q.cpu().numpy()
+    for s in sorted({0, 1 % S, S // 2, S - 1}):
+        k0, k1 = s * split_len, min(n_keys, (s + 1) * split_len)
+        ref = orc.attention(qh, host, L, mask, k_begin=k0, k_end=k1, rows=rows)
+        got = po[s].reshape(T * hq, d)[torch.from_numpy(rows).cuda()].cpu().numpy()
+        assert _row_err(got, ref["out"]).max() <= TOL, f"split {s}"
+        gl = pl[s].reshape(-1)[torch.from_numpy(rows).cuda()].cpu().numpy()
+        # a row that sees no key of the split (the last one holds only tree
+        # keys here) has lse -inf on both sides
+        same = gl == ref["lse"]
+        assert np.all(same | (np.abs(gl - ref["lse"]) <= TOL)), f"split {s}"
+    out = stv.split_merge(po.reshape(S, T * hq, d), pl.reshape(S, T * hq))
+    one = stv.verify_attention(q, kv, L, mask, n_splits=1)
+    torch.cuda.synchronize()
+    assert _row_err(out.cpu().numpy(), one.reshape(T * hq, d).cpu().numpy()).max() <= TOL
