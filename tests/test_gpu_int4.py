@@ -119,10 +119,13 @@ def test_full_size_262k_sampled_rows(gpu, orc, T, n_rows):
 @pytest.mark.parametrize("scale_mul", [8.0, 32.0])
 def test_parity_int4_peaked(gpu, orc, scale_mul):
     """Nearly one-hot softmax: the running max moves often, which rescales
-    the few-row kernel's per-row V-scale sums with the accumulators."""
+    the few-row kernel's per-row V-scale sums with the accumulators, and the
+    32-row kernel's accumulators at the 64-node tree."""
     run4(gpu, orc, 24, 4, 256, 1500, 1, "tree", 212, scale_mul=scale_mul)
     run4(gpu, orc, 24, 4, 256, 900, 8, "tree", 213, scale_mul=scale_mul)
     run4(gpu, orc, 24, 4, 256, 700, 16, "tree", 214, scale_mul=scale_mul)
+    # the 64-node tree: the 32-row kernel rescales its accumulators
+    run4(gpu, orc, 24, 4, 256, 1200, 64, "tree", 215, scale_mul=scale_mul)
 
 
 @pytest.mark.parametrize("d,pos0,n_tok", [(64, 0, 1), (128, 29, 8), (256, 61, 64), (256, 0, 100)])
