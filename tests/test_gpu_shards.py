@@ -41,7 +41,7 @@ def _slice(host, k0, k1):
 
 
 CASES = [
-    # name, hq, hkv, d, L, T, fmt (few-row, 16-row and 32-row kernels; 4-bit few-row)
+    # name, hq, hkv, d, L, T, fmt (few-row, 16-row and wave-specialized kernels; 4-bit few-row)
     ("one_token", 24, 4, 256, 5000, 1, "b3"),
     ("tree8", 24, 4, 256, 5000, 8, "b3"),
     ("tree64", 24, 4, 256, 3000, 64, "b3"),
