@@ -170,3 +170,20 @@ def test_commit4_matches_oracle(gpu, orc, hkv, d, L, T, seed):
     assert np.array_equal(kv.k_scales.cpu().numpy().view(np.uint16), host.k_scales)
     assert np.array_equal(kv.v_codes.cpu().numpy().view(np.uint32), host.v_codes)
     assert np.array_equal(kv.v_scales.cpu().numpy().view(np.uint16), host.v_scales)
+
+
+def test_shape_sweep_kernel_boundaries_int4(gpu, orc):
+    """The 4-bit format on both sides of its plan's boundaries (64 | 65 rows
+    per KV head: few-row / 32-row kernel; 96 | 97: two / four row tiles),
+    over head dims, context lengths and split counts, against the oracle on
+    sampled rows, int8 Q and int32 logits bit for bit."""
+    rng = np.random.default_rng(1500)
+    for i, (g, T) in enumerate([(1, 64), (2, 32), (2, 33), (6, 10), (6, 11), (6, 16), (6, 17),
+                                (8, 8), (8, 9), (3, 22), (6, 64), (8, 64)]):
+        hkv = int(rng.choice([1, 2, 4]))
+        d = int(rng.choice([64, 128, 256]))
+        L = int(rng.choice([0, 1, 31, 700, 2049]))
+        ns = int(rng.choice([0, 0, 1, 2, 3, 5]))
+        hq = g * hkv
+        rows = np.unique(np.linspace(0, T * hq - 1, 12).round().astype(np.int64))
+        run4(gpu, orc, hq, hkv, d, L, T, "tree", 1600 + i, n_splits=ns, rows=rows)

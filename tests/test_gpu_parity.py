@@ -587,3 +587,28 @@ def test_wave_specialized_item_runs(gpu, orc, hq, hkv, n_splits):
     one = stv.verify_attention(q, kv, L, mask, n_splits=1)
     torch.cuda.synchronize()
     assert _row_err(out.cpu().numpy(), one.reshape(T * hq, d).cpu().numpy()).max() <= TOL
+
+
+# (query heads per KV head, tree rows): rows per KV head on both sides of
+# each kernel boundary (16 | 17: few-row / 16-row; 32 | 33; 64 | 65: 16-row /
+# 32-row; 96 | 97: two / four row tiles per work-group), and the largest.
+_BOUNDARY_SHAPES = [(1, 16), (1, 17), (2, 8), (2, 9), (2, 16), (2, 17), (2, 32), (2, 33),
+                    (2, 48), (2, 49), (6, 2), (6, 3), (6, 5), (6, 6), (6, 10), (6, 11),
+                    (6, 16), (6, 17), (8, 4), (8, 8), (8, 12), (8, 13), (3, 22), (3, 32),
+                    (6, 64), (8, 64), (1, 64), (4, 25)]
+
+
+def test_shape_sweep_kernel_boundaries(gpu, orc):
+    """Seeded shapes on both sides of every boundary of the plan's kernel
+    choice, over the head dims, context lengths (including none) and split
+    counts: outputs and lse against the oracle on sampled rows, int8 Q and
+    int32 logits bit for bit."""
+    rng = np.random.default_rng(1300)
+    for i, (g, T) in enumerate(_BOUNDARY_SHAPES):
+        hkv = int(rng.choice([1, 2, 4]))
+        d = int(rng.choice([64, 128, 256]))
+        L = int(rng.choice([0, 1, 31, 33, 700, 2049, 3000]))
+        ns = int(rng.choice([0, 0, 1, 2, 3, 5, 7]))
+        hq = g * hkv
+        rows = np.unique(np.linspace(0, T * hq - 1, 12).round().astype(np.int64))
+        run_case(gpu, orc, hq, hkv, d, L, T, "tree", 1400 + i, n_splits=ns, rows=rows)
