@@ -344,6 +344,28 @@ def test_plan_is_consistent(stvmod, T, hq, hkv, d, L, causal, fmt):
     assert S0 == S1
 
 
+def test_plan_wave_specialized_rounds(stvmod):
+    """The wave-specialized kernel's split plan with the fixed MI355X figure
+    used when no device answers (256 CUs, one work-group each, eight XCDs):
+    work items run ceil(items / 8) to an XCD, a round costs its tiles plus 12
+    tile steps, and the plan takes the cheapest split count.  The 64-node tree
+    (three row groups per KV head) gets 21 splits at 262K and at 32K: 252
+    items, 32 per XCD, one round."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("with a device the plan follows its occupancy")
+    for L in (262144, 32768):
+        S, _ = stvmod.attention_plan(64, 24, 4, 256, L, False, 0, "b3")
+        n_tiles = -(-(L + 64) // 32)
+
+        def cost(s):
+            per_xcd = -(-(4 * 3 * s) // 8)
+            return -(-per_xcd // 32) * (-(-n_tiles // s) + 12)
+
+        assert S == 21
+        assert cost(S) == min(cost(s) for s in range(1, 89))
+
+
 def test_workspace_bytes(stvmod):
     lib = stvmod.load_library()
     assert stvmod.workspace_bytes(64, 24, 256, 42) == 42 * 64 * 24 * 257 * 4
