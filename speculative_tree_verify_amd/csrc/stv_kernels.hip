@@ -607,6 +607,84 @@ struct TileIo {
     }
 };
 
+// The 16-row kernel's tile I/O (256 threads, 3-bit format): thread tid
+// holds K item tid and, with V, element rows of the V side: row tid, or
+// (VWAVE) rows lane + 64i, i < D / 64, of the one wave that unpacks all of
+// them (the kernel gives them to its fourth wave when that wave has no query
+// rows, so the wave that would idle through the math takes the V unpack and
+// the three computing waves only the K items).
+template <int D, bool VWAVE>
+struct Split16Io {
+    static constexpr int NB = D / 32;
+    static constexpr int KI = kKeyTile * NB;           // K items per tile (at most 256)
+    static constexpr int NV = VWAVE ? D / 64 : 1;
+    static_assert(KI <= 256 && D <= 256 && D % 64 == 0, "one K item per thread");
+    using L = TileLds<D, true>;
+    KItem k;
+    VItem v[NV];
+
+    __device__ __forceinline__ static int vrow(int tid, int i) {
+        return VWAVE ? (tid & 63) + 64 * i : tid;
+    }
+
+    // Buffer-descriptor loads as in TileIo: zeros past k1 (and for rows
+    // d >= D, which are not stored), nothing for a tile at or past k1.
+    __device__ __forceinline__ void load(const AttnArgs &a, int head, int kb, int k0, int k1,
+                                         int tid, bool with_v) {
+        const bool valid = kb < k1;
+        const int kt = valid ? kb : k0;
+        const int nk = valid ? min(kKeyTile, k1 - kb) : 0;
+        const size_t head_base = (size_t)head * a.cap;
+        const size_t grp = (size_t)head * a.ngroups + (size_t)(kt / kKeyTile);
+        const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint32_t *>(a.kc + (head_base + kt) * NB * 3), (short)0, nk * NB * 12, kBufWord3);
+        const __amdgpu_buffer_rsrc_t rks = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t *>(a.ks + (head_base + kt) * NB), (short)0, nk * NB * 2, kBufWord3);
+        const u32x3 w = __builtin_amdgcn_raw_buffer_load_b96(rk, tid * 12, 0, 0);
+        k.w[0] = w[0];
+        k.w[1] = w[1];
+        k.w[2] = w[2];
+        k.s = __builtin_amdgcn_raw_buffer_load_b16(rks, tid * 2, 0, 0);
+        if (!with_v) return;
+        const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint32_t *>(a.vc + grp * D * 3), (short)0, valid ? D * 12 : 0, kBufWord3);
+        const __amdgpu_buffer_rsrc_t rvs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t *>(a.vs + grp * D), (short)0, valid ? D * 2 : 0, kBufWord3);
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int d = vrow(tid, i);
+            const u32x3 x = __builtin_amdgcn_raw_buffer_load_b96(rv, d * 12, 0, 0);
+            v[i].w[0] = x[0];
+            v[i].w[1] = x[1];
+            v[i].w[2] = x[2];
+            v[i].s = __builtin_amdgcn_raw_buffer_load_b16(rvs, d * 2, 0, 0);
+        }
+    }
+
+    // Tile into one LDS buffer: K int8 rows kq, fp16 K scales skh, V^ rows
+    // vt; svs stages the V scales.  nk: keys of the tile below k1 (V scales
+    // of later keys become 0, so their V^ is exactly 0).  The V scales a
+    // wave's rows read are the ones that wave wrote (one row per thread:
+    // entries 64w .. 64w + 63, blocks 2w and 2w + 1; VWAVE: all of them), so
+    // a wave-local sync orders them.
+    __device__ __forceinline__ void store(int8_t *kq, _Float16 *skh, _Float16 *vt, uint16_t *svs,
+                                          int tid, int nk, bool with_v) const {
+        if (tid < KI)
+            unpack_k_item<NB, L::KQS, false, true>(k, tid / NB, tid % NB, kq, skh, nullptr, nullptr,
+                                                   nullptr, 0);
+        if (!with_v || vrow(tid, 0) >= D) return;       // (wave-uniform)
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int d = vrow(tid, i);
+            svs[d] = (d & 31) < nk ? v[i].s : (uint16_t)0;
+        }
+        wave_lds_sync();
+#pragma unroll
+        for (int i = 0; i < NV; ++i)
+            unpack_v_row<L::VTS, L::VBPAD, true>(v[i], vrow(tid, i), vt, svs);
+    }
+};
+
 // ---- the 4-bit per-token-head format: 8 codes per word (element 8w + i in
 // bits 4i), one fp16 scale per (token, KV head) for K and for V.
 struct KItem4 {
@@ -1788,6 +1866,21 @@ void attn_ws_kernel(const AttnArgs a) {
 typedef int32_t i32x4s __attribute__((ext_vector_type(4)));
 typedef int64_t i64_t;
 
+// The 16-row kernel's LDS: two tile buffers (the unpack of tile j + 1 runs
+// beside the math of tile j, one barrier per tile) and the V scale staging;
+// 52 KB at D = 256, so three work-groups share a CU.
+template <int D>
+struct S16Lds {
+    using L = TileLds<D, true>;
+    struct Buf {
+        int8_t kq[kKeyTile * L::KQS];
+        alignas(16) _Float16 vt[D * L::VTS];
+        alignas(16) _Float16 skh[(D / 32) * kKeyTile];   // fp16 K scales [D/32][32 keys]
+    };
+    alignas(16) Buf b[2];
+    alignas(16) uint16_t svs[D];
+};
+
 template <int D, bool CAUSAL, bool DEBUG, bool PV16>
 __global__ __launch_bounds__(256) void attn_split16_kernel(const AttnArgs a) {
     constexpr int NB = D / 32;
@@ -1796,7 +1889,8 @@ __global__ __launch_bounds__(256) void attn_split16_kernel(const AttnArgs a) {
     constexpr int NW = 4;
     constexpr int NT = NW * 64;
     using L = TileLds<D, true>;
-    __shared__ __attribute__((aligned(16))) L lds;
+    using SL = S16Lds<D>;
+    __shared__ __attribute__((aligned(16))) SL lds;
 
     // ---- work-group -> (kv head, split, group of 64 rows); the row groups of
     // one (head, split) get ids 8 apart so they share an XCD and its L2.
@@ -1828,7 +1922,33 @@ __global__ __launch_bounds__(256) void attn_split16_kernel(const AttnArgs a) {
         k1 = min(k1, a.L + rho_last / a.G + 1);
     }
     const int vis_from = min(k1, a.L);
+    const int n_tiles = k1 > k0 ? (k1 - k0 + KT - 1) / KT : 0;
 
+    // Step j stores tile j + 1 (fetched into registers during step j - 1)
+    // into buffer (j + 1) & 1, fetches tile j + 2, and runs the math of tile
+    // j from buffer j & 1; one barrier ends the step.  With at most 48 rows
+    // in the work-group its fourth wave, which has no rows, unpacks all V
+    // rows in a loop of its own (the same barriers), and the other waves only
+    // the K items.
+    const bool vw = (rg * NW + NW - 1) * 16 >= a.R;
+    if (vw && wave == NW - 1) {
+        Split16Io<D, true> vio;
+        vio.load(a, head, k0, k0, k1, tid, true);
+        if (n_tiles > 0)
+            vio.store(lds.b[0].kq, lds.b[0].skh, lds.b[0].vt, lds.svs, tid, min(KT, k1 - k0), true);
+        vio.load(a, head, k0 + KT, k0, k1, tid, true);
+        __syncthreads();
+        for (int j = 0; j < n_tiles; ++j) {
+            if (j + 1 < n_tiles) {
+                typename SL::Buf &nb = lds.b[(j + 1) & 1];
+                const int kn = k0 + (j + 1) * KT;
+                vio.store(nb.kq, nb.skh, nb.vt, lds.svs, tid, min(KT, k1 - kn), true);
+            }
+            vio.load(a, head, k0 + (j + 2) * KT, k0, k1, tid, true);
+            __syncthreads();
+        }
+        return;
+    }
     // ---- Q: lane (row i16, chunk qc) quantizes and holds elements
     // 32b + 8qc + [0, 8) of every block b (B operand of the 16x16x32 MFMA)
     i64_t qop[NB];
@@ -1862,7 +1982,7 @@ __global__ __launch_bounds__(256) void attn_split16_kernel(const AttnArgs a) {
     // eight logits are keys 8qc + [0, 8), the run the P.V operand wants.
     const int krow0 = 8 * (i16 >> 2) + (i16 & 3);
     // (row shift: rows krow0 and krow0 + 4 both start 8 (i16 % 4) bytes in)
-    const int8_t *kq_lane = lds.kq + krow0 * L::KQS + 8 * (i16 & 3) + 8 * qc;
+    const int kq_off = krow0 * L::KQS + 8 * (i16 & 3) + 8 * qc;
 
     f32x4 oacc[NDT];
 #pragma unroll
@@ -1875,19 +1995,28 @@ __global__ __launch_bounds__(256) void attn_split16_kernel(const AttnArgs a) {
     float m_run = -INFINITY;
     float l_run = 0.0f;
 
-    TileIo<D, NT, false, true> io;
-    io.load(a, head, k0, k0, k1, tid);
-    for (int kb = k0; kb < k1; kb += KT) {
-        io.store(lds, tid, min(KT, k1 - kb), kb);
-        __syncthreads();
-        io.load(a, head, kb + KT, k0, k1, tid);
+    Split16Io<D, false> io;
+    io.load(a, head, k0, k0, k1, tid, !vw);
+    if (n_tiles > 0)
+        io.store(lds.b[0].kq, lds.b[0].skh, lds.b[0].vt, lds.svs, tid, min(KT, k1 - k0), !vw);
+    io.load(a, head, k0 + KT, k0, k1, tid, !vw);
+    __syncthreads();
+    for (int j = 0; j < n_tiles; ++j) {
+        const int kb = k0 + j * KT;
+        if (j + 1 < n_tiles) {
+            typename SL::Buf &nb = lds.b[(j + 1) & 1];
+            io.store(nb.kq, nb.skh, nb.vt, lds.svs, tid, min(KT, k1 - (kb + KT)), !vw);
+        }
+        io.load(a, head, kb + 2 * KT, k0, k1, tid, !vw);
+        const typename SL::Buf &cb = lds.b[j & 1];
+        const int8_t *kq_lane = cb.kq + kq_off;
 
         if (wave_active) {
             float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
             // ---- Q.K^T, one int8 MFMA per (block, key half), fp32 epilogue
 #pragma unroll
             for (int b = 0; b < NB; ++b) {
-                const f16x8 h = *reinterpret_cast<const f16x8 *>(lds.skh + b * KT + 8 * qc);
+                const f16x8 h = *reinterpret_cast<const f16x8 *>(cb.skh + b * KT + 8 * qc);
 #pragma unroll
                 for (int kh = 0; kh < 2; ++kh) {
                     const i64_t kop = *reinterpret_cast<const i64_t *>(kq_lane + 4 * kh * L::KQS + 32 * b);
@@ -1971,7 +2100,7 @@ __global__ __launch_bounds__(256) void attn_split16_kernel(const AttnArgs a) {
             for (int dt = 0; dt < NDT; ++dt) {
                 const int d = 16 * dt + i16;
                 // (d >> 1) & 3 = (i16 >> 1) & 3: the layout's chunk swizzle
-                const f16x8 vop = *reinterpret_cast<const f16x8 *>(lds.vt + d * L::VTS + 8 * (qc ^ ((i16 >> 1) & 3)));
+                const f16x8 vop = *reinterpret_cast<const f16x8 *>(cb.vt + d * L::VTS + 8 * (qc ^ ((i16 >> 1) & 3)));
                 if constexpr (PV16) {
                     const f32x4 tp = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop, pk, f32x4{}, 0, 0, 0);
                     oh[dt][0] += __builtin_convertvector(f32x2{tp[0], tp[1]}, f16x2);

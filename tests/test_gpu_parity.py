@@ -163,13 +163,16 @@ def _f16_bits(x):
     return np.asarray(x, dtype=np.float16).view(np.uint16)
 
 
-@pytest.mark.parametrize("kind,T", [("tree", 64), ("prefill", 40), ("prefill", 200)])
+@pytest.mark.parametrize("kind,T", [("tree", 64), ("prefill", 40), ("prefill", 200),
+                                    ("tree", 8), ("tree", 10), ("prefill", 8)])
 def test_k_scale_exponent_spread(gpu, orc, kind, T):
     """Keys whose fp16 block scales span more than three binades, or hold
     zeros and subnormals, next to ordinary keys in one call.  For more than
     64 rows per KV head the kernel sums a key's blocks in int32 with integer
     scales when the spread allows it and takes the per-block fp32 epilogue
-    for tiles where it does not; both match the oracle."""
+    for tiles where it does not; the 16-row kernel (48 and 60 rows: with and
+    without its V-unpacking wave) takes the fp32 epilogue on every tile.  All
+    match the oracle."""
     rng = np.random.default_rng(150 if kind == "tree" else 151)
     hq, hkv, d, L = 24, 4, 256, 2000
     host = synth.make_kv(rng, hkv, d, L + T, L + T + 3)
@@ -197,7 +200,8 @@ def test_k_scale_exponent_spread(gpu, orc, kind, T):
     run_case(gpu, orc, hq, hkv, d, L, T, kind, 153, host=host, scale_mul=16.0)
 
 
-@pytest.mark.parametrize("kind,T", [("tree", 64), ("prefill", 40), ("prefill", 200)])
+@pytest.mark.parametrize("kind,T", [("tree", 64), ("prefill", 40), ("prefill", 200),
+                                    ("tree", 8), ("prefill", 10)])
 def test_k_scale_integer_sum_bound(gpu, orc, kind, T):
     """The largest sums the integer-scale path can meet.  Rows whose Q
     elements are all equal quantize to int8 +-127; keys with every code 0
