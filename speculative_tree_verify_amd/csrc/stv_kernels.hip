@@ -59,6 +59,13 @@ constexpr uint32_t kC4Lo = 0xBCC0C2C4u;
 constexpr uint32_t kC4Hi = 0x42403C00u;
 
 // Combine a value with the same lane of the other 32-lane half.
+// Maximum over lanes l and l ^ 16: v_permlane16_swap trades rows 2k + 1 of
+// one copy with rows 2k of the other, so the two results hold, per lane, the
+// values of both rows of its pair (a VALU exchange, no LDS round trip).
+__device__ __forceinline__ float max_xor16(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
 __device__ __forceinline__ float max_halves(float x) {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
@@ -1957,7 +1964,7 @@ __global__ __launch_bounds__(256) void attn_split16_kernel(const AttnArgs a) {
         QPart<NB, 2> qp;
         qp.load(a.q + (size_t)flat * D + 8 * qc);
         float amax = qp.absmax(row_ok);
-        amax = fmaxf(amax, __shfl_xor(amax, 16));
+        amax = max_xor16(amax);
         amax = max_halves(amax);
         const float inv = amax > 0.0f ? 127.0f / amax : 0.0f;
         sq = amax / 127.0f;
@@ -2051,7 +2058,7 @@ __global__ __launch_bounds__(256) void attn_split16_kernel(const AttnArgs a) {
             float amax = acc[0];
 #pragma unroll
             for (int r = 1; r < 8; ++r) amax = fmaxf(amax, acc[r]);
-            amax = fmaxf(amax, __shfl_xor(amax, 16));
+            amax = max_xor16(amax);
             amax = max_halves(amax);
             const float tmax = amax == -INFINITY ? -INFINITY : amax * c_row;
             const float m_new = tmax > m_run + kLazy ? tmax : m_run;
@@ -2226,7 +2233,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_dec_kernel(const AttnArgs
         QPart<NB, 2> qp;
         qp.load(a.q + (size_t)flat * D + 8 * qc);
         float amax = qp.absmax(row_ok);
-        amax = fmaxf(amax, __shfl_xor(amax, 16));
+        amax = max_xor16(amax);
         amax = max_halves(amax);
         const float inv = amax > 0.0f ? 127.0f / amax : 0.0f;
         sq = amax / 127.0f;
@@ -2491,7 +2498,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_dec_kernel(const AttnArgs
         float amax = acc[0];
 #pragma unroll
         for (int r = 1; r < 8; ++r) amax = fmaxf(amax, acc[r]);
-        amax = fmaxf(amax, __shfl_xor(amax, 16));
+        amax = max_xor16(amax);
         amax = max_halves(amax);
         const float tmax = amax == -INFINITY ? -INFINITY : amax * c_row;
         const float m_new = tmax > m_run + lazy ? tmax : m_run;
