@@ -602,6 +602,19 @@ _BOUNDARY_SHAPES = [(1, 16), (1, 17), (2, 8), (2, 9), (2, 16), (2, 17), (2, 32),
                     (6, 64), (8, 64), (1, 64), (4, 25)]
 
 
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("T,ns", [(8, 0), (8, 3), (10, 0), (10, 2)])
+def test_16row_kernel_roles(gpu, orc, d, T, ns):
+    """The 16-row kernel (17 to 64 rows per KV head) at each head dim: 48 rows
+    (T = 8, GQA group 6), where the work-group's fourth wave has no rows and
+    unpacks every V row while the other three unpack K, and 60 rows (T = 10),
+    where all four waves compute and every thread unpacks one K item and one
+    V row; a ragged context (1,000 keys: a partial last tile per split)."""
+    rows = np.arange(T * 6)
+    run_case(gpu, orc, 6, 1, d, 1000, T, "tree", 1700 + 10 * T + d // 64 + ns, n_splits=ns,
+             rows=rows)
+
+
 def test_shape_sweep_kernel_boundaries(gpu, orc):
     """Seeded shapes on both sides of every boundary of the plan's kernel
     choice, over the head dims, context lengths (including none) and split
